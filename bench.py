@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Paged GQA decode step benchmark on one MI355X.
+
+A step is one pass of the decode hot path over one batch: the fused per-head
+RMSNorm + rotary + paged K/V cache write of the batch's new tokens, then paged
+split-KV GQA decode attention with the log-sum-exp combine.  The default
+workload is the Qwen3-1.7B decode shape at batch 64 (16 q heads, 8 kv heads,
+head_dim 128, block size 16, contexts uniform in [1024, 2048], shuffled block
+tables, N(0,1) bf16 inputs).
+
+Consecutive steps use different layers' caches (``--layers`` pools of the same
+shape, cycled), as a model's decode step does, so a layer's K/V has been
+evicted from the 256 MB Infinity Cache before it is read again.
+
+Prints ONE JSON line.  value = algorithmic bytes of the step / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn HBM GB/s (% of peak) + seqs/s, Qwen3-1.7B shapes"
+HBM_PEAK_GBS = 8000.0
+
+
+def decode_alg_bytes(w) -> int:
+    """K and V rows of every attended key, q in, out, block-table entries read, context lengths."""
+    s = w.spec
+    n = w.dec_ctx.astype("int64")
+    kv = int(n.sum()) * s.num_kv_heads * 128 * 2 * 2
+    qo = 2 * w.num_decode * s.num_q_heads * 128 * 2
+    bt = int((-(-n // s.block_size)).sum()) * 4
+    return kv + qo + bt + w.num_decode * 4
+
+
+def write_alg_bytes(w) -> int:
+    """q, k, v in; q_out; k', v into the cache; the two weight vectors; positions, seq ids, table entries."""
+    s = w.spec
+    T = w.num_tokens
+    rows_in = T * (s.num_q_heads + 2 * s.num_kv_heads) * 128 * 2
+    rows_out = T * (s.num_q_heads + 2 * s.num_kv_heads) * 128 * 2
+    return rows_in + rows_out + 2 * 128 * 2 + T * 12
+
+
+def cpu_baseline(w, seconds: float):
+    """The fp64 reference decode, timed on the host on a bounded sample of sequences."""
+    import numpy as np
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    s = w.spec
+    scale = 1.0 / math.sqrt(128)
+    q = O.bf16_bits_to_f64(w.tok_q[w.dec_tok])
+    done, t0 = 0, time.perf_counter()
+    nbytes = 0
+    while True:
+        b = done % w.num_decode
+        O.decode_attention(q[b:b + 1], w.prefix_k, w.prefix_v, w.dec_block_tables[b:b + 1], w.dec_ctx[b:b + 1],
+                           scale)
+        n = int(w.dec_ctx[b])
+        nbytes += n * s.num_kv_heads * 128 * 4 + 2 * s.num_q_heads * 128 * 2 + 4 * (-(-n // s.block_size)) + 4
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": nbytes / el / 1e9, "unit": "GB/s", "seqs_per_s": done / el, "cores": int(threads),
+        "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+        "sample": f"{done} sequences of this step's decode batch (cycled), fp64 numpy reference, "
+                  f"{el:.1f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="cfg3b")
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--split-tokens", type=int, default=0, help="override the planner's split length")
+    ap.add_argument("--waves", type=int, default=0, help="override the planner's waves per split")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+              "shards by sequence or kv head with no exchange, which this benchmark does not exercise",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_head_amd as pg
+    from paged_gqa_decode_head_amd.workloads import SPECS, make_step
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = make_step(SPECS[args.workload])
+    s = w.spec
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    pools = []
+    for _ in range(args.layers):
+        p = pg.Pool(s.num_blocks, s.block_size, s.num_kv_heads, device=dev)
+        p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
+                       blocks=w.used_blocks)
+        pools.append(p)
+    q, k, v = to_bf16(w.tok_q), to_bf16(w.tok_k), to_bf16(w.tok_v)
+    wq, wk = to_bf16(w.wq), to_bf16(w.wk)
+    pos, seq, bt = to_i32(w.tok_pos), to_i32(w.tok_seq), to_i32(w.block_tables)
+    ctx = to_i32(w.dec_ctx)
+    max_ctx = int(w.dec_ctx.max())
+    scale = 1.0 / math.sqrt(128)
+    q_out = torch.empty((w.num_tokens, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((w.num_decode, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+    props = torch.cuda.get_device_properties(dev)
+    plan = pg.plan_decode(props.multi_processor_count, s.block_size, w.num_decode, s.num_kv_heads, s.num_q_heads,
+                          max_ctx)
+    if args.split_tokens:
+        plan.split_tokens = args.split_tokens
+        plan.max_splits = -(-max_ctx // args.split_tokens)
+    if args.waves:
+        plan.waves_per_split = args.waves
+    ws = torch.zeros(pg.decode_workspace_bytes(pools[0], w.num_decode, s.num_q_heads, max_ctx, plan),
+                     dtype=torch.uint8, device=dev)
+    assert w.num_tokens == w.num_decode and np.array_equal(w.dec_tok, np.arange(w.num_decode))
+    calls = []
+    for p in pools:
+        calls.append((pg.bind_cache_write(p, q, k, v, wq, wk, pos, seq, bt, s.eps, s.rope_theta, q_out),
+                      pg.bind_decode(p, q_out, ctx, bt, max_ctx, scale, out, plan=plan, workspace=ws)))
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.warmup):
+        wr, dc = calls[i % args.layers]
+        wr()
+        dc()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wr, dc = calls[i % args.layers]
+        e0, e1, e2 = ev[i]
+        e0.record()
+        wr()
+        e1.record()
+        dc()
+        e2.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for p in pools:
+        assert p.check_errors() == 0
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    write_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
+    decode_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
+    dec_bytes = decode_alg_bytes(w)
+    wr_bytes = write_alg_bytes(w)
+    step_bytes = dec_bytes + wr_bytes
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
+
+    # sampled parity of the last step's output against the fp64 reference
+    import oracle as O
+
+    rows = [0, w.num_decode // 2, w.num_decode - 1]
+    k_all, v_all = pools[(args.steps - 1) % args.layers].read_logical(blocks=w.used_blocks)
+    inv = np.full(s.num_blocks, -1, dtype=np.int64)
+    inv[w.used_blocks] = np.arange(len(w.used_blocks))
+    bt_c = np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1)
+    q_gpu = O.bf16_bits_to_f64(q_out.view(torch.int16).cpu().numpy().view(np.uint16))
+    ref = O.decode_attention(q_gpu[rows], k_all.numpy().view(np.uint16), v_all.numpy().view(np.uint16),
+                             bt_c[rows], w.dec_ctx[rows], scale)
+    got = O.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))[rows]
+    d = np.abs(got - ref)
+    parity = {"rows": rows, "max_abs": float(d.max()), "mean_rel": float(d.sum() / np.abs(ref).sum())}
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {s.description}",
+            "batch": w.num_decode, "num_q_heads": s.num_q_heads, "num_kv_heads": s.num_kv_heads,
+            "head_dim": 128, "block_size": s.block_size, "context_tokens": int(w.dec_ctx.sum()),
+            "layers_cycled": args.layers,
+            "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
+                     "waves_per_split": plan.waves_per_split},
+        },
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s": round(w.num_decode / (ms_step * 1e-3), 1),
+        "tokens_per_s": round(w.num_decode / (ms_step * 1e-3), 1),
+        "step_alg_bytes": step_bytes,
+        "decode_us": round(decode_ms * 1e3, 3),
+        "write_us": round(write_ms * 1e3, 3),
+        "roofline": {
+            "kernel": "decode_kernel (paged split-KV decode + fused combine)",
+            "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(decode_ms * 1e3, 3),
+        },
+        "parity_sample": parity,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,241 @@
+/*
+ * pgqa.h - paged grouped-query attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpgqa.so.  Every pointer named "device" is a HIP device address on
+ * the pool's device; every pointer named "host" is ordinary host memory.  No
+ * call allocates device memory except pgqa_pool_create, no call synchronises
+ * the device except pgqa_pool_check_errors, and no call copies device data to
+ * the host.  Work is enqueued on the caller's HIP stream (passed as void*,
+ * NULL = the null stream) and the call returns.
+ *
+ * Sources (web pages, cited by title and section):
+ *   [P1] "perf: Qwen3 offline inference - hybrid attention backend, fused
+ *        rms_norm_rope, chunked prefill + prompt-lookup spec decoding"
+ *        (InfiniLM pull request 585).
+ *   [P2] "Ascend qwen3.6 optimizate baseline" (vllm-plugin-FL pull request 301).
+ *   [P3] "[2026春季][T2-1-3]" (InfiniLM issue 498).
+ *
+ * Shapes: D (head_dim) is 128.  Hq query heads share Hkv key/value heads in
+ * contiguous groups of r = Hq / Hkv: query head h reads kv head h / r.
+ * bf16 tensors are IEEE bfloat16, rounded to nearest-even when produced.
+ *
+ * Error behaviour: every call returns a pgqa_status; nothing throws across the
+ * ABI; pgqa_last_error() gives a thread-local message for the last failure.
+ * Host-visible argument errors are detected before anything is enqueued.
+ * Metadata that lives in device memory (positions, block ids, context lengths)
+ * is range-checked by the kernels themselves: a bad entry never causes an
+ * out-of-bounds access; the affected row is skipped (cache write) or produces a
+ * zero output row (attention) and a sticky bit is set in the pool's device
+ * error word, read with pgqa_pool_check_errors().
+ */
+#ifndef PGQA_H
+#define PGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PGQA_OK = 0,
+  PGQA_ERR_INVALID_ARG = 1,   /* a host argument is out of range or inconsistent */
+  PGQA_ERR_UNSUPPORTED = 2,   /* a shape this library does not implement (never a silent fallback) */
+  PGQA_ERR_POINTER_KIND = 3,  /* a pointer is not device memory of the pool's device */
+  PGQA_ERR_WORKSPACE = 4,     /* workspace missing or smaller than required */
+  PGQA_ERR_HIP = 5,           /* the HIP runtime reported an error */
+  PGQA_ERR_DEVICE = 6         /* pgqa_pool_check_errors found kernel-detected metadata errors */
+} pgqa_status;
+
+/* Bits of the pool's sticky device error word. */
+#define PGQA_DEVERR_SEQ_ID   0x1u  /* a seq_id outside [0, num_seqs) */
+#define PGQA_DEVERR_POSITION 0x2u  /* a position < 0 or past the end of its block-table row */
+#define PGQA_DEVERR_BLOCK_ID 0x4u  /* a block-table entry outside [0, num_blocks) where it is read */
+#define PGQA_DEVERR_CONTEXT  0x8u  /* a context length < 0, past its table row, or above max_context_len */
+#define PGQA_DEVERR_QUERY    0x10u /* query_start_loc not ascending, or a chunk longer than its context or max_q_len */
+
+/*
+ * Paged KV pool configuration.  [P3] Summary and file list: the cache is
+ * configured by (num_blocks, block_size, max_batch_size), and the two-argument
+ * form (no batch bound) stays valid, here as max_batch_size = 0.
+ */
+typedef struct {
+  int32_t num_blocks;      /* physical blocks in the pool, >= 1 */
+  int32_t block_size;      /* tokens per block: 16, 32, 64, 128 or 256 */
+  int32_t num_kv_heads;    /* Hkv, >= 1 */
+  int32_t head_dim;        /* D: 128 only (else PGQA_ERR_UNSUPPORTED) */
+  int32_t max_batch_size;  /* upper bound on batch / segments per call; 0 = no bound */
+} pgqa_pool_config;
+
+typedef struct pgqa_pool pgqa_pool;  /* opaque */
+
+/* Bytes of device memory the caller must provide for the pool's K/V storage. */
+size_t pgqa_pool_bytes(const pgqa_pool_config* cfg);
+
+/*
+ * Create a pool over caller-owned device storage `kv_storage` (device, at
+ * least pgqa_pool_bytes(cfg) bytes, 256-byte aligned) on the current HIP
+ * device.  The storage layout is owned by the library and reported by
+ * pgqa_pool_layout; callers never pass cache strides (the layout mismatch of
+ * [P2] section 2.3 cannot arise).  The pool allocates only a small device
+ * error word.  The storage is not cleared.
+ */
+pgqa_status pgqa_pool_create(const pgqa_pool_config* cfg, void* kv_storage, pgqa_pool** out);
+
+/* Release the pool handle and its error word; the K/V storage stays the caller's. */
+pgqa_status pgqa_pool_destroy(pgqa_pool* pool);
+
+/*
+ * Element strides (and element offsets from kv_storage) of the logical views
+ * K[num_blocks][block_size][num_kv_heads][head_dim] and the same for V, so that
+ * a caller can build strided views of the cache.  Within one (block, kv head)
+ * the library stores K row-major [slot][dim] followed by V transposed
+ * [dim][slot]; strides are ordered (block, slot, head, dim).
+ */
+pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_t* k_offset,
+                             int64_t v_strides[4], int64_t* v_offset);
+
+/*
+ * Synchronise `stream`, read and clear the pool's sticky device error word.
+ * *flags (host) receives the PGQA_DEVERR_* bits.  Returns PGQA_ERR_DEVICE if any
+ * bit was set, PGQA_OK otherwise.
+ */
+pgqa_status pgqa_pool_check_errors(pgqa_pool* pool, void* stream, uint32_t* flags);
+
+/*
+ * a1 + a2 + a3: per-head RMSNorm of q and k, neox rotary of the normed q and k,
+ * and the write of k' and v into the paged cache, in one launch.
+ * [P1] Summary item 2 (per-head RMSNorm fused with RoPE, full rotary) and item 1
+ * (block-table paged cache).
+ *
+ *   q  device bf16 [num_tokens][num_q_heads][128], token stride q_row_stride elements
+ *   k  device bf16 [num_tokens][Hkv][128], token stride k_row_stride
+ *   v  device bf16 [num_tokens][Hkv][128], token stride v_row_stride
+ *      (strides allow q/k/v to be views of one fused projection output; each
+ *       stride is >= heads*128 and the head/dim axes are dense)
+ *   q_norm_weight, k_norm_weight  device bf16 [128], shared by all heads
+ *   positions  device int32 [num_tokens]: absolute 0-based position of each token
+ *   seq_ids    device int32 [num_tokens]: row of block_tables holding its sequence
+ *   block_tables device int32 [num_seqs][bt_stride]
+ *   eps        RMSNorm epsilon (inside the square root), >= 0
+ *   rope_theta rotary base (inverse frequency theta^(-2i/128)), > 0
+ *   q_out      device bf16 [num_tokens][num_q_heads][128], dense
+ *
+ * For token t: y = x / sqrt(mean(x^2) + eps) * w per head row, then each pair
+ * (i, i+64) is rotated by positions[t] * theta^(-2i/128); k' and v go to slot
+ * positions[t] % block_size of block block_tables[seq_ids[t]][positions[t] / block_size].
+ * Tokens may belong to any mix of sequences; two tokens must not share a slot.
+ * num_tokens = 0 is a no-op.
+ */
+pgqa_status pgqa_rms_norm_rope_cache_write(
+    pgqa_pool* pool,
+    const void* q, int64_t q_row_stride,
+    const void* k, int64_t k_row_stride,
+    const void* v, int64_t v_row_stride,
+    const void* q_norm_weight, const void* k_norm_weight,
+    const int32_t* positions, const int32_t* seq_ids,
+    const int32_t* block_tables, int32_t bt_stride, int32_t num_seqs,
+    int32_t num_tokens, int32_t num_q_heads,
+    float eps, double rope_theta,
+    void* q_out, void* stream);
+
+/*
+ * Split plan of a decode call: keys of each (sequence, kv head) are cut into
+ * splits of split_tokens keys, each processed by one workgroup, then merged by
+ * a log-sum-exp combine.  pgqa_plan_decode fills it from host-known sizes only
+ * ([P1] Summary item 3: routing decisions are host-side, with no device sync).
+ */
+typedef struct {
+  int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64) */
+  int32_t max_splits;       /* ceil(max_context_len / split_tokens) */
+  int32_t waves_per_split;  /* 64-lane waves per workgroup: 1, 2, 4 or 8 */
+  int32_t reserved;         /* 0 */
+} pgqa_decode_plan;
+
+/* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,
+ * for a device with num_cus compute units. */
+pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch, int32_t num_kv_heads,
+                             int32_t num_q_heads, int32_t max_context_len, pgqa_decode_plan* out);
+
+/* Device workspace bytes a decode call with this plan needs (plan = NULL: the default plan). */
+size_t pgqa_decode_workspace_bytes(const pgqa_pool* pool, int32_t batch, int32_t num_q_heads,
+                                   int32_t max_context_len, const pgqa_decode_plan* plan);
+
+/*
+ * a4 + a5: paged split-KV GQA decode attention with log-sum-exp combine.
+ * [P1] Summary item 1 (self-written paged split-KV kernel for pure decode).
+ *
+ *   q            device bf16 [batch][num_q_heads][128] (the q_out of the cache write)
+ *   context_lens device int32 [batch]: keys attended by each sequence (its newly
+ *                written token included); 0 gives a zero output row
+ *   block_tables device int32 [batch][bt_stride]
+ *   max_context_len host hint >= every context_lens entry (sizes the split grid)
+ *   scale        softmax scale applied to q.k (1/sqrt(128) for Qwen3)
+ *   plan         host, optional (NULL = pgqa_plan_decode for this device)
+ *   workspace    device scratch of >= pgqa_decode_workspace_bytes(...) bytes,
+ *                zero-filled once before its first use; every call leaves it
+ *                ready for the next (its counters return to zero).  Calls that
+ *                share a workspace must be ordered on one stream.
+ *   out          device bf16 [batch][num_q_heads][128]
+ *
+ * out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) V_j over keys j < n_b of kv
+ * head h / r, key j at slot j % block_size of block block_tables[b][j / block_size].
+ * Outputs are deterministic for a given plan (fixed combine order).
+ */
+pgqa_status pgqa_paged_decode_attention(
+    pgqa_pool* pool,
+    const void* q, const int32_t* context_lens,
+    const int32_t* block_tables, int32_t bt_stride,
+    int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+    float scale, const pgqa_decode_plan* plan,
+    void* workspace, size_t workspace_bytes,
+    void* out, void* stream);
+
+/* Device workspace bytes a chunk call needs. */
+size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, int32_t total_q,
+                                  int32_t num_q_heads, int32_t max_q_len, int32_t max_context_len);
+
+/*
+ * a6: causal attention of short query chunks over the paged cache: chunked-
+ * prefill slices and b x (k+1) speculative-verify rows.  [P1] Summary items 1
+ * (varlen path over the same paged cache) and 4 (chunked prefill, fixed
+ * b x (k+1) verify shape).
+ *
+ *   q               device bf16 [total_q][num_q_heads][128]
+ *   query_start_loc device int32 [num_segments + 1], ascending, [0] = 0,
+ *                   [num_segments] = total_q (cu_seqlens convention, [P2] section 2.1)
+ *   context_lens    device int32 [num_segments]: keys of each segment, its own
+ *                   q_len tokens included (they must already be in the cache)
+ *   block_tables    device int32 [num_segments][bt_stride]
+ *   max_q_len, max_context_len  host hints >= the device values
+ *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes,
+ *                   zero-filled once before first use (as for decode)
+ *   out             device bf16 [total_q][num_q_heads][128]
+ *
+ * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits
+ * at position n_s - q_len_s + i and attends to keys 0 .. that position.
+ */
+pgqa_status pgqa_paged_chunk_attention(
+    pgqa_pool* pool,
+    const void* q, const int32_t* query_start_loc, const int32_t* context_lens,
+    const int32_t* block_tables, int32_t bt_stride,
+    int32_t num_segments, int32_t total_q, int32_t num_q_heads,
+    int32_t max_q_len, int32_t max_context_len,
+    float scale, void* workspace, size_t workspace_bytes,
+    void* out, void* stream);
+
+/* Static description of a status code. */
+const char* pgqa_status_string(pgqa_status s);
+
+/* Thread-local detail message of the last failing call on this thread ("" if none). */
+const char* pgqa_last_error(void);
+
+/* Library version, "major.minor.patch". */
+const char* pgqa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGQA_H */

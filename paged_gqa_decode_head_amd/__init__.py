@@ -1,0 +1,382 @@
+"""Paged GQA attention hot path for MI355X (gfx950): Python binding of libpgqa.
+
+The C ABI (include/pgqa.h) does the work; this module only marshals torch
+tensors (device memory) and the current HIP stream into it.  There is no
+fallback: if ``libpgqa.so`` is missing or fails to load, every entry point
+raises.  Build it with ``python -m paged_gqa_decode_head_amd.build``.
+
+Entry points (same names as the C ABI, without the ``pgqa_`` prefix):
+  Pool(...)                         pgqa_pool_create / pgqa_pool_destroy / pgqa_pool_layout
+  rms_norm_rope_cache_write(...)    pgqa_rms_norm_rope_cache_write
+  paged_decode_attention(...)       pgqa_paged_decode_attention
+  paged_chunk_attention(...)        pgqa_paged_chunk_attention
+  plan_decode(...)                  pgqa_plan_decode
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpgqa.so")
+
+PGQA_OK = 0
+STATUS_NAMES = {
+    0: "PGQA_OK", 1: "PGQA_ERR_INVALID_ARG", 2: "PGQA_ERR_UNSUPPORTED", 3: "PGQA_ERR_POINTER_KIND",
+    4: "PGQA_ERR_WORKSPACE", 5: "PGQA_ERR_HIP", 6: "PGQA_ERR_DEVICE",
+}
+DEVERR_SEQ_ID, DEVERR_POSITION, DEVERR_BLOCK_ID, DEVERR_CONTEXT, DEVERR_QUERY = 0x1, 0x2, 0x4, 0x8, 0x10
+
+
+class PgqaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class PoolConfig(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("max_batch_size", ctypes.c_int32)]
+
+
+class DecodePlan(ctypes.Structure):
+    _fields_ = [("split_tokens", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("waves_per_split", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"DecodePlan(split_tokens={self.split_tokens}, max_splits={self.max_splits}, "
+                f"waves_per_split={self.waves_per_split})")
+
+
+_lib = None
+
+_P, _I32, _I64, _SZ, _F32, _F64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
+                                   ctypes.c_float, ctypes.c_double)
+_SIGNATURES = {
+    "pgqa_version": ([], ctypes.c_char_p),
+    "pgqa_last_error": ([], ctypes.c_char_p),
+    "pgqa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "pgqa_pool_bytes": ([ctypes.POINTER(PoolConfig)], _SZ),
+    "pgqa_pool_create": ([ctypes.POINTER(PoolConfig), _P, ctypes.POINTER(_P)], ctypes.c_int),
+    "pgqa_pool_destroy": ([_P], ctypes.c_int),
+    "pgqa_pool_layout": ([_P, ctypes.POINTER(_I64), ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                          ctypes.POINTER(_I64)], ctypes.c_int),
+    "pgqa_pool_check_errors": ([_P, _P, ctypes.POINTER(ctypes.c_uint32)], ctypes.c_int),
+    "pgqa_rms_norm_rope_cache_write": ([_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _I32, _I32,
+                                        _I32, _I32, _F32, _F64, _P, _P], ctypes.c_int),
+    "pgqa_plan_decode": ([_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(DecodePlan)], ctypes.c_int),
+    "pgqa_decode_workspace_bytes": ([_P, _I32, _I32, _I32, ctypes.POINTER(DecodePlan)], _SZ),
+    "pgqa_paged_decode_attention": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, ctypes.POINTER(DecodePlan),
+                                     _P, _SZ, _P, _P], ctypes.c_int),
+    "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32], _SZ),
+    "pgqa_paged_chunk_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _SZ, _P,
+                                    _P], ctypes.c_int),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpgqa (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_gqa_decode_head_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def _check(status: int):
+    if status != PGQA_OK:
+        raise PgqaError(status, lib().pgqa_last_error().decode())
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, name, dtype=None, device=None, contiguous=True):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the pool on {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def version() -> str:
+    return lib().pgqa_version().decode()
+
+
+def pool_bytes(num_blocks, block_size, num_kv_heads, head_dim=128, max_batch_size=0) -> int:
+    cfg = PoolConfig(num_blocks, block_size, num_kv_heads, head_dim, max_batch_size)
+    return int(lib().pgqa_pool_bytes(ctypes.byref(cfg)))
+
+
+class Pool:
+    """A paged K/V pool: torch owns the storage, libpgqa owns its layout."""
+
+    def __init__(self, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int = 128,
+                 max_batch_size: int = 0, device=None):
+        import torch
+
+        self.config = PoolConfig(num_blocks, block_size, num_kv_heads, head_dim, max_batch_size)
+        nbytes = int(lib().pgqa_pool_bytes(ctypes.byref(self.config)))
+        if nbytes == 0:
+            _check(lib().pgqa_pool_create(ctypes.byref(self.config), None, ctypes.byref(_P())))
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        if dev.index is None:
+            dev = torch.device(dev.type, torch.cuda.current_device())
+        self.device = dev
+        with torch.cuda.device(self.device):
+            self.storage = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=self.device)
+            h = _P()
+            _check(lib().pgqa_pool_create(ctypes.byref(self.config), _ptr(self.storage), ctypes.byref(h)))
+        self.handle = h
+        self.num_blocks, self.block_size, self.num_kv_heads = num_blocks, block_size, num_kv_heads
+        self.head_dim = head_dim
+        ks, vs = (_I64 * 4)(), (_I64 * 4)()
+        ko, vo = _I64(), _I64()
+        _check(lib().pgqa_pool_layout(self.handle, ks, ctypes.byref(ko), vs, ctypes.byref(vo)))
+        self.k_strides, self.k_offset = tuple(ks), ko.value
+        self.v_strides, self.v_offset = tuple(vs), vo.value
+        self._ws = {}
+
+    def k_view(self):
+        """K cache as a strided bf16 view [num_blocks, block_size, num_kv_heads, head_dim]."""
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        return self.storage.as_strided(shape, self.k_strides, self.k_offset)
+
+    def v_view(self):
+        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        return self.storage.as_strided(shape, self.v_strides, self.v_offset)
+
+    def fill_logical(self, k, v, blocks=None):
+        """Copy logical [n, block_size, Hkv, 128] K/V (bf16, or int16/uint16 bit
+        patterns) into the cache: all blocks, or the listed physical ``blocks``."""
+        import torch
+
+        def as_bf16(x):
+            x = torch.as_tensor(x)
+            if x.dtype in (torch.int16, torch.uint16):
+                x = x.view(torch.int16).view(torch.bfloat16)
+            return x.to(self.device)
+
+        kv, vv = self.k_view(), self.v_view()
+        if blocks is None:
+            kv.copy_(as_bf16(k))
+            vv.copy_(as_bf16(v))
+        else:
+            idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
+            kv[idx] = as_bf16(k)
+            vv[idx] = as_bf16(v)
+
+    def read_logical(self, blocks=None):
+        """(K, V) as CPU int16 bit patterns [n, block_size, Hkv, 128] in logical order."""
+        import torch
+
+        kv, vv = self.k_view(), self.v_view()
+        if blocks is not None:
+            idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
+            kv, vv = kv[idx], vv[idx]
+        return (kv.contiguous().view(torch.int16).cpu(), vv.contiguous().view(torch.int16).cpu())
+
+    def check_errors(self, stream=None) -> int:
+        """Synchronise the stream and return (and clear) the device error bits."""
+        flags = ctypes.c_uint32(0)
+        st = lib().pgqa_pool_check_errors(self.handle, _stream(stream), ctypes.byref(flags))
+        if st not in (PGQA_OK, 6):
+            _check(st)
+        return int(flags.value)
+
+    def workspace(self, nbytes: int, key: str):
+        """A zero-filled device workspace of at least nbytes, cached per purpose."""
+        import torch
+
+        ws = self._ws.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self._ws[key] = ws
+        return ws
+
+    def close(self):
+        if getattr(self, "handle", None):
+            _check(lib().pgqa_pool_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def rms_norm_rope_cache_write(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids,
+                              block_tables, eps: float, rope_theta: float, q_out=None, stream=None):
+    """Fused per-head RMSNorm + neox RoPE of q/k and paged K/V write; returns q_out.
+
+    q [T, Hq, 128], k/v [T, Hkv, 128] bf16 (token rows may be strided: the
+    head and dim axes must be dense), weights [128] bf16, positions/seq_ids [T]
+    int32, block_tables [num_seqs, width] int32.
+    """
+    import torch
+
+    T, hq = q.shape[0], q.shape[1]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
+        if t.dim() != 3 or t.shape[2] != 128 or t.stride(2) != 1 or t.stride(1) != 128:
+            raise ValueError(f"{name} must be [T, heads, 128] with dense heads and dims")
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _require(t, name, torch.bfloat16, pool.device)
+    for name, t in (("positions", positions), ("seq_ids", seq_ids), ("block_tables", block_tables)):
+        _require(t, name, torch.int32, pool.device)
+    if q_out is None:
+        q_out = torch.empty((T, hq, 128), dtype=torch.bfloat16, device=pool.device)
+    _require(q_out, "q_out", torch.bfloat16, pool.device)
+    _check(lib().pgqa_rms_norm_rope_cache_write(
+        pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(seq_ids), _ptr(block_tables),
+        block_tables.shape[1], block_tables.shape[0], T, hq, float(eps), float(rope_theta), _ptr(q_out),
+        _stream(stream)))
+    return q_out
+
+
+def plan_decode(num_cus, block_size, batch, num_kv_heads, num_q_heads, max_context_len) -> DecodePlan:
+    p = DecodePlan()
+    _check(lib().pgqa_plan_decode(num_cus, block_size, batch, num_kv_heads, num_q_heads, max_context_len,
+                                  ctypes.byref(p)))
+    return p
+
+
+def decode_workspace_bytes(pool: Pool, batch, num_q_heads, max_context_len, plan: DecodePlan = None) -> int:
+    return int(lib().pgqa_decode_workspace_bytes(pool.handle, batch, num_q_heads, max_context_len,
+                                                 None if plan is None else ctypes.byref(plan)))
+
+
+def paged_decode_attention(pool: Pool, q, context_lens, block_tables, max_context_len: int, scale: float,
+                           plan: DecodePlan = None, workspace=None, out=None, stream=None):
+    """Paged split-KV GQA decode attention; returns out [B, Hq, 128] bf16.
+
+    ``max_context_len`` is a host-side upper bound of ``context_lens`` (no
+    device read).  ``workspace`` (uint8, zero-filled once) defaults to a
+    per-pool cached buffer.
+    """
+    import torch
+
+    _require(q, "q", torch.bfloat16, pool.device)
+    _require(context_lens, "context_lens", torch.int32, pool.device)
+    _require(block_tables, "block_tables", torch.int32, pool.device)
+    B, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device=pool.device)
+    _require(out, "out", torch.bfloat16, pool.device)
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
+    if workspace is None:
+        workspace = pool.workspace(need, "decode")
+    _check(lib().pgqa_paged_decode_attention(
+        pool.handle, _ptr(q), _ptr(context_lens), _ptr(block_tables), block_tables.shape[1], B, hq,
+        int(max_context_len), float(scale), pp, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(out), _stream(stream)))
+    return out
+
+
+def chunk_workspace_bytes(pool: Pool, num_segments, total_q, num_q_heads, max_q_len, max_context_len) -> int:
+    return int(lib().pgqa_chunk_workspace_bytes(pool.handle, num_segments, total_q, num_q_heads, max_q_len,
+                                                max_context_len))
+
+
+def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int,
+                          max_context_len: int, scale: float, workspace=None, out=None, stream=None):
+    """Causal chunk attention over the paged cache; returns out [total_q, Hq, 128] bf16."""
+    import torch
+
+    _require(q, "q", torch.bfloat16, pool.device)
+    for name, t in (("query_start_loc", query_start_loc), ("context_lens", context_lens),
+                    ("block_tables", block_tables)):
+        _require(t, name, torch.int32, pool.device)
+    Tq, hq = q.shape[0], q.shape[1]
+    N = context_lens.shape[0]
+    if out is None:
+        out = torch.empty((Tq, hq, 128), dtype=torch.bfloat16, device=pool.device)
+    _require(out, "out", torch.bfloat16, pool.device)
+    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len)))
+    if workspace is None:
+        workspace = pool.workspace(need, "chunk")
+    _check(lib().pgqa_paged_chunk_attention(
+        pool.handle, _ptr(q), _ptr(query_start_loc), _ptr(context_lens), _ptr(block_tables), block_tables.shape[1],
+        N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    return out
+
+
+class BoundCall:
+    """A C-ABI call with its arguments marshalled once; calling it re-issues the
+    same launch (same tensors, same stream) without per-call Python work."""
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != PGQA_OK:
+            _check(st)
+
+
+def bind_cache_write(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables,
+                     eps: float, rope_theta: float, q_out, stream=None) -> BoundCall:
+    keep = (q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables, q_out)
+    args = (pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
+            _ptr(k_norm_weight), _ptr(positions), _ptr(seq_ids), _ptr(block_tables), block_tables.shape[1],
+            block_tables.shape[0], q.shape[0], q.shape[1], float(eps), float(rope_theta), _ptr(q_out),
+            _stream(stream))
+    return BoundCall(lib().pgqa_rms_norm_rope_cache_write, args, keep)
+
+
+def bind_decode(pool: Pool, q, context_lens, block_tables, max_context_len: int, scale: float, out,
+                plan: DecodePlan = None, workspace=None, stream=None) -> BoundCall:
+    B, hq = q.shape[0], q.shape[1]
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
+    if workspace is None:
+        workspace = pool.workspace(need, "decode")
+    keep = (q, context_lens, block_tables, out, workspace, plan)
+    args = (pool.handle, _ptr(q), _ptr(context_lens), _ptr(block_tables), block_tables.shape[1], B, hq,
+            int(max_context_len), float(scale), pp, _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _ptr(out), _stream(stream))
+    return BoundCall(lib().pgqa_paged_decode_attention, args, keep)
+
+
+def bind_chunk(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int, max_context_len: int,
+               scale: float, out, workspace=None, stream=None) -> BoundCall:
+    Tq, hq = q.shape[0], q.shape[1]
+    N = context_lens.shape[0]
+    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len)))
+    if workspace is None:
+        workspace = pool.workspace(need, "chunk")
+    keep = (q, query_start_loc, context_lens, block_tables, out, workspace)
+    args = (pool.handle, _ptr(q), _ptr(query_start_loc), _ptr(context_lens), _ptr(block_tables),
+            block_tables.shape[1], N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
+    return BoundCall(lib().pgqa_paged_chunk_attention, args, keep)

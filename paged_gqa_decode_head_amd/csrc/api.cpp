@@ -1,0 +1,402 @@
+// C ABI of libpgqa: argument validation, pointer-kind checks, the decode split
+// planner and kernel launches.  No call here synchronises the device or copies
+// device data to the host, except pgqa_pool_check_errors and pool set-up.
+//
+// Page "[2026春季][T2-1-3]" (InfiniLM issue 498), Review notes: the host checks
+// that a buffer it is about to read really is host memory; here every pointer
+// is checked to be device memory of the pool's device before anything is
+// enqueued.  Page "perf: Qwen3 offline inference - ...", Summary item 3:
+// routing decisions are made on the host with no device synchronisation; the
+// split plan below uses host-known sizes and the CU count only.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "../../include/pgqa.h"
+#include "launch.hpp"
+
+using namespace pgqa;
+
+struct pgqa_pool {
+  pgqa_pool_config cfg;
+  PoolGeom geom;
+  int device;
+  int num_cus;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pgqa_status fail(pgqa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+pgqa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PGQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_block_size(int32_t bs) { return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256; }
+
+// Device memory of `device`?  hipPointerGetAttributes is a host-side lookup (no sync).
+pgqa_status check_device_ptr(const void* p, int device, const char* name, size_t align = 2) {
+  if (p == nullptr) return fail(PGQA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    return fail(PGQA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  hipPointerAttribute_t at;
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(PGQA_ERR_POINTER_KIND, "%s is not HIP device memory (%s)", name, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+    return fail(PGQA_ERR_POINTER_KIND, "%s is host memory, device memory is required", name);
+  if (at.device != device)
+    return fail(PGQA_ERR_POINTER_KIND, "%s lives on device %d, the pool on device %d", name, at.device, device);
+  return PGQA_OK;
+}
+
+#define PGQA_TRY(expr)                 \
+  do {                                 \
+    pgqa_status s_ = (expr);           \
+    if (s_ != PGQA_OK) return s_;      \
+  } while (0)
+
+pgqa_status check_pool(const pgqa_pool* pool) {
+  if (pool == nullptr) return fail(PGQA_ERR_INVALID_ARG, "pool is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != pool->device)
+    return fail(PGQA_ERR_INVALID_ARG, "current device %d is not the pool's device %d", dev, pool->device);
+  return PGQA_OK;
+}
+
+pgqa_status check_group(const pgqa_pool* pool, int32_t num_q_heads) {
+  const int32_t hkv = pool->cfg.num_kv_heads;
+  if (num_q_heads <= 0 || num_q_heads % hkv != 0)
+    return fail(PGQA_ERR_INVALID_ARG, "num_q_heads=%d is not a positive multiple of num_kv_heads=%d", num_q_heads,
+                hkv);
+  const int32_t r = num_q_heads / hkv;
+  if (r != 1 && r != 2 && r != 4 && r != 8)
+    return fail(PGQA_ERR_UNSUPPORTED, "query heads per kv head = %d (supported: 1, 2, 4, 8)", r);
+  return PGQA_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+constexpr int32_t kMaxSplitTokens = 4096;
+
+pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t max_context_len) {
+  const int32_t gran = block_size > 64 ? block_size : 64;
+  if (p.split_tokens <= 0 || p.split_tokens % gran != 0 || p.split_tokens > kMaxSplitTokens)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.split_tokens=%d must be a positive multiple of %d, at most %d",
+                p.split_tokens, gran, kMaxSplitTokens);
+  if (p.waves_per_split != 1 && p.waves_per_split != 2 && p.waves_per_split != 4 && p.waves_per_split != 8)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.waves_per_split=%d (1, 2, 4 or 8)", p.waves_per_split);
+  const int64_t need = (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens;
+  if (p.max_splits < need || p.max_splits > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
+                max_context_len);
+  return PGQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pgqa_version(void) { return "0.1.0"; }
+
+const char* pgqa_last_error(void) { return g_err; }
+
+const char* pgqa_status_string(pgqa_status s) {
+  switch (s) {
+    case PGQA_OK: return "ok";
+    case PGQA_ERR_INVALID_ARG: return "invalid argument";
+    case PGQA_ERR_UNSUPPORTED: return "unsupported shape";
+    case PGQA_ERR_POINTER_KIND: return "pointer is not device memory of the pool's device";
+    case PGQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PGQA_ERR_HIP: return "HIP runtime error";
+    case PGQA_ERR_DEVICE: return "kernel-detected metadata error";
+  }
+  return "unknown status";
+}
+
+size_t pgqa_pool_bytes(const pgqa_pool_config* cfg) {
+  if (cfg == nullptr || cfg->num_blocks <= 0 || cfg->num_kv_heads <= 0 || !valid_block_size(cfg->block_size) ||
+      cfg->head_dim != 128)
+    return 0;
+  return size_t(cfg->num_blocks) * cfg->num_kv_heads * 2 * cfg->block_size * cfg->head_dim * sizeof(uint16_t);
+}
+
+pgqa_status pgqa_pool_create(const pgqa_pool_config* cfg, void* kv_storage, pgqa_pool** out) {
+  g_err[0] = 0;
+  if (out == nullptr) return fail(PGQA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (cfg == nullptr) return fail(PGQA_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->num_blocks <= 0) return fail(PGQA_ERR_INVALID_ARG, "num_blocks=%d", cfg->num_blocks);
+  if (cfg->num_kv_heads <= 0) return fail(PGQA_ERR_INVALID_ARG, "num_kv_heads=%d", cfg->num_kv_heads);
+  if (cfg->max_batch_size < 0) return fail(PGQA_ERR_INVALID_ARG, "max_batch_size=%d", cfg->max_batch_size);
+  if (cfg->head_dim != 128) return fail(PGQA_ERR_UNSUPPORTED, "head_dim=%d (only 128)", cfg->head_dim);
+  if (!valid_block_size(cfg->block_size))
+    return fail(PGQA_ERR_UNSUPPORTED, "block_size=%d (16, 32, 64, 128 or 256)", cfg->block_size);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  PGQA_TRY(check_device_ptr(kv_storage, dev, "kv_storage", 256));
+  int cus = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  uint32_t* err = nullptr;
+  e = hipMalloc(reinterpret_cast<void**>(&err), 256);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(error word)");
+  e = hipMemset(err, 0, 256);
+  if (e != hipSuccess) {
+    (void)hipFree(err);
+    return hip_fail(e, "hipMemset(error word)");
+  }
+  pgqa_pool* p = new (std::nothrow) pgqa_pool;
+  if (p == nullptr) {
+    (void)hipFree(err);
+    return fail(PGQA_ERR_INVALID_ARG, "out of host memory");
+  }
+  p->cfg = *cfg;
+  p->geom.kv = static_cast<uint16_t*>(kv_storage);
+  p->geom.num_blocks = cfg->num_blocks;
+  p->geom.block_size = cfg->block_size;
+  p->geom.num_kv_heads = cfg->num_kv_heads;
+  p->geom.err = err;
+  p->device = dev;
+  p->num_cus = cus;
+  *out = p;
+  return PGQA_OK;
+}
+
+pgqa_status pgqa_pool_destroy(pgqa_pool* pool) {
+  if (pool == nullptr) return PGQA_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(pool->device);
+  hipError_t e = hipFree(pool->geom.err);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete pool;
+  if (e != hipSuccess) return hip_fail(e, "hipFree(error word)");
+  return PGQA_OK;
+}
+
+pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_t* k_offset, int64_t v_strides[4],
+                             int64_t* v_offset) {
+  if (pool == nullptr || k_strides == nullptr || k_offset == nullptr || v_strides == nullptr || v_offset == nullptr)
+    return fail(PGQA_ERR_INVALID_ARG, "NULL argument");
+  const int64_t bs = pool->cfg.block_size, D = 128, hkv = pool->cfg.num_kv_heads;
+  const int64_t tile = 2 * bs * D;
+  // order (block, slot, head, dim)
+  k_strides[0] = tile * hkv;
+  k_strides[1] = D;
+  k_strides[2] = tile;
+  k_strides[3] = 1;
+  *k_offset = 0;
+  v_strides[0] = tile * hkv;
+  v_strides[1] = 1;
+  v_strides[2] = tile;
+  v_strides[3] = bs;
+  *v_offset = bs * D;
+  return PGQA_OK;
+}
+
+pgqa_status pgqa_pool_check_errors(pgqa_pool* pool, void* stream, uint32_t* flags) {
+  PGQA_TRY(check_pool(pool));
+  if (flags == nullptr) return fail(PGQA_ERR_INVALID_ARG, "flags is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  uint32_t v = 0;
+  e = hipMemcpy(&v, pool->geom.err, sizeof(v), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpy(error word)");
+  e = hipMemset(pool->geom.err, 0, sizeof(v));
+  if (e != hipSuccess) return hip_fail(e, "hipMemset(error word)");
+  *flags = v;
+  if (v != 0) return fail(PGQA_ERR_DEVICE, "device metadata errors 0x%x", v);
+  return PGQA_OK;
+}
+
+pgqa_status pgqa_rms_norm_rope_cache_write(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
+                                           int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                           const void* q_norm_weight, const void* k_norm_weight,
+                                           const int32_t* positions, const int32_t* seq_ids,
+                                           const int32_t* block_tables, int32_t bt_stride, int32_t num_seqs,
+                                           int32_t num_tokens, int32_t num_q_heads, float eps, double rope_theta,
+                                           void* q_out, void* stream) {
+  g_err[0] = 0;
+  PGQA_TRY(check_pool(pool));
+  PGQA_TRY(check_group(pool, num_q_heads));
+  const int64_t hkv = pool->cfg.num_kv_heads;
+  if (num_tokens < 0) return fail(PGQA_ERR_INVALID_ARG, "num_tokens=%d", num_tokens);
+  if (bt_stride <= 0 || num_seqs <= 0)
+    return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d num_seqs=%d", bt_stride, num_seqs);
+  if (pool->cfg.max_batch_size > 0 && num_seqs > pool->cfg.max_batch_size)
+    return fail(PGQA_ERR_INVALID_ARG, "num_seqs=%d exceeds max_batch_size=%d", num_seqs, pool->cfg.max_batch_size);
+  if (q_row_stride < int64_t(num_q_heads) * 128 || k_row_stride < hkv * 128 || v_row_stride < hkv * 128)
+    return fail(PGQA_ERR_INVALID_ARG, "row strides (%lld, %lld, %lld) below the dense row length",
+                (long long)q_row_stride, (long long)k_row_stride, (long long)v_row_stride);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(PGQA_ERR_INVALID_ARG, "eps=%g", double(eps));
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(PGQA_ERR_INVALID_ARG, "rope_theta=%g", rope_theta);
+  if (num_tokens == 0) return PGQA_OK;
+  const int dev = pool->device;
+  PGQA_TRY(check_device_ptr(q, dev, "q"));
+  PGQA_TRY(check_device_ptr(k, dev, "k"));
+  PGQA_TRY(check_device_ptr(v, dev, "v"));
+  PGQA_TRY(check_device_ptr(q_norm_weight, dev, "q_norm_weight"));
+  PGQA_TRY(check_device_ptr(k_norm_weight, dev, "k_norm_weight"));
+  PGQA_TRY(check_device_ptr(positions, dev, "positions", 4));
+  PGQA_TRY(check_device_ptr(seq_ids, dev, "seq_ids", 4));
+  PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
+  PGQA_TRY(check_device_ptr(q_out, dev, "q_out"));
+  WriteArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_stride = q_row_stride;
+  a.k = static_cast<const uint16_t*>(k);
+  a.k_stride = k_row_stride;
+  a.v = static_cast<const uint16_t*>(v);
+  a.v_stride = v_row_stride;
+  a.wq = static_cast<const uint16_t*>(q_norm_weight);
+  a.wk = static_cast<const uint16_t*>(k_norm_weight);
+  a.pos = positions;
+  a.seq = seq_ids;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.eps = eps;
+  a.theta = rope_theta;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  hipError_t e = launch_cache_write(pool->geom, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache write launch");
+  return PGQA_OK;
+}
+
+pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch, int32_t num_kv_heads,
+                             int32_t num_q_heads, int32_t max_context_len, pgqa_decode_plan* out) {
+  if (out == nullptr) return fail(PGQA_ERR_INVALID_ARG, "out is NULL");
+  if (num_cus <= 0 || !valid_block_size(block_size) || batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      max_context_len < 0)
+    return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
+  // Enough workgroups to give every CU several, so that contexts of different
+  // lengths even out; splits no shorter than 256 keys, so the partial results
+  // stay below 1% of the K/V bytes; never longer than the LDS block-id stage.
+  const int64_t gran = block_size > 64 ? block_size : 64;
+  const int64_t units = int64_t(batch > 0 ? batch : 1) * num_kv_heads;
+  const int64_t target_wgs = 8ll * num_cus;
+  const int64_t want = (target_wgs + units - 1) / units;
+  const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
+  int64_t split = round_up((ctx + want - 1) / want, gran);
+  if (split < 256) split = round_up(256, gran);
+  if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
+  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  out->split_tokens = int32_t(split);
+  out->max_splits = int32_t((ctx + split - 1) / split);
+  out->waves_per_split = 4;
+  out->reserved = 0;
+  return PGQA_OK;
+}
+
+size_t pgqa_decode_workspace_bytes(const pgqa_pool* pool, int32_t batch, int32_t num_q_heads,
+                                   int32_t max_context_len, const pgqa_decode_plan* plan) {
+  if (pool == nullptr || batch < 0 || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return 0;
+  pgqa_decode_plan p;
+  if (plan != nullptr) {
+    p = *plan;
+  } else if (pgqa_plan_decode(pool->num_cus, pool->cfg.block_size, batch, pool->cfg.num_kv_heads, num_q_heads,
+                              max_context_len, &p) != PGQA_OK) {
+    return 0;
+  }
+  return decode_workspace_layout(batch, pool->cfg.num_kv_heads, num_q_heads / pool->cfg.num_kv_heads, p.max_splits)
+      .total;
+}
+
+pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const int32_t* context_lens,
+                                        const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                                        int32_t num_q_heads, int32_t max_context_len, float scale,
+                                        const pgqa_decode_plan* plan, void* workspace, size_t workspace_bytes,
+                                        void* out, void* stream) {
+  g_err[0] = 0;
+  PGQA_TRY(check_pool(pool));
+  PGQA_TRY(check_group(pool, num_q_heads));
+  if (batch < 0 || batch > 65535) return fail(PGQA_ERR_INVALID_ARG, "batch=%d", batch);
+  if (pool->cfg.max_batch_size > 0 && batch > pool->cfg.max_batch_size)
+    return fail(PGQA_ERR_INVALID_ARG, "batch=%d exceeds max_batch_size=%d", batch, pool->cfg.max_batch_size);
+  if (bt_stride <= 0) return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d", bt_stride);
+  if (max_context_len < 0) return fail(PGQA_ERR_INVALID_ARG, "max_context_len=%d", max_context_len);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PGQA_ERR_INVALID_ARG, "scale=%g", double(scale));
+  if (batch == 0) return PGQA_OK;
+  pgqa_decode_plan p;
+  if (plan != nullptr) {
+    p = *plan;
+  } else {
+    PGQA_TRY(pgqa_plan_decode(pool->num_cus, pool->cfg.block_size, batch, pool->cfg.num_kv_heads, num_q_heads,
+                              max_context_len, &p));
+  }
+  PGQA_TRY(validate_plan(p, pool->cfg.block_size, max_context_len));
+  const int32_t r = num_q_heads / pool->cfg.num_kv_heads;
+  const DecodeWorkspace wl = decode_workspace_layout(batch, pool->cfg.num_kv_heads, r, p.max_splits);
+  const int dev = pool->device;
+  PGQA_TRY(check_device_ptr(q, dev, "q", 16));
+  PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
+  PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
+  PGQA_TRY(check_device_ptr(out, dev, "out"));
+  if (p.max_splits > 1 || max_context_len > p.split_tokens) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(PGQA_ERR_WORKSPACE, "decode workspace of %zu bytes needed, %zu given", wl.total,
+                  workspace == nullptr ? size_t(0) : workspace_bytes);
+    PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  }
+  DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.ctx = context_lens;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.max_ctx = max_context_len;
+  a.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
+  a.split_tokens = p.split_tokens;
+  a.max_splits = p.max_splits;
+  a.waves = p.waves_per_split;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = ws ? reinterpret_cast<uint32_t*>(ws + wl.counters_off) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  hipError_t e = launch_decode(pool->geom, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return PGQA_OK;
+}
+
+size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, int32_t total_q, int32_t num_q_heads,
+                                  int32_t max_q_len, int32_t max_context_len) {
+  (void)pool; (void)num_segments; (void)total_q; (void)num_q_heads; (void)max_q_len; (void)max_context_len;
+  return 0;
+}
+
+pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
+                                       const int32_t* context_lens, const int32_t* block_tables, int32_t bt_stride,
+                                       int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t max_q_len,
+                                       int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
+                                       void* out, void* stream) {
+  (void)pool; (void)q; (void)query_start_loc; (void)context_lens; (void)block_tables; (void)bt_stride;
+  (void)num_segments; (void)total_q; (void)num_q_heads; (void)max_q_len; (void)max_context_len; (void)scale;
+  (void)workspace; (void)workspace_bytes; (void)out; (void)stream;
+  return fail(PGQA_ERR_UNSUPPORTED, "chunk attention not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Device helpers shared by the gfx950 kernels of libpgqa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgqa {
+
+constexpr int kHeadDim = 128;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Sticky error bits, mirrored from include/pgqa.h.
+constexpr uint32_t kErrSeqId = 0x1u;
+constexpr uint32_t kErrPosition = 0x2u;
+constexpr uint32_t kErrBlockId = 0x4u;
+constexpr uint32_t kErrContext = 0x8u;
+constexpr uint32_t kErrQuery = 0x10u;
+
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bit) {
+  __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// bf16 halves of a 32-bit word widened to fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t p = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi with bf16 pairs a, b and an fp32 accumulator.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         acc, false);
+}
+
+// DPP lane exchanges within 16-lane rows.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF,
+                                                                false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;  // lane i <-> 15-i within each 16 lanes
+
+// Sum over each aligned group of 8 lanes; every lane of the group gets the sum.
+__device__ __forceinline__ float sum8(float v) {
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace pgqa

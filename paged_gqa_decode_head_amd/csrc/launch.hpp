@@ -1,0 +1,71 @@
+// Internal launch interface between the C ABI layer (api.cpp) and the kernels.
+// Arguments are validated by the caller; these functions only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pgqa {
+
+// Physical layout of one pool: for block b and kv head g the (b, g) tile holds
+// K row-major [block_size][128] and then V transposed [128][block_size], bf16.
+struct PoolGeom {
+  uint16_t* kv;          // device base
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  uint32_t* err;         // device sticky error word
+};
+
+__host__ __device__ inline int64_t tile_elems(const PoolGeom& p) { return 2ll * p.block_size * 128; }
+
+struct WriteArgs {
+  const uint16_t* q; int64_t q_stride;
+  const uint16_t* k; int64_t k_stride;
+  const uint16_t* v; int64_t v_stride;
+  const uint16_t* wq; const uint16_t* wk;
+  const int32_t* pos; const int32_t* seq;
+  const int32_t* bt; int32_t bt_stride; int32_t num_seqs;
+  int32_t num_tokens; int32_t num_q_heads;
+  float eps; double theta;
+  uint16_t* q_out;
+};
+
+hipError_t launch_cache_write(const PoolGeom& pool, const WriteArgs& a, hipStream_t stream);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const int32_t* ctx;
+  const int32_t* bt; int32_t bt_stride;
+  int32_t batch; int32_t num_q_heads; int32_t max_ctx;
+  float qk_scale_log2;   // softmax scale * log2(e)
+  int32_t split_tokens; int32_t max_splits; int32_t waves;
+  float* part_o;         // [batch][Hkv][max_splits][r][128]
+  float* part_lse;       // [batch][Hkv][max_splits][r]
+  uint32_t* counters;    // [batch][Hkv], zero between calls
+  uint16_t* out;
+};
+
+hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream);
+
+// Workspace carve-up shared by the host API and the launchers.
+struct DecodeWorkspace {
+  size_t counters_off, part_o_off, part_lse_off, total;
+};
+DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_splits);
+
+struct ChunkArgs {
+  const uint16_t* q;
+  const int32_t* qsl; const int32_t* ctx;
+  const int32_t* bt; int32_t bt_stride;
+  int32_t num_segments; int32_t total_q; int32_t num_q_heads;
+  int32_t max_q_len; int32_t max_ctx;
+  float qk_scale_log2;
+  int32_t split_tokens; int32_t max_splits; int32_t q_tiles;
+  float* part_o; float* part_lse; uint32_t* counters;
+  uint16_t* out;
+};
+
+hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream);
+
+}  // namespace pgqa

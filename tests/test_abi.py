@@ -1,0 +1,93 @@
+"""The C-ABI library builds for gfx950, loads and exports what include/pgqa.h
+declares; host-side checks and the split planner work without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_decode_head_amd as pg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "pgqa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pgqa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = pg.lib()
+    declared = _declared_functions()
+    assert len(declared) >= 14
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(pg.exported_symbols()) == declared
+
+
+def test_library_is_built_for_gfx950():
+    data = open(pg.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def test_version_and_status_strings():
+    assert re.fullmatch(r"\d+\.\d+\.\d+", pg.version())
+    for s in range(7):
+        assert pg.lib().pgqa_status_string(s)
+
+
+def test_pool_bytes():
+    assert pg.pool_bytes(32, 16, 8) == 32 * 8 * 2 * 16 * 128 * 2
+    assert pg.pool_bytes(7680, 16, 4) == 7680 * 4 * 2 * 16 * 128 * 2
+    assert pg.pool_bytes(10, 256, 2) == 10 * 2 * 2 * 256 * 128 * 2
+    assert pg.pool_bytes(32, 24, 8) == 0        # block size not a supported power of two
+    assert pg.pool_bytes(32, 16, 8, head_dim=64) == 0
+    assert pg.pool_bytes(0, 16, 8) == 0
+
+
+def test_pool_create_rejects_bad_config_before_touching_the_device():
+    L = pg.lib()
+    h = ctypes.c_void_p()
+    cfg = pg.PoolConfig(32, 16, 8, 64, 0)
+    assert L.pgqa_pool_create(ctypes.byref(cfg), None, ctypes.byref(h)) == 2   # head_dim 64: unsupported
+    assert b"head_dim" in L.pgqa_last_error()
+    cfg = pg.PoolConfig(32, 48, 8, 128, 0)
+    assert L.pgqa_pool_create(ctypes.byref(cfg), None, ctypes.byref(h)) == 2
+    cfg = pg.PoolConfig(0, 16, 8, 128, 0)
+    assert L.pgqa_pool_create(ctypes.byref(cfg), None, ctypes.byref(h)) == 1
+    assert L.pgqa_pool_create(None, None, ctypes.byref(h)) == 1
+    assert L.pgqa_pool_create(ctypes.byref(cfg), None, None) == 1
+
+
+def test_calls_reject_null_pool():
+    L = pg.lib()
+    assert L.pgqa_paged_decode_attention(None, None, None, None, 1, 1, 16, 10, 0.1, None, None, 0, None,
+                                         None) == 1
+    assert L.pgqa_rms_norm_rope_cache_write(None, None, 0, None, 0, None, 0, None, None, None, None, None, 1, 1,
+                                            1, 16, 1e-6, 1e6, None, None) == 1
+    assert L.pgqa_pool_destroy(None) == 0
+    flags = ctypes.c_uint32()
+    assert L.pgqa_pool_check_errors(None, None, ctypes.byref(flags)) == 1
+
+
+@pytest.mark.parametrize("cus", [256, 304, 80])
+@pytest.mark.parametrize("bs", [16, 32, 256])
+@pytest.mark.parametrize("batch,hkv,ctx", [(1, 8, 32769), (64, 8, 2049), (8, 8, 4097), (64, 4, 1281),
+                                            (2, 8, 101), (1, 1, 1), (512, 8, 100000)])
+def test_decode_plan_properties(cus, bs, batch, hkv, ctx):
+    p = pg.plan_decode(cus, bs, batch, hkv, 2 * hkv, ctx)
+    gran = max(bs, 64)
+    assert p.split_tokens % gran == 0
+    assert 0 < p.split_tokens <= 4096
+    assert p.max_splits == -(-ctx // p.split_tokens)          # covers every key, no empty tail split
+    assert p.waves_per_split in (1, 2, 4, 8)
+    if ctx >= 256 * 4 and batch * hkv < cus:
+        assert batch * hkv * p.max_splits >= cus                 # long contexts spread over the chip
+
+
+def test_plan_rejects_bad_input():
+    with pytest.raises(pg.PgqaError):
+        pg.plan_decode(0, 16, 1, 8, 16, 100)
+    with pytest.raises(pg.PgqaError):
+        pg.plan_decode(256, 24, 1, 8, 16, 100)

@@ -1,0 +1,257 @@
+"""GPU parity of the fused cache write and of paged decode attention against
+the fp64 reference, on the five Qwen3-shaped synthetic steps and on small
+ragged cases.  Calls go through the C ABI (libpgqa.so) via the binding."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_gqa_decode_head_amd as pg
+from paged_gqa_decode_head_amd.workloads import SPECS, Group, StepSpec, make_step
+
+from harness import SCALE, SENTINEL, StepRun, bits_of, compare, dev_bf16, dev_i32, f64_of
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def workload(name, rep=0):
+    key = (name, rep)
+    if key not in _CACHE:
+        _CACHE.clear()
+        _CACHE[key] = make_step(SPECS[name], rep)
+    return _CACHE[key]
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- write (a1-a3)
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5"])
+def test_cache_write_parity_and_exact_slots(name):
+    _note(f"[write] {name}")
+    w = workload(name)
+    run = StepRun(w, fill_prefix=False)
+    s = w.spec
+    shape = (len(run.used), s.block_size, s.num_kv_heads, 128)
+    sent = np.full(shape, SENTINEL, dtype=np.uint16)
+    run.pool.fill_logical(sent.view(np.int16), sent.view(np.int16), blocks=run.used)
+    q_out = run.write()
+    assert run.pool.check_errors() == 0
+    q_ref, k_ref, (blk, off), _ = run.oracle_write()
+    compare(q_out, q_ref, f"{name} q_out")
+    pk, pv, _ = run.read_pool()
+    # the set of written slots is exactly the reference's (bit-exact addressing)
+    changed_k = np.any(pk != SENTINEL, axis=(2, 3))
+    changed_v = np.any(pv != SENTINEL, axis=(2, 3))
+    expect = np.zeros_like(changed_k)
+    expect[blk, off] = True
+    assert np.array_equal(changed_k, expect)
+    assert np.array_equal(changed_v, expect)
+    # written rows: V bit-exact, K within tolerance
+    assert np.array_equal(pv[blk, off], w.tok_v)
+    k_got = torch.from_numpy(pk[blk, off].view(np.int16)).view(torch.bfloat16)
+    compare(k_got, k_ref, f"{name} k cache")
+
+
+# ---------------------------------------------------------------- decode (a4-a5)
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5"])
+def test_decode_parity(name):
+    _note(f"[decode] {name}")
+    w = workload(name)
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    out = run.decode(q=q)
+    assert run.pool.check_errors() == 0
+    ref = run.oracle_decode_on_gpu_inputs(q)
+    ma, mr = compare(out, ref, f"{name} decode")
+    _note(f"  max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def test_cfg1_end_to_end_chain():
+    """Whole step in fp64 (bf16 rounding only where the library stores bf16) vs the GPU."""
+    _note("[e2e] cfg1")
+    w = workload("cfg1")
+    run = StepRun(w)
+    run.write()
+    out = run.decode()
+    q_ref, _, _, (pk, pv) = run.oracle_write()
+    from harness import compact
+    bt_c = compact(w.block_tables, run.used)
+    q_dec = O.bf16_round(q_ref[w.dec_tok])
+    ref = O.decode_attention(q_dec, pk, pv, bt_c, w.dec_ctx, SCALE)
+    compare(out, ref, "cfg1 end to end")
+
+
+# ---------------------------------------------------------------- small ragged cases
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
+                                       (16, 4, 256)])
+@pytest.mark.parametrize("plan", [None, (64, 1), (128, 2), (256, 4), (512, 8), (4096, 4)])
+def test_decode_small_shapes_and_plans(hq, hkv, bs, plan):
+    spec = StepSpec(f"small-{hq}-{hkv}-{bs}", 901 + hq + bs, hq, hkv, 256 if bs < 256 else 32,
+                    decode=(Group(1, 0, 0), Group(1, 15, 15), Group(1, 16, 16), Group(4, 1, 700)),
+                    block_size=bs)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    p = None
+    if plan is not None:
+        split = max(plan[0], bs)
+        p = pg.DecodePlan(split, -(-int(w.dec_ctx.max()) // split), plan[1], 0)
+    out = run.decode(plan=p, q=q)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_decode_on_gpu_inputs(q), f"{spec.name} plan={plan}")
+
+
+def test_decode_deterministic_and_block_permutation_bit_identical():
+    _note("[perm] small")
+    w = make_step(StepSpec("perm", 950, 16, 8, 640, decode=(Group(6, 100, 1500),)))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    plan = pg.DecodePlan(256, 6, 4, 0)
+    a = bits_of(run.decode(plan=plan, q=q))
+    b = bits_of(run.decode(plan=plan, q=q))
+    assert np.array_equal(a, b)
+    # the same logical cache under another physical block assignment
+    pk, pv, bt_c = run.read_pool()
+    rng = np.random.default_rng(3)
+    nb = w.spec.num_blocks
+    new_ids = rng.permutation(nb)[: len(run.used)]
+    pool2 = pg.Pool(nb, 16, 8)
+    pool2.fill_logical(pk.view(np.int16), pv.view(np.int16), blocks=new_ids)
+    bt2 = np.where(bt_c >= 0, new_ids[np.maximum(bt_c, 0)], -1).astype(np.int32)
+    out2 = pg.paged_decode_attention(pool2, q, run.dec_ctx, dev_i32(bt2), int(w.dec_ctx.max()), SCALE, plan=plan)
+    assert np.array_equal(a, bits_of(out2))
+
+
+def test_single_key_returns_v_exactly():
+    w = make_step(StepSpec("one", 960, 16, 8, 16, decode=(Group(3, 0, 0),)))
+    run = StepRun(w)
+    run.write()
+    out = bits_of(run.decode())
+    for b in range(3):
+        for h in range(16):
+            assert np.array_equal(out[b, h], w.tok_v[b, h // 2])
+
+
+def test_addressing_probe_one_hot_every_position():
+    """Only key j* matches q strongly: the output must be V_j* bit-exactly, for
+    every logical position j* of every sequence (every table entry, every offset)."""
+    bs, hkv, hq = 16, 2, 4
+    lens = [37, 100, 16, 1]
+    nb = 24
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(nb)
+    need = [-(-n // bs) for n in lens]
+    bt = np.full((len(lens), max(need)), -1, dtype=np.int32)
+    c = 0
+    for i, k in enumerate(need):
+        bt[i, :k] = perm[c:c + k]
+        c += k
+    pool = pg.Pool(nb, bs, hkv)
+    u = np.zeros(128)
+    u[:32] = 1.0                                   # q = u; hot key = 15 u gives z = 15*32/sqrt(128) ~ 42
+    vk = O.f64_to_bf16_bits(rng.standard_normal((nb, bs, hkv, 128)))
+    q = dev_bf16(np.broadcast_to(O.f64_to_bf16_bits(u), (len(lens), hq, 128)).copy())
+    bt_d = dev_i32(bt)
+    ctx = dev_i32(np.array(lens, dtype=np.int32))
+    hot = O.f64_to_bf16_bits(15.0 * u)
+    for jstar in range(max(lens)):
+        kk = np.zeros((nb, bs, hkv, 128), dtype=np.uint16)
+        for s, n in enumerate(lens):
+            j = jstar % n
+            kk[bt[s, j // bs], j % bs] = hot
+        pool.fill_logical(kk.view(np.int16), vk.view(np.int16))
+        for plan in (pg.DecodePlan(64, 2, 1, 0), pg.DecodePlan(4096, 1, 4, 0)):
+            out = bits_of(pg.paged_decode_attention(pool, q, ctx, bt_d, max(lens), SCALE, plan=plan))
+            for s, n in enumerate(lens):
+                j = jstar % n
+                for h in range(hq):
+                    assert np.array_equal(out[s, h], vk[bt[s, j // bs], j % bs, h // 2]), (jstar, s, h)
+
+
+def test_empty_batch_and_zero_context():
+    w = make_step(StepSpec("z", 970, 16, 8, 16, decode=(Group(2, 5, 5),)))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    out = torch.full((2, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    pg.paged_decode_attention(run.pool, q[:0], run.dec_ctx[:0], run.dec_bt[:0], 6, SCALE, out=out[:0])
+    ctx0 = dev_i32(np.array([0, 6], dtype=np.int32))
+    pg.paged_decode_attention(run.pool, q, ctx0, run.dec_bt, 6, SCALE, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out[0] == 0)
+    assert run.pool.check_errors() == 0
+
+
+def test_bad_metadata_sets_flags_without_faulting():
+    w = make_step(StepSpec("bad", 980, 16, 8, 16, decode=(Group(2, 20, 20),)))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    # context longer than the table row: flagged, row zeroed
+    ctx = dev_i32(np.array([21, 16 * run.dec_bt.shape[1] + 1], dtype=np.int32))
+    out = pg.paged_decode_attention(run.pool, q, ctx, run.dec_bt, 16 * run.dec_bt.shape[1] + 1, SCALE)
+    assert run.pool.check_errors() & pg.DEVERR_CONTEXT
+    assert torch.all(out[1] == 0)
+    # block id outside the pool: flagged, no fault
+    bt = w.dec_block_tables.copy()
+    bt[0, 0] = 10_000
+    out = pg.paged_decode_attention(run.pool, q, run.dec_ctx, dev_i32(bt), 21, SCALE)
+    assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
+    # cache write with a position past the table and a bad seq id: skipped and flagged
+    pos = dev_i32(np.array([10_000, 3], dtype=np.int32))
+    seq = dev_i32(np.array([0, 7], dtype=np.int32))
+    pg.rms_norm_rope_cache_write(run.pool, run.q[:2], run.k[:2], run.v[:2], run.wq, run.wk, pos, seq, run.bt,
+                                 1e-6, 1e6)
+    f = run.pool.check_errors()
+    assert f & pg.DEVERR_POSITION and f & pg.DEVERR_SEQ_ID
+
+
+def test_host_pointer_rejected():
+    """The C ABI refuses a host buffer where device memory is required."""
+    import ctypes
+
+    w = make_step(StepSpec("hp", 990, 16, 8, 16, decode=(Group(1, 3, 3),)))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    out = torch.empty_like(q)
+    host_ctx = np.array([4], dtype=np.int32)
+    L = pg.lib()
+    st = L.pgqa_paged_decode_attention(run.pool.handle, ctypes.c_void_p(q.data_ptr()),
+                                       host_ctx.ctypes.data_as(ctypes.c_void_p),
+                                       ctypes.c_void_p(run.dec_bt.data_ptr()), run.dec_bt.shape[1], 1, 16, 4,
+                                       SCALE, None, None, 0, ctypes.c_void_p(out.data_ptr()), None)
+    assert st == 3 and b"context_lens" in L.pgqa_last_error()
+
+
+def test_decode_ignores_garbage_past_the_context():
+    """Slots past each context hold NaN bit patterns: weights there are 0 and
+    the result must not see them."""
+    w = make_step(StepSpec("garbage", 975, 16, 8, 160, decode=(Group(6, 1, 300),)))
+    run = StepRun(w, fill_prefix=False)
+    s = w.spec
+    k = np.full((s.num_blocks, s.block_size, s.num_kv_heads, 128), SENTINEL, dtype=np.uint16)
+    v = k.copy()
+    for row in range(w.num_decode):
+        L = int(w.dec_ctx[row]) - 1
+        for j in range(L):
+            blk, off = w.block_tables[row, j // s.block_size], j % s.block_size
+            k[blk, off] = w.prefix_k[blk, off]
+            v[blk, off] = w.prefix_v[blk, off]
+    run.pool.fill_logical(k.view(np.int16), v.view(np.int16))
+    run.write()
+    q = run.decode_q()
+    for plan in (None, pg.DecodePlan(64, 5, 1, 0), pg.DecodePlan(4096, 1, 8, 0)):
+        out = run.decode(plan=plan, q=q)
+        compare(out, run.oracle_decode_on_gpu_inputs(q), f"garbage plan={plan}")
