@@ -147,10 +147,10 @@ pgqa_status pgqa_rms_norm_rope_cache_write(
  * ([P1] Summary item 3: routing decisions are host-side, with no device sync).
  */
 typedef struct {
-  int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64) */
+  int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64), <= 1024 * waves_per_split */
   int32_t max_splits;       /* ceil(max_context_len / split_tokens) */
   int32_t waves_per_split;  /* 64-lane waves per workgroup: 1, 2, 4 or 8 */
-  int32_t reserved;         /* 0 */
+  int32_t load_hint;        /* K/V loads: 0 library default, 1 cached, 2 streaming (non-temporal) */
 } pgqa_decode_plan;
 
 /* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,
@@ -173,15 +173,16 @@ size_t pgqa_decode_workspace_bytes(const pgqa_pool* pool, int32_t batch, int32_t
  *   max_context_len host hint >= every context_lens entry (sizes the split grid)
  *   scale        softmax scale applied to q.k (1/sqrt(128) for Qwen3)
  *   plan         host, optional (NULL = pgqa_plan_decode for this device)
- *   workspace    device scratch of >= pgqa_decode_workspace_bytes(...) bytes,
- *                zero-filled once before its first use; every call leaves it
- *                ready for the next (its counters return to zero).  Calls that
+ *   workspace    device scratch of >= pgqa_decode_workspace_bytes(...) bytes for
+ *                the split partials (0 bytes, and NULL allowed, when the plan
+ *                has one split); no initial contents are needed.  Calls that
  *                share a workspace must be ordered on one stream.
  *   out          device bf16 [batch][num_q_heads][128]
  *
  * out[b][h] = sum_j softmax_j(scale * q[b][h] . K_j) V_j over keys j < n_b of kv
  * head h / r, key j at slot j % block_size of block block_tables[b][j / block_size].
- * Outputs are deterministic for a given plan (fixed combine order).
+ * Outputs are deterministic for a given plan (fixed combine order).  With more
+ * than one split the call enqueues two kernels (splits, then the combine).
  */
 pgqa_status pgqa_paged_decode_attention(
     pgqa_pool* pool,
@@ -209,8 +210,8 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  *                   q_len tokens included (they must already be in the cache)
  *   block_tables    device int32 [num_segments][bt_stride]
  *   max_q_len, max_context_len  host hints >= the device values
- *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes,
- *                   zero-filled once before first use (as for decode)
+ *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes
+ *                   (no initial contents needed)
  *   out             device bf16 [total_q][num_q_heads][128]
  *
  * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits

@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <new>
 
 #include "../../include/pgqa.h"
@@ -94,6 +95,8 @@ pgqa_status check_group(const pgqa_pool* pool, int32_t num_q_heads) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int32_t kMaxSplitTokens = 4096;
+// Non-temporal K/V loads by default (K/V bytes are read once per launch).
+constexpr bool kDefaultStreamLoads = true;
 
 pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t max_context_len) {
   const int32_t gran = block_size > 64 ? block_size : 64;
@@ -102,6 +105,10 @@ pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t
                 p.split_tokens, gran, kMaxSplitTokens);
   if (p.waves_per_split != 1 && p.waves_per_split != 2 && p.waves_per_split != 4 && p.waves_per_split != 8)
     return fail(PGQA_ERR_INVALID_ARG, "plan.waves_per_split=%d (1, 2, 4 or 8)", p.waves_per_split);
+  if (p.split_tokens > 1024 * p.waves_per_split)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.split_tokens=%d exceeds 1024 keys per wave (%d waves)", p.split_tokens,
+                p.waves_per_split);
+  if (p.load_hint < 0 || p.load_hint > 2) return fail(PGQA_ERR_INVALID_ARG, "plan.load_hint=%d", p.load_hint);
   const int64_t need = (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens;
   if (p.max_splits < need || p.max_splits > 65535)
     return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
@@ -291,22 +298,39 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   if (num_cus <= 0 || !valid_block_size(block_size) || batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
       max_context_len < 0)
     return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
-  // Enough workgroups to give every CU several, so that contexts of different
-  // lengths even out; splits no shorter than 256 keys, so the partial results
-  // stay below 1% of the K/V bytes; never longer than the LDS block-id stage.
+  // Measured on MI355X (decode sweeps over the five Qwen3 workloads): each
+  // workgroup pays a few microseconds of dependent-load latency before its
+  // first K/V tile arrives, so long splits win over many short ones.
+  //  * one split per (sequence, kv head) when that already gives at least half
+  //    a workgroup per CU (no partials, no combine launch);
+  //  * otherwise about one workgroup per CU, with splits of at least 1024 keys
+  //    (2048 for contexts of 16k keys or more);
+  //  * 8 waves per workgroup when 8 query heads share a kv head (more dot
+  //    products per byte), else 4.
+  const int32_t r = num_q_heads / num_kv_heads;
+  const int32_t waves = r >= 8 ? 8 : 4;
   const int64_t gran = block_size > 64 ? block_size : 64;
   const int64_t units = int64_t(batch > 0 ? batch : 1) * num_kv_heads;
-  const int64_t target_wgs = 8ll * num_cus;
-  const int64_t want = (target_wgs + units - 1) / units;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  int64_t split = round_up((ctx + want - 1) / want, gran);
-  if (split < 256) split = round_up(256, gran);
-  if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
-  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  const int64_t max_split = std::min<int64_t>(1024ll * waves, kMaxSplitTokens);
+  int64_t split;
+  if (2 * units >= num_cus) {
+    split = round_up(ctx, gran);
+  } else {
+    const int64_t want = (num_cus + units - 1) / units;
+    split = round_up((ctx + want - 1) / want, gran);
+    const int64_t floor_split = round_up(ctx >= 16384 ? 2048 : 1024, gran);
+    if (split < floor_split) split = floor_split;
+    if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
+  }
+  if (split > max_split) {
+    const int64_t parts = (ctx + max_split - 1) / max_split;
+    split = std::min(round_up((ctx + parts - 1) / parts, gran), max_split / gran * gran);
+  }
   out->split_tokens = int32_t(split);
   out->max_splits = int32_t((ctx + split - 1) / split);
-  out->waves_per_split = 4;
-  out->reserved = 0;
+  out->waves_per_split = waves;
+  out->load_hint = 0;
   return PGQA_OK;
 }
 
@@ -354,7 +378,7 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
   PGQA_TRY(check_device_ptr(out, dev, "out"));
-  if (p.max_splits > 1 || max_context_len > p.split_tokens) {
+  if (wl.total > 0) {
     if (workspace == nullptr || workspace_bytes < wl.total)
       return fail(PGQA_ERR_WORKSPACE, "decode workspace of %zu bytes needed, %zu given", wl.total,
                   workspace == nullptr ? size_t(0) : workspace_bytes);
@@ -372,8 +396,8 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   a.split_tokens = p.split_tokens;
   a.max_splits = p.max_splits;
   a.waves = p.waves_per_split;
-  char* ws = static_cast<char*>(workspace);
-  a.counters = ws ? reinterpret_cast<uint32_t*>(ws + wl.counters_off) : nullptr;
+  a.stream_loads = p.load_hint == 2 || (p.load_hint == 0 && kDefaultStreamLoads);
+  char* ws = wl.total > 0 ? static_cast<char*>(workspace) : nullptr;
   a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
   a.out = static_cast<uint16_t*>(out);

@@ -13,27 +13,31 @@
 // (wave w: tiles w, w+W, ...), each wave keeping its own online softmax state.
 //
 // Inside a wave, for one 16-key tile of one (block, kv head):
-//   * keys: the 8-lane group G = lane/8 owns keys 2G and 2G+1, lane % 8 owns
-//     16 of the 128 dims.  Each lane loads 2 x 32 contiguous bytes of K, takes
-//     bf16 pair dot products with q (v_dot2_f32_bf16, no unpacking), and three
-//     DPP steps finish the 128-dim sums inside the 8-lane group.
+//   * keys: the 8-lane group G = lane/8 owns keys 2G and 2G+1; lane s = lane%8
+//     owns dims 8s..8s+7 and 64+8s..64+8s+7.  With that split every 16-byte
+//     load instruction reads whole 128-byte lines across its lanes.  Scores are
+//     bf16 pair dot products (v_dot2_f32_bf16, no unpacking) finished by three
+//     DPP steps inside the 8-lane group.
 //   * softmax: scores are in log2 units (q.k * scale * log2 e).  The running
 //     maximum is only raised when a score exceeds it by more than kTau, which a
 //     wave-wide ballot detects; otherwise no max reduction and no rescale is
 //     done.  The weights exp2(s - m) (at most 2^kTau) are packed to bf16 pairs
 //     and broadcast through LDS.
 //   * values: the cache stores each V tile transposed, [dim][slot], so lane l
-//     loads dims 2l and 2l+1 for all 16 keys (64 contiguous bytes) and the
-//     weighted sum over key pairs is again v_dot2_f32_bf16.  No lane needs
-//     another lane's accumulator until the end of the split.
-//   * the next tile's 128 bytes per lane are loaded while the current one is
-//     computed (register double buffer, DEPTH tiles in flight per wave).
+//     reads dims 32j + l/2 (j = 0..3) for keys 8(l&1)..8(l&1)+7: consecutive
+//     lanes read consecutive 16-byte pieces of the 4 KiB tile (block size 16).
+//     The weighted sum over key pairs is again v_dot2_f32_bf16; the two key
+//     halves of a dim meet once, at the end of the split.
+//   * the next tile is loaded while the current one is computed (two register
+//     buffers per wave); K/V loads may carry the non-temporal hint.
 //
 // Combine.  With one split the workgroup writes bf16 directly.  Otherwise it
-// writes its normalised partial o_k and lse_k, and the last workgroup of the
-// (b, g) pair to arrive (an atomic ticket, used for ordering only) merges all
-// partials in split order: o = sum_k 2^(lse_k - lse) o_k.  The combine order is
-// fixed, so results do not depend on which workgroup arrives last.
+// writes its normalised partial o_k and lse_k (log2 units), and a second small
+// kernel merges the partials of each (sequence, query head) in split order:
+// o = sum_k 2^(lse_k - lse) o_k.  (Merging inside the split kernel, by the last
+// workgroup to finish, needs device-scope release/acquire fences per
+// workgroup; on this chip those write back and invalidate the XCD's L2 and cost
+// far more than the extra launch.)
 #include <math.h>
 
 #include "device_common.hpp"
@@ -43,11 +47,11 @@ namespace pgqa {
 namespace {
 
 constexpr float kTau = 8.0f;              // log2 headroom before the running max is raised
-constexpr int kMaxSplitTokens = 4096;     // bounds the per-split block-id stage in LDS
+constexpr int kMaxTilesPerWave = 64;      // block ids of a wave's tiles live one per lane
 
 struct Tile {
-  uint4 k[4];  // k[0..1]: key 2G, dims 16*(lane%8) .. +16;  k[2..3]: key 2G+1
-  uint4 v[4];  // v[0..1]: V^T row 2*lane (16 keys); v[2..3]: row 2*lane+1
+  uint4 k[4];  // key 2G: k[0] dims 8s.., k[1] dims 64+8s..;  key 2G+1: k[2], k[3]
+  uint4 v[4];  // v[j]: V^T row 32j + lane/2, keys 8(lane&1) .. +7 (four bf16 pairs)
   int ok;
 };
 
@@ -55,20 +59,46 @@ __device__ __forceinline__ uint32_t comp(const uint4& x, int i) {
   return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
 }
 
-template <int R, int W, int DEPTH>
+template <bool kStream>
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) {
+  if constexpr (kStream) return load_stream(p);
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <int R, int W, bool kStream>
 __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a) {
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int grp = lane >> 3, sub = lane & 7;
+  const int grp = lane >> 3, sub = lane & 7, khalf = lane & 1;
   const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
 
-  __shared__ int32_t s_blk[kMaxSplitTokens / 16];
   __shared__ __align__(16) uint32_t s_p[W][R][8];
   __shared__ float s_m[W][R], s_l[W][R];
   __shared__ __align__(16) float s_acc[W][R][kHeadDim];
-  __shared__ int s_last;
 
+  // Issue the context length, this wave's block ids and q together: lane i
+  // fetches the block id of the wave's i-th tile (tile wave + i*W of the
+  // split), read back per tile with readlane.  Entries are fetched only inside
+  // the table row, before the context length is known.
   const int n = a.ctx[b];
+  const int k0 = sp * a.split_tokens;
+  int32_t lane_blk = -1;
+  {
+    const int tile = wave + lane * W;
+    const int64_t entry = (int64_t(k0) + tile * 16) / bs;
+    if (tile * 16 < a.split_tokens && entry < a.bt_stride) lane_blk = a.bt[int64_t(b) * a.bt_stride + entry];
+  }
+  // q of the group, as bf16 pairs, for the lane's dims 8s.. and 64+8s..
+  uint32_t qv[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    const uint16_t* qrow = a.q + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 8;
+    const uint4 x = *reinterpret_cast<const uint4*>(qrow);
+    const uint4 y = *reinterpret_cast<const uint4*>(qrow + 64);
+    qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
+    qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
+  }
+
   const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;
   uint16_t* out_bg = a.out + (int64_t(b) * hq + g * R) * kHeadDim;
   if (bad_ctx || n == 0) {
@@ -80,60 +110,39 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   }
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (sp >= ns) return;
-  const int k0 = sp * a.split_tokens;
   const int k1 = min(n, k0 + a.split_tokens);
-  const int nblk = (k1 - k0 + bs - 1) / bs;
-  {
-    const int32_t* row = a.bt + int64_t(b) * a.bt_stride + k0 / bs;
-    for (int i = tid; i < nblk; i += 64 * W) s_blk[i] = row[i];
-  }
-
-  // q rows of the group: lane holds dims 16*sub .. 16*sub+15 of each head, as bf16 pairs.
-  uint32_t qv[R][8];
-#pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const uint4* qp = reinterpret_cast<const uint4*>(a.q + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 16);
-    const uint4 x = qp[0], y = qp[1];
-    qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
-    qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
-  }
-  __syncthreads();
 
   const int64_t tstride = tile_elems(pool);
   const int64_t bstride = tstride * hkv;
   const uint16_t* pool_g = pool.kv + int64_t(g) * tstride;
   const int ntiles = (k1 - k0 + 15) >> 4;
 
-  float m[R], l[R], acc[R][2];
+  float m[R], l[R], acc[R][4];
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
-    acc[h][0] = acc[h][1] = 0.f;
+    acc[h][0] = acc[h][1] = acc[h][2] = acc[h][3] = 0.f;
   }
 
-  auto load = [&](Tile& tb, int tt) {
-    const int rel = tt * 16;
-    int32_t blk = s_blk[rel / bs];
-    const int sub16 = (rel & (bs - 1)) >> 4;
-    tb.ok = unsigned(blk) < unsigned(pool.num_blocks);
-    if (!tb.ok) {
-      if (lane == 0) raise_error(pool.err, kErrBlockId);
-      blk = 0;
-    }
+  // Branch-free tile load (no atomics, no divergent paths), so that the
+  // compiler counts outstanding loads exactly and waits only for the tile
+  // about to be used.  i is the wave-local tile number.
+  auto load = [&](Tile& tb, int i) {
+    const int tt = wave + i * W;
+    const int32_t raw = __builtin_amdgcn_readlane(lane_blk, i);
+    const int sub16 = ((k0 + tt * 16) & (bs - 1)) >> 4;
+    tb.ok = unsigned(raw) < unsigned(pool.num_blocks);
+    const int32_t blk = tb.ok ? raw : 0;
     const uint16_t* base = pool_g + int64_t(blk) * bstride;
-    const uint4* kp = reinterpret_cast<const uint4*>(base + (sub16 * 16 + 2 * grp) * kHeadDim + sub * 16);
-    tb.k[0] = kp[0];
-    tb.k[1] = kp[1];
-    tb.k[2] = kp[kHeadDim / 8];
-    tb.k[3] = kp[kHeadDim / 8 + 1];
-    const uint16_t* vrow = base + int64_t(bs) * kHeadDim + int64_t(2 * lane) * bs + sub16 * 16;
-    const uint4* vp0 = reinterpret_cast<const uint4*>(vrow);
-    const uint4* vp1 = reinterpret_cast<const uint4*>(vrow + bs);
-    tb.v[0] = vp0[0];
-    tb.v[1] = vp0[1];
-    tb.v[2] = vp1[0];
-    tb.v[3] = vp1[1];
+    const uint16_t* kp = base + (sub16 * 16 + 2 * grp) * kHeadDim + sub * 8;
+    tb.k[0] = ld16<kStream>(kp);
+    tb.k[1] = ld16<kStream>(kp + 64);
+    tb.k[2] = ld16<kStream>(kp + kHeadDim);
+    tb.k[3] = ld16<kStream>(kp + kHeadDim + 64);
+    const uint16_t* vp = base + int64_t(bs) * kHeadDim + int64_t(lane >> 1) * bs + sub16 * 16 + khalf * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tb.v[j] = ld16<kStream>(vp + int64_t(32 * j) * bs);
   };
 
   // Zero the V entries of keys that are not attended (past the split end, or
@@ -142,20 +151,24 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   auto mask_v = [&](Tile& tb, int tt) {
     const int nv = tb.ok ? k1 - (k0 + tt * 16) : 0;  // valid keys in this tile
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint32_t keep = 2 * c + 1 < nv ? 0xffffffffu : 2 * c < nv ? 0x0000ffffu : 0u;
-      uint4& a0 = tb.v[c >> 2];
-      uint4& a1 = tb.v[2 + (c >> 2)];
-      switch (c & 3) {
-        case 0: a0.x &= keep; a1.x &= keep; break;
-        case 1: a0.y &= keep; a1.y &= keep; break;
-        case 2: a0.z &= keep; a1.z &= keep; break;
-        default: a0.w &= keep; a1.w &= keep; break;
+    for (int t = 0; t < 4; ++t) {
+      const int key = 8 * khalf + 2 * t;  // first key of the lane's pair t
+      const uint32_t keep = key + 1 < nv ? 0xffffffffu : key < nv ? 0x0000ffffu : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        switch (t) {
+          case 0: tb.v[j].x &= keep; break;
+          case 1: tb.v[j].y &= keep; break;
+          case 2: tb.v[j].z &= keep; break;
+          default: tb.v[j].w &= keep; break;
+        }
       }
     }
   };
 
+  bool bad_blk = false;
   auto compute = [&](Tile& tb, int tt) {
+    bad_blk |= !tb.ok;
     if (!tb.ok || k0 + tt * 16 + 16 > k1) mask_v(tb, tt);
     const int key = k0 + tt * 16 + 2 * grp;
     const bool ok0 = tb.ok && key < k1;
@@ -190,8 +203,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
         tm = fmaxf(tm, __shfl_xor(tm, 32));
         if (tm > m[h]) {
           const float corr = fast_exp2(m[h] - tm);
-          acc[h][0] *= corr;
-          acc[h][1] *= corr;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[h][j] *= corr;
           l[h] *= corr;
           m[h] = tm;
         }
@@ -210,17 +223,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int h = 0; h < R; ++h) {
-      const uint4 pa = *reinterpret_cast<const uint4*>(&s_p[wave][h][0]);
-      const uint4 pb = *reinterpret_cast<const uint4*>(&s_p[wave][h][4]);
+      const uint4 pp = *reinterpret_cast<const uint4*>(&s_p[wave][h][4 * khalf]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[h][0] = dot2_bf16(comp(pa, i), comp(tb.v[0], i), acc[h][0]);
-        acc[h][1] = dot2_bf16(comp(pa, i), comp(tb.v[2], i), acc[h][1]);
-      }
+      for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[h][0] = dot2_bf16(comp(pb, i), comp(tb.v[1], i), acc[h][0]);
-        acc[h][1] = dot2_bf16(comp(pb, i), comp(tb.v[3], i), acc[h][1]);
+        for (int j = 0; j < 4; ++j) acc[h][j] = dot2_bf16(comp(pp, t), comp(tb.v[j], t), acc[h][j]);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -228,30 +235,31 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  Tile buf[DEPTH];
-#pragma unroll
-  for (int j = 0; j < DEPTH - 1; ++j) {
-    const int tt = wave + j * W;
-    if (tt < ntiles) load(buf[j], tt);
-  }
-  for (int base = 0; wave + base * W < ntiles; base += DEPTH) {
-#pragma unroll
-    for (int j = 0; j < DEPTH; ++j) {
-      const int tt = wave + (base + j) * W;
-      if (tt < ntiles) {
-        const int tn = tt + (DEPTH - 1) * W;
-        if (tn < ntiles) load(buf[(j + DEPTH - 1) % DEPTH], tn);
-        compute(buf[j], tt);
-      }
+  // Two register buffers; every iteration prefetches unconditionally (past
+  // the wave's last tile it re-reads that tile).
+  const int my_tiles = ntiles > wave ? (ntiles - wave + W - 1) / W : 0;
+  if (my_tiles > 0) {
+    auto at = [&](int i) { return min(i, my_tiles - 1); };
+    Tile ta, tb;
+    load(ta, 0);
+    for (int i = 0; i < my_tiles; i += 2) {
+      load(tb, at(i + 1));
+      compute(ta, wave + i * W);
+      load(ta, at(i + 2));
+      if (i + 1 < my_tiles) compute(tb, wave + (i + 1) * W);
     }
   }
+  if (bad_blk && lane == 0) raise_error(pool.err, kErrBlockId);
 
-  // Wave totals: each 8-lane group summed the weights of its own keys.
+  // Wave totals: each 8-lane group summed the weights of its own keys; each
+  // lane pair (l, l^1) holds the two key halves of the same four dims.
 #pragma unroll
   for (int h = 0; h < R; ++h) {
     l[h] += __shfl_xor(l[h], 8);
     l[h] += __shfl_xor(l[h], 16);
     l[h] += __shfl_xor(l[h], 32);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[h][j] += dpp<kDppXor1>(acc[h][j]);
   }
   if (lane == 0) {
 #pragma unroll
@@ -260,9 +268,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
       s_l[wave][h] = l[h];
     }
   }
+  if (khalf == 0) {
 #pragma unroll
-  for (int h = 0; h < R; ++h)
-    *reinterpret_cast<float2*>(&s_acc[wave][h][2 * lane]) = make_float2(acc[h][0], acc[h][1]);
+    for (int h = 0; h < R; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_acc[wave][h][32 * j + (lane >> 1)] = acc[h][j];
+    }
+  }
   __syncthreads();
 
   // Merge the W waves: thread handles (head, dim) pairs.
@@ -292,46 +304,54 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
       if (d == 0) plse[h] = L > 0.f ? M + __log2f(L) : -INFINITY;
     }
   }
-  if (single) return;
+}
 
-  // Last workgroup of (b, g) combines the ns partials in split order.
-  __threadfence();
-  __syncthreads();
-  uint32_t* ctr = a.counters + int64_t(b) * hkv + g;
-  if (tid == 0) {
-    const uint32_t ticket = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ticket == uint32_t(ns - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const float* po0 = a.part_o + (int64_t(b) * hkv + g) * a.max_splits * kPairs;
-  const float* pl0 = a.part_lse + (int64_t(b) * hkv + g) * a.max_splits * R;
-  for (int idx = tid; idx < kPairs; idx += 64 * W) {
-    const int h = idx >> 7;
-    float M = -INFINITY;
-    for (int k = 0; k < ns; ++k) M = fmaxf(M, pl0[k * R + h]);
-    float o = 0.f;
-    if (M != -INFINITY) {
-      float L = 0.f;
-      for (int k = 0; k < ns; ++k) {
-        const float lk = pl0[k * R + h];
-        const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
-        L += e;
-        o += e * po0[int64_t(k) * kPairs + idx];
-      }
-      o /= L;
+// Log-sum-exp combine of the split partials: one workgroup per (sequence,
+// query head), one thread per dim.  Partials are merged in split order, so
+// the result does not depend on the order in which split workgroups ran.
+// A separate launch: the kernel boundary makes the partials visible without
+// per-workgroup cache write-back fences.
+__global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, DecodeArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
+  const int g = h / r, hh = h - g * r;
+  const int n = a.ctx[b];
+  if (n <= 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * pool.block_size) return;
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;  // written directly by the split kernel
+  const int64_t unit = int64_t(b) * hkv + g;
+  const float* pl = a.part_lse + unit * a.max_splits * r + hh;
+  const float* po = a.part_o + (unit * a.max_splits * r + hh) * kHeadDim + d;
+  float M = -INFINITY;
+  for (int k = 0; k < ns; ++k) M = fmaxf(M, pl[k * r]);
+  float o = 0.f;
+  if (M != -INFINITY) {
+    float L = 0.f;
+    for (int k = 0; k < ns; ++k) {
+      const float lk = pl[k * r];
+      const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+      L += e;
+      o += e * po[int64_t(k) * r * kHeadDim];
     }
-    out_bg[idx] = f32_to_bf16(o);
+    o /= L;
   }
-  if (tid == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(o);
+}
+
+template <int R, int W, bool kStream>
+hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.max_splits, pool.num_kv_heads, a.batch);
+  hipLaunchKernelGGL((decode_kernel<R, W, kStream>), grid, dim3(64 * W), 0, stream, pool, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits == 1) return e;
+  hipLaunchKernelGGL(combine_kernel, dim3(a.num_q_heads, a.batch), dim3(kHeadDim), 0, stream, pool, a);
+  return hipGetLastError();
 }
 
 template <int R, int W>
 hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_splits, pool.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_kernel<R, W, 2>), grid, dim3(64 * W), 0, stream, pool, a);
-  return hipGetLastError();
+  if (a.stream_loads) return launch_rws<R, W, true>(pool, a, stream);
+  return launch_rws<R, W, false>(pool, a, stream);
 }
 
 template <int R>
@@ -351,8 +371,11 @@ DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   DecodeWorkspace w;
   const size_t units = size_t(batch) * num_kv_heads;
-  w.counters_off = 0;
-  w.part_o_off = up(units * sizeof(uint32_t));
+  if (max_splits <= 1) {
+    w.part_o_off = w.part_lse_off = w.total = 0;
+    return w;
+  }
+  w.part_o_off = 0;
   w.part_lse_off = w.part_o_off + up(units * max_splits * group * kHeadDim * sizeof(float));
   w.total = w.part_lse_off + up(units * max_splits * group * sizeof(float));
   return w;
@@ -360,7 +383,7 @@ DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int
 
 hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
-  if (a.split_tokens > kMaxSplitTokens) return hipErrorInvalidValue;
+  if (a.split_tokens > kMaxTilesPerWave * 16 * a.waves) return hipErrorInvalidValue;
   switch (a.num_q_heads / pool.num_kv_heads) {
     case 1: return launch_r<1>(pool, a, stream);
     case 2: return launch_r<2>(pool, a, stream);

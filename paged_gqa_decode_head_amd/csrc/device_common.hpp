@@ -9,6 +9,14 @@ namespace pgqa {
 constexpr int kHeadDim = 128;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load that is not kept in the caches (global_load ... nt):
+// K/V bytes are read once per launch.
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Sticky error bits, mirrored from include/pgqa.h.
 constexpr uint32_t kErrSeqId = 0x1u;

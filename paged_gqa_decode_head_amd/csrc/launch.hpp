@@ -40,9 +40,9 @@ struct DecodeArgs {
   int32_t batch; int32_t num_q_heads; int32_t max_ctx;
   float qk_scale_log2;   // softmax scale * log2(e)
   int32_t split_tokens; int32_t max_splits; int32_t waves;
+  int32_t stream_loads;  // 1: K/V loads carry the non-temporal (streaming) hint
   float* part_o;         // [batch][Hkv][max_splits][r][128]
   float* part_lse;       // [batch][Hkv][max_splits][r]
-  uint32_t* counters;    // [batch][Hkv], zero between calls
   uint16_t* out;
 };
 
@@ -50,7 +50,7 @@ hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, hipStream_t 
 
 // Workspace carve-up shared by the host API and the launchers.
 struct DecodeWorkspace {
-  size_t counters_off, part_o_off, part_lse_off, total;
+  size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
 };
 DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int32_t group, int32_t max_splits);
 
@@ -62,7 +62,7 @@ struct ChunkArgs {
   int32_t max_q_len; int32_t max_ctx;
   float qk_scale_log2;
   int32_t split_tokens; int32_t max_splits; int32_t q_tiles;
-  float* part_o; float* part_lse; uint32_t* counters;
+  float* part_o; float* part_lse;
   uint16_t* out;
 };
 

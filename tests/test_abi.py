@@ -76,14 +76,18 @@ def test_calls_reject_null_pool():
 @pytest.mark.parametrize("batch,hkv,ctx", [(1, 8, 32769), (64, 8, 2049), (8, 8, 4097), (64, 4, 1281),
                                             (2, 8, 101), (1, 1, 1), (512, 8, 100000)])
 def test_decode_plan_properties(cus, bs, batch, hkv, ctx):
-    p = pg.plan_decode(cus, bs, batch, hkv, 2 * hkv, ctx)
-    gran = max(bs, 64)
-    assert p.split_tokens % gran == 0
-    assert 0 < p.split_tokens <= 4096
-    assert p.max_splits == -(-ctx // p.split_tokens)          # covers every key, no empty tail split
-    assert p.waves_per_split in (1, 2, 4, 8)
-    if ctx >= 256 * 4 and batch * hkv < cus:
-        assert batch * hkv * p.max_splits >= cus                 # long contexts spread over the chip
+    for r in (1, 2, 8):
+        p = pg.plan_decode(cus, bs, batch, hkv, r * hkv, ctx)
+        gran = max(bs, 64)
+        assert p.split_tokens % gran == 0
+        assert 0 < p.split_tokens <= min(4096, 1024 * p.waves_per_split)
+        assert p.max_splits == -(-ctx // p.split_tokens)          # covers every key, no empty tail split
+        assert p.waves_per_split in (1, 2, 4, 8)
+        assert p.load_hint == 0
+        if 2 * batch * hkv >= cus:
+            assert p.max_splits == -(-ctx // min(4096, 1024 * p.waves_per_split)) or p.max_splits == 1
+        elif ctx >= 8192:
+            assert batch * hkv * p.max_splits >= cus // 4            # long contexts spread over the chip
 
 
 def test_plan_rejects_bad_input():
