@@ -193,9 +193,27 @@ pgqa_status pgqa_paged_decode_attention(
     void* workspace, size_t workspace_bytes,
     void* out, void* stream);
 
-/* Device workspace bytes a chunk call needs. */
+/*
+ * Split plan of a chunk call: each 32-row query tile (rows are (token, query
+ * head) pairs of one kv head) reads its keys in splits of split_tokens keys,
+ * one workgroup each, merged by a log-sum-exp combine when max_splits > 1.
+ */
+typedef struct {
+  int32_t split_tokens;  /* a multiple of max(block_size, 64), at most 4096 */
+  int32_t max_splits;    /* ceil(max_context_len / split_tokens) */
+  int32_t reserved0;     /* 0 */
+  int32_t reserved1;     /* 0 */
+} pgqa_chunk_plan;
+
+/* Host-only: the plan pgqa_paged_chunk_attention uses when given plan = NULL. */
+pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_segments, int32_t total_q,
+                            int32_t num_kv_heads, int32_t num_q_heads, int32_t max_q_len,
+                            int32_t max_context_len, pgqa_chunk_plan* out);
+
+/* Device workspace bytes a chunk call with this plan needs (plan = NULL: the default plan). */
 size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, int32_t total_q,
-                                  int32_t num_q_heads, int32_t max_q_len, int32_t max_context_len);
+                                  int32_t num_q_heads, int32_t max_q_len, int32_t max_context_len,
+                                  const pgqa_chunk_plan* plan);
 
 /*
  * a6: causal attention of short query chunks over the paged cache: chunked-
@@ -210,12 +228,16 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  *                   q_len tokens included (they must already be in the cache)
  *   block_tables    device int32 [num_segments][bt_stride]
  *   max_q_len, max_context_len  host hints >= the device values
+ *   plan            host, optional (NULL = pgqa_plan_chunk for this device)
  *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes
- *                   (no initial contents needed)
+ *                   (0 and NULL allowed for a one-split plan; no initial contents needed)
  *   out             device bf16 [total_q][num_q_heads][128]
  *
  * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits
- * at position n_s - q_len_s + i and attends to keys 0 .. that position.
+ * at position n_s - q_len_s + i and attends to keys 0 .. that position.  A
+ * segment whose metadata is inconsistent gets zero output rows and sets
+ * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  With more than one split the call
+ * enqueues two kernels (splits, then the combine).
  */
 pgqa_status pgqa_paged_chunk_attention(
     pgqa_pool* pool,
@@ -223,7 +245,8 @@ pgqa_status pgqa_paged_chunk_attention(
     const int32_t* block_tables, int32_t bt_stride,
     int32_t num_segments, int32_t total_q, int32_t num_q_heads,
     int32_t max_q_len, int32_t max_context_len,
-    float scale, void* workspace, size_t workspace_bytes,
+    float scale, const pgqa_chunk_plan* plan,
+    void* workspace, size_t workspace_bytes,
     void* out, void* stream);
 
 /* Static description of a status code. */

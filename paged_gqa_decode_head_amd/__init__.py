@@ -50,6 +50,14 @@ class DecodePlan(ctypes.Structure):
                 f"waves_per_split={self.waves_per_split}, load_hint={self.load_hint})")
 
 
+class ChunkPlan(ctypes.Structure):
+    _fields_ = [("split_tokens", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("reserved1", ctypes.c_int32)]
+
+    def __repr__(self):
+        return f"ChunkPlan(split_tokens={self.split_tokens}, max_splits={self.max_splits})"
+
+
 _lib = None
 
 _P, _I32, _I64, _SZ, _F32, _F64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
@@ -70,9 +78,11 @@ _SIGNATURES = {
     "pgqa_decode_workspace_bytes": ([_P, _I32, _I32, _I32, ctypes.POINTER(DecodePlan)], _SZ),
     "pgqa_paged_decode_attention": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, ctypes.POINTER(DecodePlan),
                                      _P, _SZ, _P, _P], ctypes.c_int),
-    "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32], _SZ),
-    "pgqa_paged_chunk_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32, _P, _SZ, _P,
-                                    _P], ctypes.c_int),
+    "pgqa_plan_chunk": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)],
+                        ctypes.c_int),
+    "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)], _SZ),
+    "pgqa_paged_chunk_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32,
+                                    ctypes.POINTER(ChunkPlan), _P, _SZ, _P, _P], ctypes.c_int),
 }
 
 
@@ -302,14 +312,28 @@ def paged_decode_attention(pool: Pool, q, context_lens, block_tables, max_contex
     return out
 
 
-def chunk_workspace_bytes(pool: Pool, num_segments, total_q, num_q_heads, max_q_len, max_context_len) -> int:
+def plan_chunk(num_cus, block_size, num_segments, total_q, num_kv_heads, num_q_heads, max_q_len,
+               max_context_len) -> ChunkPlan:
+    p = ChunkPlan()
+    _check(lib().pgqa_plan_chunk(num_cus, block_size, num_segments, total_q, num_kv_heads, num_q_heads,
+                                 max_q_len, max_context_len, ctypes.byref(p)))
+    return p
+
+
+def chunk_workspace_bytes(pool: Pool, num_segments, total_q, num_q_heads, max_q_len, max_context_len,
+                          plan: ChunkPlan = None) -> int:
     return int(lib().pgqa_chunk_workspace_bytes(pool.handle, num_segments, total_q, num_q_heads, max_q_len,
-                                                max_context_len))
+                                                max_context_len, None if plan is None else ctypes.byref(plan)))
 
 
 def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int,
-                          max_context_len: int, scale: float, workspace=None, out=None, stream=None):
-    """Causal chunk attention over the paged cache; returns out [total_q, Hq, 128] bf16."""
+                          max_context_len: int, scale: float, plan: ChunkPlan = None, workspace=None, out=None,
+                          stream=None):
+    """Causal chunk attention over the paged cache; returns out [total_q, Hq, 128] bf16.
+
+    Segment s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1 and
+    context_lens[s] keys (its own tokens included, already in the cache).
+    """
     import torch
 
     _require(q, "q", torch.bfloat16, pool.device)
@@ -321,15 +345,15 @@ def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_ta
     if out is None:
         out = torch.empty((Tq, hq, 128), dtype=torch.bfloat16, device=pool.device)
     _require(out, "out", torch.bfloat16, pool.device)
-    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len)))
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len), pp))
     if workspace is None:
         workspace = pool.workspace(need, "chunk")
     _check(lib().pgqa_paged_chunk_attention(
         pool.handle, _ptr(q), _ptr(query_start_loc), _ptr(context_lens), _ptr(block_tables), block_tables.shape[1],
-        N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), _ptr(workspace),
+        N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), pp, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
     return out
-
 
 class BoundCall:
     """A C-ABI call with its arguments marshalled once; calling it re-issues the
@@ -369,14 +393,15 @@ def bind_decode(pool: Pool, q, context_lens, block_tables, max_context_len: int,
 
 
 def bind_chunk(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int, max_context_len: int,
-               scale: float, out, workspace=None, stream=None) -> BoundCall:
+               scale: float, out, plan: ChunkPlan = None, workspace=None, stream=None) -> BoundCall:
     Tq, hq = q.shape[0], q.shape[1]
     N = context_lens.shape[0]
-    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len)))
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len), pp))
     if workspace is None:
         workspace = pool.workspace(need, "chunk")
-    keep = (q, query_start_loc, context_lens, block_tables, out, workspace)
+    keep = (q, query_start_loc, context_lens, block_tables, out, workspace, plan)
     args = (pool.handle, _ptr(q), _ptr(query_start_loc), _ptr(context_lens), _ptr(block_tables),
-            block_tables.shape[1], N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
+            block_tables.shape[1], N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), pp,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
     return BoundCall(lib().pgqa_paged_chunk_attention, args, keep)

@@ -406,21 +406,118 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   return PGQA_OK;
 }
 
+pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_segments, int32_t total_q,
+                            int32_t num_kv_heads, int32_t num_q_heads, int32_t max_q_len,
+                            int32_t max_context_len, pgqa_chunk_plan* out) {
+  if (out == nullptr) return fail(PGQA_ERR_INVALID_ARG, "out is NULL");
+  if (num_cus <= 0 || !valid_block_size(block_size) || num_segments < 0 || total_q < 0 || num_kv_heads <= 0 ||
+      num_q_heads <= 0 || max_q_len < 0 || max_context_len < 0)
+    return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
+  // About two workgroups per CU over the (row tile, kv head) units the hints
+  // allow, splits of 512 .. 4096 keys.
+  const int64_t r = num_q_heads / num_kv_heads;
+  const int64_t gran = block_size > 64 ? block_size : 64;
+  const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
+  const int64_t tiles = (int64_t(total_q) * r + 31) / 32 + num_segments;
+  const int64_t units = (tiles > 0 ? tiles : 1) * num_kv_heads;
+  const int64_t want = (2ll * num_cus + units - 1) / units;
+  int64_t split = round_up((ctx + want - 1) / want, gran);
+  if (split < 512) split = round_up(512, gran);
+  if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
+  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  out->split_tokens = int32_t(split);
+  out->max_splits = int32_t((ctx + split - 1) / split);
+  out->reserved0 = out->reserved1 = 0;
+  return PGQA_OK;
+}
+
 size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, int32_t total_q, int32_t num_q_heads,
-                                  int32_t max_q_len, int32_t max_context_len) {
-  (void)pool; (void)num_segments; (void)total_q; (void)num_q_heads; (void)max_q_len; (void)max_context_len;
-  return 0;
+                                  int32_t max_q_len, int32_t max_context_len, const pgqa_chunk_plan* plan) {
+  if (pool == nullptr || total_q < 0 || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return 0;
+  pgqa_chunk_plan p;
+  if (plan != nullptr) {
+    p = *plan;
+  } else if (pgqa_plan_chunk(pool->num_cus, pool->cfg.block_size, num_segments, total_q, pool->cfg.num_kv_heads,
+                             num_q_heads, max_q_len, max_context_len, &p) != PGQA_OK) {
+    return 0;
+  }
+  return chunk_workspace_layout(total_q, num_q_heads, p.max_splits).total;
 }
 
 pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
                                        const int32_t* context_lens, const int32_t* block_tables, int32_t bt_stride,
                                        int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t max_q_len,
-                                       int32_t max_context_len, float scale, void* workspace, size_t workspace_bytes,
-                                       void* out, void* stream) {
-  (void)pool; (void)q; (void)query_start_loc; (void)context_lens; (void)block_tables; (void)bt_stride;
-  (void)num_segments; (void)total_q; (void)num_q_heads; (void)max_q_len; (void)max_context_len; (void)scale;
-  (void)workspace; (void)workspace_bytes; (void)out; (void)stream;
-  return fail(PGQA_ERR_UNSUPPORTED, "chunk attention not built yet");
+                                       int32_t max_context_len, float scale, const pgqa_chunk_plan* plan,
+                                       void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  g_err[0] = 0;
+  PGQA_TRY(check_pool(pool));
+  PGQA_TRY(check_group(pool, num_q_heads));
+  const int32_t hkv = pool->cfg.num_kv_heads;
+  const int32_t r = num_q_heads / hkv;
+  if (num_segments < 0 || int64_t(num_segments) * hkv > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d (num_segments * num_kv_heads must be <= 65535)",
+                num_segments);
+  if (pool->cfg.max_batch_size > 0 && num_segments > pool->cfg.max_batch_size)
+    return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d exceeds max_batch_size=%d", num_segments,
+                pool->cfg.max_batch_size);
+  if (total_q < 0 || total_q > 65535 * 256)
+    return fail(PGQA_ERR_INVALID_ARG, "total_q=%d", total_q);
+  if (bt_stride <= 0) return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d", bt_stride);
+  if (max_q_len < 0 || max_context_len < max_q_len)
+    return fail(PGQA_ERR_INVALID_ARG, "max_q_len=%d max_context_len=%d", max_q_len, max_context_len);
+  if ((int64_t(max_q_len) * r + 31) / 32 > 65535) return fail(PGQA_ERR_INVALID_ARG, "max_q_len=%d", max_q_len);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PGQA_ERR_INVALID_ARG, "scale=%g", double(scale));
+  if (num_segments == 0 || total_q == 0) return PGQA_OK;
+  pgqa_chunk_plan p;
+  if (plan != nullptr) {
+    p = *plan;
+  } else {
+    PGQA_TRY(pgqa_plan_chunk(pool->num_cus, pool->cfg.block_size, num_segments, total_q, hkv, num_q_heads,
+                             max_q_len, max_context_len, &p));
+  }
+  const int32_t gran = pool->cfg.block_size > 64 ? pool->cfg.block_size : 64;
+  if (p.split_tokens <= 0 || p.split_tokens % gran != 0 || p.split_tokens > kMaxSplitTokens)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.split_tokens=%d must be a positive multiple of %d, at most %d",
+                p.split_tokens, gran, kMaxSplitTokens);
+  if (p.max_splits < (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens || p.max_splits > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
+                max_context_len);
+  const ChunkWorkspace wl = chunk_workspace_layout(total_q, num_q_heads, p.max_splits);
+  const int dev = pool->device;
+  PGQA_TRY(check_device_ptr(q, dev, "q", 16));
+  PGQA_TRY(check_device_ptr(query_start_loc, dev, "query_start_loc", 4));
+  PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
+  PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
+  PGQA_TRY(check_device_ptr(out, dev, "out"));
+  if (wl.total > 0) {
+    if (workspace == nullptr || workspace_bytes < wl.total)
+      return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", wl.total,
+                  workspace == nullptr ? size_t(0) : workspace_bytes);
+    PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  }
+  ChunkArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.qsl = query_start_loc;
+  a.ctx = context_lens;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_segments = num_segments;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.max_q_len = max_q_len;
+  a.max_ctx = max_context_len;
+  a.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
+  a.split_tokens = p.split_tokens;
+  a.max_splits = p.max_splits;
+  a.q_tiles = int32_t((int64_t(max_q_len) * r + 31) / 32);
+  char* ws = wl.total > 0 ? static_cast<char*>(workspace) : nullptr;
+  a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
+  a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  if (a.q_tiles == 0) return PGQA_OK;
+  hipError_t e = launch_chunk(pool->geom, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk launch");
+  return PGQA_OK;
 }
 
 }  // extern "C"

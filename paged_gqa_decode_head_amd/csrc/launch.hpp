@@ -68,4 +68,9 @@ struct ChunkArgs {
 
 hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream);
 
+struct ChunkWorkspace {
+  size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
+};
+ChunkWorkspace chunk_workspace_layout(int32_t total_q, int32_t num_q_heads, int32_t max_splits);
+
 }  // namespace pgqa

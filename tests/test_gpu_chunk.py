@@ -1,0 +1,195 @@
+"""GPU parity of paged causal chunk attention (chunked-prefill slices and
+b x (k+1) verify rows) against the fp64 reference, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import paged_gqa_decode_head_amd as pg
+from paged_gqa_decode_head_amd.workloads import SPECS, Group, StepSpec, make_step
+
+from harness import SCALE, SENTINEL, StepRun, bits_of, compare, dev_bf16, dev_i32, f64_of
+
+pytestmark = pytest.mark.gpu
+
+
+def _note(msg):
+    print(msg, flush=True)
+
+
+def test_cfg5_mixed_step_parity():
+    """The mixed Qwen3-1.7B step: 8 decode streams, a 512-token slice at offset
+    6144, 8 verify rows of 5 tokens; one write, one decode, one chunk call."""
+    _note("[chunk] cfg5")
+    w = make_step(SPECS["cfg5"])
+    run = StepRun(w)
+    run.write()
+    qd = run.decode_q()
+    out_d = run.decode(q=qd)
+    qc = run.chunk_q()
+    out_c = run.chunk(q=qc)
+    assert run.pool.check_errors() == 0
+    compare(out_d, run.oracle_decode_on_gpu_inputs(qd), "cfg5 decode")
+    ma, mr = compare(out_c, run.oracle_chunk_on_gpu_inputs(qc), "cfg5 chunk")
+    _note(f"  chunk max_abs={ma:.2e} mean_rel={mr:.2e}")
+
+
+def _chunk_spec(name, seed, hq, hkv, bs, segs, nb):
+    groups = tuple(Group(1, L, L, ql) for L, ql in segs)
+    return StepSpec(name, seed, hq, hkv, nb, chunks=groups, block_size=bs)
+
+
+SEGS = [(0, 7), (20, 5), (33, 1), (3, 40), (100, 64), (250, 33), (1, 1), (15, 17)]
+
+
+@pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
+                                       (16, 4, 256)])
+@pytest.mark.parametrize("split", [None, 64, 256, 4096])
+def test_chunk_small_ragged(hq, hkv, bs, split):
+    spec = _chunk_spec(f"chunk-{hq}-{hkv}-{bs}", 700 + hq + bs, hq, hkv, bs, SEGS, 256 if bs < 256 else 16)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    plan = None
+    if split is not None:
+        sp = max(split, bs)
+        plan = pg.ChunkPlan(sp, -(-int(w.chk_ctx.max()) // sp), 0, 0)
+    qlens = np.diff(w.chk_qsl)
+    out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, int(qlens.max()),
+                                   int(w.chk_ctx.max()), SCALE, plan=plan)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_chunk_on_gpu_inputs(q), f"{spec.name} split={split}")
+
+
+def test_chunk_q_len_one_matches_decode():
+    spec = StepSpec("chunk1", 720, 16, 8, 256, chunks=(Group(6, 1, 900, 1),))
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    out_c = run.chunk(q=q)
+    out_d = pg.paged_decode_attention(run.pool, q, run.chk_ctx, run.chk_bt, int(w.chk_ctx.max()), SCALE)
+    ref = run.oracle_chunk_on_gpu_inputs(q)
+    compare(out_c, ref, "chunk q_len=1")
+    compare(out_d, ref, "decode on the same rows")
+    d = np.abs(f64_of(out_c) - f64_of(out_d))
+    assert d.max() <= 2e-2
+
+
+def test_chunk_without_prefix_is_plain_causal_attention():
+    spec = _chunk_spec("causal0", 721, 16, 8, 16, [(0, 96), (0, 33)], 32)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    out = run.chunk(q=q)
+    # textbook causal attention over the dense K/V of each segment (torch SDPA, fp64, CPU)
+    pk, pv, bt_c = run.read_pool()
+    qf = f64_of(q)
+    for s in range(w.num_chunks):
+        n = int(w.chk_ctx[s])
+        K, V = [], []
+        for g in range(8):
+            kg, vg = O.gather_kv(pk, pv, bt_c[w.num_decode + s], n, g)
+            K.append(kg)
+            V.append(vg)
+        K, V = np.stack(K), np.stack(V)
+        q0, q1 = w.chk_qsl[s], w.chk_qsl[s + 1]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qf[q0:q1].transpose(1, 0, 2))[None], torch.from_numpy(K)[None],
+            torch.from_numpy(V)[None], is_causal=True, enable_gqa=True)[0].numpy().transpose(1, 0, 2)
+        compare(out[q0:q1], ref, f"causal segment {s}")
+
+
+def test_causal_boundary_probe():
+    """A key placed right after a query's position must not change that query's
+    output (bit-identical), and must change the next query's."""
+    spec = _chunk_spec("probe", 722, 4, 2, 16, [(20, 12)], 8)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    plan = pg.ChunkPlan(64, 1, 0, 0)
+    base = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 12, 32, SCALE,
+                                            plan=plan))
+    i = 5                                        # query i sits at position 20 + i
+    j = 20 + i + 1                               # the key right after it
+    blk, off = int(w.block_tables[w.num_decode, j // 16]), j % 16
+    kb, vb = run.pool.read_logical(blocks=[blk])
+    kk = kb.numpy().view(np.uint16).copy()
+    vv = vb.numpy().view(np.uint16).copy()
+    kk[0, off] = bits_of(q[i + 1, 0::2] * 40)   # each kv head: aligned with query i+1, huge score
+    vv[0, off] = O.f64_to_bf16_bits(np.full((2, 128), 50.0))
+    run.pool.fill_logical(kk.view(np.int16), vv.view(np.int16), blocks=[blk])
+    got = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 12, 32, SCALE,
+                                           plan=plan))
+    assert np.array_equal(got[: i + 1], base[: i + 1])
+    assert not np.array_equal(got[i + 1], base[i + 1])
+
+
+def test_chunk_block_permutation_bit_identical_and_deterministic():
+    spec = _chunk_spec("cperm", 723, 16, 8, 16, [(300, 40), (1000, 5), (64, 64)], 200)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    plan = pg.ChunkPlan(256, 5, 0, 0)
+    qlens = np.diff(w.chk_qsl)
+    call = lambda pool, bt: bits_of(pg.paged_chunk_attention(pool, q, run.chk_qsl, run.chk_ctx, bt,
+                                                             int(qlens.max()), int(w.chk_ctx.max()), SCALE,
+                                                             plan=plan))
+    a = call(run.pool, run.chk_bt)
+    assert np.array_equal(a, call(run.pool, run.chk_bt))
+    pk, pv, bt_c = run.read_pool()
+    rng = np.random.default_rng(9)
+    new_ids = rng.permutation(w.spec.num_blocks)[: len(run.used)]
+    pool2 = pg.Pool(w.spec.num_blocks, 16, 8)
+    pool2.fill_logical(pk.view(np.int16), pv.view(np.int16), blocks=new_ids)
+    bt2 = np.where(bt_c >= 0, new_ids[np.maximum(bt_c, 0)], -1).astype(np.int32)
+    assert np.array_equal(a, call(pool2, dev_i32(bt2[w.num_decode:])))
+
+
+def test_chunk_ignores_garbage_past_the_context():
+    spec = _chunk_spec("cgarb", 724, 16, 8, 16, [(10, 7), (50, 30), (0, 3)], 40)
+    w = make_step(spec)
+    run = StepRun(w, fill_prefix=False)
+    s = w.spec
+    k = np.full((s.num_blocks, 16, 8, 128), SENTINEL, dtype=np.uint16)
+    v = k.copy()
+    for row in range(w.num_chunks):
+        L = int(w.chk_ctx[row]) - int(np.diff(w.chk_qsl)[row])
+        for j in range(L):
+            blk, off = w.block_tables[row, j // 16], j % 16
+            k[blk, off] = w.prefix_k[blk, off]
+            v[blk, off] = w.prefix_v[blk, off]
+    run.pool.fill_logical(k.view(np.int16), v.view(np.int16))
+    run.write()
+    q = run.chunk_q()
+    for split in (None, 64):
+        plan = None if split is None else pg.ChunkPlan(64, 2, 0, 0)
+        out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 30, 80, SCALE, plan=plan)
+        compare(out, run.oracle_chunk_on_gpu_inputs(q), f"chunk garbage split={split}")
+
+
+def test_chunk_bad_metadata_flags_and_zero_rows():
+    spec = _chunk_spec("cbad", 725, 16, 8, 16, [(10, 4), (20, 6)], 16)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    # second segment claims fewer keys than query tokens
+    ctx = dev_i32(np.array([14, 3], dtype=np.int32))
+    out = torch.full((10, 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    pg.paged_chunk_attention(run.pool, q, run.chk_qsl, ctx, run.chk_bt, 6, 26, SCALE, out=out)
+    assert run.pool.check_errors() & pg.DEVERR_QUERY
+    assert torch.all(out[4:] == 0)
+    assert torch.all(torch.isfinite(out[:4].float()))
+    # query_start_loc past total_q
+    qsl = dev_i32(np.array([0, 4, 99], dtype=np.int32))
+    pg.paged_chunk_attention(run.pool, q, qsl, run.chk_ctx, run.chk_bt, 6, 26, SCALE, out=out)
+    assert run.pool.check_errors() & pg.DEVERR_QUERY
+    # empty call
+    pg.paged_chunk_attention(run.pool, q[:0], run.chk_qsl[:1], run.chk_ctx[:0], run.chk_bt[:0], 0, 0, SCALE,
+                             out=out[:0])
+    assert run.pool.check_errors() == 0
