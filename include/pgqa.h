@@ -113,14 +113,16 @@ pgqa_status pgqa_pool_check_errors(pgqa_pool* pool, void* stream, uint32_t* flag
  *   k  device bf16 [num_tokens][Hkv][128], token stride k_row_stride
  *   v  device bf16 [num_tokens][Hkv][128], token stride v_row_stride
  *      (strides allow q/k/v to be views of one fused projection output; each
- *       stride is >= heads*128 and the head/dim axes are dense)
- *   q_norm_weight, k_norm_weight  device bf16 [128], shared by all heads
+ *       stride is >= heads*128 and a multiple of 8, the head/dim axes are dense,
+ *       and q, k, v are 16-byte aligned)
+ *   q_norm_weight, k_norm_weight  device bf16 [128], shared by all heads, 16-byte aligned
  *   positions  device int32 [num_tokens]: absolute 0-based position of each token
  *   seq_ids    device int32 [num_tokens]: row of block_tables holding its sequence
  *   block_tables device int32 [num_seqs][bt_stride]
  *   eps        RMSNorm epsilon (inside the square root), >= 0
  *   rope_theta rotary base (inverse frequency theta^(-2i/128)), > 0
- *   q_out      device bf16 [num_tokens][num_q_heads][128], dense
+ *   q_out      device bf16 [num_tokens][num_q_heads][128], dense, 16-byte aligned
+ *   (num_q_heads + 2 * Hkv <= 128)
  *
  * For token t: y = x / sqrt(mean(x^2) + eps) * w per head row, then each pair
  * (i, i+64) is rotated by positions[t] * theta^(-2i/128); k' and v go to slot
@@ -194,9 +196,9 @@ pgqa_status pgqa_paged_decode_attention(
     void* out, void* stream);
 
 /*
- * Split plan of a chunk call: each 32-row query tile (rows are (token, query
- * head) pairs of one kv head) reads its keys in splits of split_tokens keys,
- * one workgroup each, merged by a log-sum-exp combine when max_splits > 1.
+ * Split plan of a chunk call: each group of 256 query rows (rows are (token,
+ * query head) pairs of one kv head) reads its keys in splits of split_tokens
+ * keys, one workgroup each, merged by a log-sum-exp combine when max_splits > 1.
  */
 typedef struct {
   int32_t split_tokens;  /* a multiple of max(block_size, 64), at most 4096 */
@@ -229,15 +231,17 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  *   block_tables    device int32 [num_segments][bt_stride]
  *   max_q_len, max_context_len  host hints >= the device values
  *   plan            host, optional (NULL = pgqa_plan_chunk for this device)
- *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes
- *                   (0 and NULL allowed for a one-split plan; no initial contents needed)
+ *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes for
+ *                   the device-built work list and the split partials (no initial
+ *                   contents needed)
  *   out             device bf16 [total_q][num_q_heads][128]
  *
  * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits
  * at position n_s - q_len_s + i and attends to keys 0 .. that position.  A
  * segment whose metadata is inconsistent gets zero output rows and sets
- * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  With more than one split the call
- * enqueues two kernels (splits, then the combine).
+ * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  The call enqueues a one-workgroup
+ * schedule kernel (it lists the work items the device metadata calls for), the
+ * attention kernel and, with more than one split, the combine.
  */
 pgqa_status pgqa_paged_chunk_attention(
     pgqa_pool* pool,

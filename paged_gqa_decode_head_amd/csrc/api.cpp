@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "../../include/pgqa.h"
@@ -27,6 +28,10 @@ struct pgqa_pool {
   PoolGeom geom;
   int device;
   int num_cus;
+  // Rotary turn frequencies of the last rope_theta seen (host, fp64).
+  std::mutex rope_mu;
+  double rope_theta = 0.0;
+  double rev_freq[64];
 };
 
 namespace {
@@ -254,20 +259,25 @@ pgqa_status pgqa_rms_norm_rope_cache_write(pgqa_pool* pool, const void* q, int64
   if (q_row_stride < int64_t(num_q_heads) * 128 || k_row_stride < hkv * 128 || v_row_stride < hkv * 128)
     return fail(PGQA_ERR_INVALID_ARG, "row strides (%lld, %lld, %lld) below the dense row length",
                 (long long)q_row_stride, (long long)k_row_stride, (long long)v_row_stride);
+  if (q_row_stride % 8 || k_row_stride % 8 || v_row_stride % 8)
+    return fail(PGQA_ERR_INVALID_ARG, "row strides must be multiples of 8 elements");
+  if (num_q_heads + 2 * hkv > 128)
+    return fail(PGQA_ERR_UNSUPPORTED, "num_q_heads + 2 * num_kv_heads = %lld (at most 128)",
+                (long long)(num_q_heads + 2 * hkv));
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(PGQA_ERR_INVALID_ARG, "eps=%g", double(eps));
   if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
     return fail(PGQA_ERR_INVALID_ARG, "rope_theta=%g", rope_theta);
   if (num_tokens == 0) return PGQA_OK;
   const int dev = pool->device;
-  PGQA_TRY(check_device_ptr(q, dev, "q"));
-  PGQA_TRY(check_device_ptr(k, dev, "k"));
-  PGQA_TRY(check_device_ptr(v, dev, "v"));
-  PGQA_TRY(check_device_ptr(q_norm_weight, dev, "q_norm_weight"));
-  PGQA_TRY(check_device_ptr(k_norm_weight, dev, "k_norm_weight"));
+  PGQA_TRY(check_device_ptr(q, dev, "q", 16));
+  PGQA_TRY(check_device_ptr(k, dev, "k", 16));
+  PGQA_TRY(check_device_ptr(v, dev, "v", 16));
+  PGQA_TRY(check_device_ptr(q_norm_weight, dev, "q_norm_weight", 16));
+  PGQA_TRY(check_device_ptr(k_norm_weight, dev, "k_norm_weight", 16));
   PGQA_TRY(check_device_ptr(positions, dev, "positions", 4));
   PGQA_TRY(check_device_ptr(seq_ids, dev, "seq_ids", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
-  PGQA_TRY(check_device_ptr(q_out, dev, "q_out"));
+  PGQA_TRY(check_device_ptr(q_out, dev, "q_out", 16));
   WriteArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.q_stride = q_row_stride;
@@ -285,7 +295,14 @@ pgqa_status pgqa_rms_norm_rope_cache_write(pgqa_pool* pool, const void* q, int64
   a.num_tokens = num_tokens;
   a.num_q_heads = num_q_heads;
   a.eps = eps;
-  a.theta = rope_theta;
+  {
+    std::lock_guard<std::mutex> lock(pool->rope_mu);
+    if (pool->rope_theta != rope_theta) {
+      for (int i = 0; i < 64; ++i) pool->rev_freq[i] = std::pow(rope_theta, -2.0 * i / 128.0) / (2.0 * M_PI);
+      pool->rope_theta = rope_theta;
+    }
+    std::memcpy(a.rev_freq, pool->rev_freq, sizeof(a.rev_freq));
+  }
   a.q_out = static_cast<uint16_t*>(q_out);
   hipError_t e = launch_cache_write(pool->geom, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache write launch");
@@ -413,18 +430,19 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
   if (num_cus <= 0 || !valid_block_size(block_size) || num_segments < 0 || total_q < 0 || num_kv_heads <= 0 ||
       num_q_heads <= 0 || max_q_len < 0 || max_context_len < 0)
     return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
-  // About two workgroups per CU over the (row tile, kv head) units the hints
-  // allow, splits of 512 .. 4096 keys.
+  // A work item is 8 query-row tiles of 32 rows (256 rows) of one segment and
+  // kv head over one key split.  Aim at about two items per CU over the
+  // (tile group, kv head) units the hints allow; splits of 256 .. 4096 keys.
   const int64_t r = num_q_heads / num_kv_heads;
   const int64_t gran = block_size > 64 ? block_size : 64;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int64_t tiles = (int64_t(total_q) * r + 31) / 32 + num_segments;
-  const int64_t units = (tiles > 0 ? tiles : 1) * num_kv_heads;
+  const int64_t groups = (int64_t(total_q) * r + 255) / 256 + num_segments;
+  const int64_t units = (groups > 0 ? groups : 1) * num_kv_heads;
   const int64_t want = (2ll * num_cus + units - 1) / units;
   int64_t split = round_up((ctx + want - 1) / want, gran);
-  if (split < 512) split = round_up(512, gran);
+  if (split < 256) split = round_up(256, gran);
   if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
-  if (split > kMaxSplitTokens) split = kMaxSplitTokens;
+  if (split > kMaxSplitTokens) split = kMaxSplitTokens / gran * gran;
   out->split_tokens = int32_t(split);
   out->max_splits = int32_t((ctx + split - 1) / split);
   out->reserved0 = out->reserved1 = 0;
@@ -441,7 +459,7 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
                              num_q_heads, max_q_len, max_context_len, &p) != PGQA_OK) {
     return 0;
   }
-  return chunk_workspace_layout(total_q, num_q_heads, p.max_splits).total;
+  return chunk_workspace_layout(num_segments, total_q, pool->cfg.num_kv_heads, num_q_heads, p.max_splits).total;
 }
 
 pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
@@ -465,7 +483,6 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   if (bt_stride <= 0) return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d", bt_stride);
   if (max_q_len < 0 || max_context_len < max_q_len)
     return fail(PGQA_ERR_INVALID_ARG, "max_q_len=%d max_context_len=%d", max_q_len, max_context_len);
-  if ((int64_t(max_q_len) * r + 31) / 32 > 65535) return fail(PGQA_ERR_INVALID_ARG, "max_q_len=%d", max_q_len);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PGQA_ERR_INVALID_ARG, "scale=%g", double(scale));
   if (num_segments == 0 || total_q == 0) return PGQA_OK;
   pgqa_chunk_plan p;
@@ -482,19 +499,19 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   if (p.max_splits < (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens || p.max_splits > 65535)
     return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
                 max_context_len);
-  const ChunkWorkspace wl = chunk_workspace_layout(total_q, num_q_heads, p.max_splits);
+  const ChunkWorkspace wl = chunk_workspace_layout(num_segments, total_q, hkv, num_q_heads, p.max_splits);
+  const int64_t max_items = chunk_max_items(num_segments, total_q, hkv, r, p.max_splits);
+  if (max_items > 0x7fffffff) return fail(PGQA_ERR_INVALID_ARG, "too many work items (%lld)", (long long)max_items);
   const int dev = pool->device;
   PGQA_TRY(check_device_ptr(q, dev, "q", 16));
   PGQA_TRY(check_device_ptr(query_start_loc, dev, "query_start_loc", 4));
   PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
-  PGQA_TRY(check_device_ptr(out, dev, "out"));
-  if (wl.total > 0) {
-    if (workspace == nullptr || workspace_bytes < wl.total)
-      return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", wl.total,
-                  workspace == nullptr ? size_t(0) : workspace_bytes);
-    PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
-  }
+  PGQA_TRY(check_device_ptr(out, dev, "out", 8));
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", wl.total,
+                workspace == nullptr ? size_t(0) : workspace_bytes);
+  PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
   ChunkArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.qsl = query_start_loc;
@@ -509,12 +526,14 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   a.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
   a.split_tokens = p.split_tokens;
   a.max_splits = p.max_splits;
-  a.q_tiles = int32_t((int64_t(max_q_len) * r + 31) / 32);
-  char* ws = wl.total > 0 ? static_cast<char*>(workspace) : nullptr;
-  a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
-  a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
+  a.max_items = int32_t(max_items);
+  char* ws = static_cast<char*>(workspace);
+  a.item_count = reinterpret_cast<int32_t*>(ws + wl.count_off);
+  a.seg_off = reinterpret_cast<int32_t*>(ws + wl.seg_off_off);
+  a.items = reinterpret_cast<int4*>(ws + wl.items_off);
+  a.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
+  a.part_lse = p.max_splits > 1 ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
   a.out = static_cast<uint16_t*>(out);
-  if (a.q_tiles == 0) return PGQA_OK;
   hipError_t e = launch_chunk(pool->geom, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk launch");
   return PGQA_OK;

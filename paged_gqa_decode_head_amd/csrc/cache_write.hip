@@ -7,27 +7,63 @@
 // cache write is folded into the same launch, so a decode step's q/k/v are read
 // once and the normed/rotated k is never stored anywhere but its cache slot.
 //
-// One workgroup of four waves per token.  Each wave takes whole 128-element
-// head rows; lane l holds dims l and l + 64, which are exactly the two members
-// of rotary pair l, so the rotation is lane-local and only the sum of squares
-// needs a cross-lane reduction.  The launch moves about 1 MB for a 64-token
-// decode step, so it is bound by launch latency rather than bandwidth.
+// One workgroup per token; 8 lanes per 128-element head row (q rows, then k
+// rows, then v rows).  Lane s of a row holds dims 8s..8s+7 and 64+8s..64+8s+7:
+// the two members of each of its 8 rotary pairs, so the rotation is lane-local
+// and the sum of squares needs three DPP steps.  All loads are issued before
+// any dependent work.  A decode step moves about 1 MB here, so the launch is
+// bound by latency, not bandwidth.
+//
+// Rotation angles: pair i of a token at position p turns by p * theta^(-2i/128)
+// radians.  At p near 32768 an fp32 product is already off by ~2e-3 rad, so the
+// angle is reduced in fp64 as a fraction of a turn, frac(p * f_i / 2pi), and
+// only that fraction (exact to ~1e-12) goes to an fp32 sincos.  The 64 values
+// f_i / 2pi come from the host in fp64.
+#include <math.h>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
 namespace pgqa {
 namespace {
 
-constexpr int kWaves = 4;
-
-__global__ __launch_bounds__(64 * kWaves) void cache_write_kernel(PoolGeom pool, WriteArgs a) {
+__global__ __launch_bounds__(1024) void cache_write_kernel(PoolGeom pool, WriteArgs a) {
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int row = tid >> 3, s = tid & 7;
   const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
+  const int rows = hq + 2 * hkv;
+
+  __shared__ float s_cos[64], s_sin[64];
 
   const int pos = a.pos[t];
   const int seq = a.seq[t];
+  // Issue this lane's row loads first.
+  const bool active = row < rows;
+  const bool is_q = row < hq, is_k = !is_q && row < hq + hkv;
+  const int h = is_q ? row : is_k ? row - hq : row - hq - hkv;
+  uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0, w0 = x0, w1 = x0;
+  if (active) {
+    const uint16_t* src = is_q ? a.q + int64_t(t) * a.q_stride + h * kHeadDim
+                               : is_k ? a.k + int64_t(t) * a.k_stride + h * kHeadDim
+                                      : a.v + int64_t(t) * a.v_stride + h * kHeadDim;
+    x0 = *reinterpret_cast<const uint4*>(src + 8 * s);
+    x1 = *reinterpret_cast<const uint4*>(src + 64 + 8 * s);
+    if (is_q || is_k) {
+      const uint16_t* wt = is_q ? a.wq : a.wk;
+      w0 = *reinterpret_cast<const uint4*>(wt + 8 * s);
+      w1 = *reinterpret_cast<const uint4*>(wt + 64 + 8 * s);
+    }
+  }
+  if (tid < 64) {
+    const double turns = double(pos) * a.rev_freq[tid];
+    const float ang = float((turns - floor(turns)) * 6.283185307179586);
+    float sn, cs;
+    sincosf(ang, &sn, &cs);
+    s_cos[tid] = cs;
+    s_sin[tid] = sn;
+  }
+
   uint32_t bad = 0;
   int32_t blk = 0;
   if (seq < 0 || seq >= a.num_seqs) {
@@ -38,50 +74,70 @@ __global__ __launch_bounds__(64 * kWaves) void cache_write_kernel(PoolGeom pool,
     blk = a.bt[int64_t(seq) * a.bt_stride + pos / bs];
     if (blk < 0 || blk >= pool.num_blocks) bad = kErrBlockId;
   }
-  if (bad && threadIdx.x == 0) raise_error(pool.err, bad);
+  if (bad && tid == 0) raise_error(pool.err, bad);
   const int off = pos & (bs - 1);
+  __syncthreads();
+  if (!active) return;
 
-  // Rotation of pair `lane` at this token's position, from an fp64 angle: at
-  // positions near 32768 an fp32 product p * f_i would already be off by
-  // ~2e-3 rad.  sincos of the fp64 angle, then rounded to fp32.
-  const double inv_freq = pow(a.theta, -2.0 * lane / double(kHeadDim));
-  double sd, cd;
-  sincos(double(pos) * inv_freq, &sd, &cd);
-  const float sn = float(sd), cs = float(cd);
-
-  const int rows = hq + 2 * hkv;
-  for (int row = wave; row < rows; row += kWaves) {
-    if (row < hq + hkv) {
-      const bool is_q = row < hq;
-      const int h = is_q ? row : row - hq;
-      const uint16_t* src = is_q ? a.q + int64_t(t) * a.q_stride + h * kHeadDim
-                                 : a.k + int64_t(t) * a.k_stride + h * kHeadDim;
-      const uint16_t* w = is_q ? a.wq : a.wk;
-      const float x0 = bf16_to_f32(src[lane]);
-      const float x1 = bf16_to_f32(src[lane + 64]);
-      const float ms = wave_sum(x0 * x0 + x1 * x1) * (1.0f / kHeadDim);
-      const float inv = 1.0f / sqrtf(ms + a.eps);
-      const float y0 = x0 * inv * bf16_to_f32(w[lane]);
-      const float y1 = x1 * inv * bf16_to_f32(w[lane + 64]);
-      const uint16_t o0 = f32_to_bf16(y0 * cs - y1 * sn);
-      const uint16_t o1 = f32_to_bf16(y1 * cs + y0 * sn);
-      if (is_q) {
-        uint16_t* dst = a.q_out + (int64_t(t) * hq + h) * kHeadDim;
-        dst[lane] = o0;
-        dst[lane + 64] = o1;
-      } else if (!bad) {
-        uint16_t* dst = pool.kv + (int64_t(blk) * hkv + h) * tile_elems(pool) + int64_t(off) * kHeadDim;
-        dst[lane] = o0;
-        dst[lane + 64] = o1;
-      }
-    } else if (!bad) {
-      // v is stored as it came, transposed: V^T[dim][slot].
-      const int h = row - hq - hkv;
-      const uint16_t* src = a.v + int64_t(t) * a.v_stride + h * kHeadDim;
-      uint16_t* dst = pool.kv + (int64_t(blk) * hkv + h) * tile_elems(pool) + int64_t(bs) * kHeadDim + off;
-      dst[int64_t(lane) * bs] = src[lane];
-      dst[int64_t(lane + 64) * bs] = src[lane + 64];
+  uint16_t* kv_tile = pool.kv + (int64_t(blk) * hkv + h) * tile_elems(pool);
+  if (!is_q && !is_k) {
+    if (bad) return;
+    // v goes into the cache as it came, transposed: V^T[dim][slot].
+    uint16_t* dst = kv_tile + int64_t(bs) * kHeadDim + off;
+    const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      dst[int64_t(8 * s + 2 * e) * bs] = uint16_t(lo[e]);
+      dst[int64_t(8 * s + 2 * e + 1) * bs] = uint16_t(lo[e] >> 16);
+      dst[int64_t(64 + 8 * s + 2 * e) * bs] = uint16_t(hi[e]);
+      dst[int64_t(64 + 8 * s + 2 * e + 1) * bs] = uint16_t(hi[e] >> 16);
     }
+    return;
+  }
+
+  float y0[8], y1[8];
+  const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y0[2 * e] = bf16_lo(a0[e]);
+    y0[2 * e + 1] = bf16_hi(a0[e]);
+    y1[2 * e] = bf16_lo(a1[e]);
+    y1[2 * e + 1] = bf16_hi(a1[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += y0[e] * y0[e] + y1[e] * y1[e];
+  const float ms = sum8(ss) * (1.0f / kHeadDim);
+  const float inv = 1.0f / sqrtf(ms + a.eps);
+  const uint32_t g0[4] = {w0.x, w0.y, w0.z, w0.w}, g1[4] = {w1.x, w1.y, w1.z, w1.w};
+  uint32_t o0[4], o1[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float r0[2], r1[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = 8 * s + 2 * e + u;  // rotary pair (i, i + 64)
+      const float wa = u ? bf16_hi(g0[e]) : bf16_lo(g0[e]);
+      const float wb = u ? bf16_hi(g1[e]) : bf16_lo(g1[e]);
+      const float ya = y0[2 * e + u] * inv * wa;
+      const float yb = y1[2 * e + u] * inv * wb;
+      const float cs = s_cos[i], sn = s_sin[i];
+      r0[u] = ya * cs - yb * sn;
+      r1[u] = yb * cs + ya * sn;
+    }
+    o0[e] = pack_bf16x2(r0[0], r0[1]);
+    o1[e] = pack_bf16x2(r1[0], r1[1]);
+  }
+  const uint4 out0 = make_uint4(o0[0], o0[1], o0[2], o0[3]);
+  const uint4 out1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+  if (is_q) {
+    uint16_t* dst = a.q_out + (int64_t(t) * hq + h) * kHeadDim;
+    *reinterpret_cast<uint4*>(dst + 8 * s) = out0;
+    *reinterpret_cast<uint4*>(dst + 64 + 8 * s) = out1;
+  } else if (!bad) {
+    uint16_t* dst = kv_tile + int64_t(off) * kHeadDim;
+    *reinterpret_cast<uint4*>(dst + 8 * s) = out0;
+    *reinterpret_cast<uint4*>(dst + 64 + 8 * s) = out1;
   }
 }
 
@@ -89,7 +145,10 @@ __global__ __launch_bounds__(64 * kWaves) void cache_write_kernel(PoolGeom pool,
 
 hipError_t launch_cache_write(const PoolGeom& pool, const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
-  hipLaunchKernelGGL(cache_write_kernel, dim3(a.num_tokens), dim3(64 * kWaves), 0, stream, pool, a);
+  const int rows = a.num_q_heads + 2 * pool.num_kv_heads;
+  const int threads = (rows * 8 + 63) / 64 * 64;
+  if (threads > 1024) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cache_write_kernel, dim3(a.num_tokens), dim3(threads), 0, stream, pool, a);
   return hipGetLastError();
 }
 

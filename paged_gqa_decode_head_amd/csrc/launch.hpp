@@ -27,7 +27,8 @@ struct WriteArgs {
   const int32_t* pos; const int32_t* seq;
   const int32_t* bt; int32_t bt_stride; int32_t num_seqs;
   int32_t num_tokens; int32_t num_q_heads;
-  float eps; double theta;
+  float eps;
+  double rev_freq[64];   // theta^(-2i/128) / (2 pi): turns per position of rotary pair i
   uint16_t* q_out;
 };
 
@@ -61,7 +62,11 @@ struct ChunkArgs {
   int32_t num_segments; int32_t total_q; int32_t num_q_heads;
   int32_t max_q_len; int32_t max_ctx;
   float qk_scale_log2;
-  int32_t split_tokens; int32_t max_splits; int32_t q_tiles;
+  int32_t split_tokens; int32_t max_splits;
+  int32_t max_items;     // grid of the main kernel: an upper bound of the work items
+  int32_t* item_count;   // written by the schedule kernel
+  int32_t* seg_off;      // [num_segments + 1] first item of each segment (schedule kernel)
+  int4* items;           // {segment, kv head, tile group, split}
   float* part_o; float* part_lse;
   uint16_t* out;
 };
@@ -69,8 +74,11 @@ struct ChunkArgs {
 hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream);
 
 struct ChunkWorkspace {
-  size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
+  size_t count_off, seg_off_off, items_off, part_o_off, part_lse_off, total;
 };
-ChunkWorkspace chunk_workspace_layout(int32_t total_q, int32_t num_q_heads, int32_t max_splits);
+int64_t chunk_max_items(int32_t num_segments, int32_t total_q, int32_t num_kv_heads, int32_t group,
+                        int32_t max_splits);
+ChunkWorkspace chunk_workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_kv_heads,
+                                      int32_t num_q_heads, int32_t max_splits);
 
 }  // namespace pgqa

@@ -39,7 +39,7 @@ def _chunk_spec(name, seed, hq, hkv, bs, segs, nb):
     return StepSpec(name, seed, hq, hkv, nb, chunks=groups, block_size=bs)
 
 
-SEGS = [(0, 7), (20, 5), (33, 1), (3, 40), (100, 64), (250, 33), (1, 1), (15, 17)]
+SEGS = [(0, 7), (20, 5), (33, 1), (3, 40), (9, 0), (100, 64), (250, 33), (1, 1), (15, 17)]
 
 
 @pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
