@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn HBM GB/s (% of peak) + seqs/s, Qwen3-1.7B shapes"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def decode_alg_bytes(w) -> int:
@@ -47,6 +48,134 @@ def write_alg_bytes(w) -> int:
     rows_in = T * (s.num_q_heads + 2 * s.num_kv_heads) * 128 * 2
     rows_out = T * (s.num_q_heads + 2 * s.num_kv_heads) * 128 * 2
     return rows_in + rows_out + 2 * 128 * 2 + T * 12
+
+
+def chunk_alg(w, qsl, ctx):
+    """(flops, KV bytes) of causal chunk attention: 4*D*Hq per visible (query, key)
+    pair (QK^T and PV), and the K/V rows of each segment read once."""
+    s = w.spec
+    pairs = 0
+    for i in range(len(ctx)):
+        ql, n = int(qsl[i + 1] - qsl[i]), int(ctx[i])
+        pairs += ql * (n - ql) + ql * (ql + 1) // 2
+    kv = int(ctx.astype("int64").sum()) * s.num_kv_heads * 128 * 2 * 2
+    return 4 * 128 * s.num_q_heads * pairs, kv
+
+
+def time_calls(calls, iters, warmup=3):
+    """Median and mean microseconds of each call (HIP events on the current stream)."""
+    import torch
+
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        calls[i % len(calls)]()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    return ts[len(ts) // 2], sum(ts) / len(ts)
+
+
+def measure_rows(args, dev):
+    """Every hot-path row on its own synthetic workload: decode on each decode
+    workload, chunk attention (slice, verify rows, both) on the mixed step."""
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_head_amd as pg
+    from paged_gqa_decode_head_amd.workloads import SPECS, make_step
+
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    scale = 1.0 / math.sqrt(128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    rows = {"decode": {}, "cache_write": {}}
+    for name in ("cfg2", "cfg3a", "cfg4", "cfg5"):
+        w = make_step(SPECS[name])
+        s = w.spec
+        pools = []
+        for _ in range(2):
+            p = pg.Pool(s.num_blocks, s.block_size, s.num_kv_heads, device=dev)
+            p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
+                           blocks=w.used_blocks)
+            pools.append(p)
+        q, k, v = to_bf16(w.tok_q), to_bf16(w.tok_k), to_bf16(w.tok_v)
+        q_out = torch.empty((w.num_tokens, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+        writes = [pg.bind_cache_write(p, q, k, v, to_bf16(w.wq), to_bf16(w.wk), to_i32(w.tok_pos), to_i32(w.tok_seq),
+                                      to_i32(w.block_tables), s.eps, s.rope_theta, q_out) for p in pools]
+        med, _ = time_calls(writes, 20)
+        rows["cache_write"][name] = {"tokens": w.num_tokens, "us": round(med, 2),
+                                     "alg_bytes": write_alg_bytes(w), "bound": "latency"}
+        for wr in writes:
+            wr()
+        qd = q_out[torch.from_numpy(w.dec_tok.astype(np.int64)).to(dev)].contiguous()
+        ctx, bt = to_i32(w.dec_ctx), to_i32(w.dec_block_tables)
+        mx = int(w.dec_ctx.max())
+        out = torch.empty((w.num_decode, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+        plan = pg.plan_decode(cus, s.block_size, w.num_decode, s.num_kv_heads, s.num_q_heads, mx)
+        calls = [pg.bind_decode(p, qd, ctx, bt, mx, scale, out, plan=plan) for p in pools]
+        med, mean = time_calls(calls, 40)
+        nb = decode_alg_bytes(w)
+        rows["decode"][name] = {"batch": w.num_decode, "keys": int(w.dec_ctx.sum()), "us": round(med, 2),
+                                "alg_bytes": nb, "gbs": round(nb / med / 1e3, 1),
+                                "frac_hbm_peak": round(nb / med / 1e3 / HBM_PEAK_GBS, 4),
+                                "plan": [plan.split_tokens, plan.max_splits, plan.waves_per_split]}
+        if name == "cfg5":
+            qc = q_out[w.chk_tok0:].contiguous()
+            res = {}
+            cases = {"slice+verify": (qc, w.chk_qsl, w.chk_ctx, w.chk_block_tables),
+                     "slice": (qc[:512].contiguous(), w.chk_qsl[:2], w.chk_ctx[:1], w.chk_block_tables[:1]),
+                     "verify": (qc[512:].contiguous(), w.chk_qsl[1:] - 512, w.chk_ctx[1:], w.chk_block_tables[1:])}
+            for label, (qq, qs, cx, bb) in cases.items():
+                mq, mc = int(np.diff(qs).max()), int(cx.max())
+                o2 = torch.empty((qq.shape[0], s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+                cp = pg.plan_chunk(cus, s.block_size, len(cx), qq.shape[0], s.num_kv_heads, s.num_q_heads, mq, mc)
+                calls = [pg.bind_chunk(p, qq, to_i32(qs), to_i32(cx), to_i32(bb), mq, mc, scale, o2, plan=cp)
+                         for p in pools]
+                med, _ = time_calls(calls, 30)
+                flops, kv = chunk_alg(w, qs, cx)
+                res[label] = {"us": round(med, 2), "tflops": round(flops / med / 1e6, 1),
+                              "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "kv_gbs": round(kv / med / 1e3, 1), "flops": flops, "kv_bytes": kv,
+                              "plan": [cp.split_tokens, cp.max_splits]}
+            rows["chunk_cfg5"] = res
+        del pools
+        torch.cuda.empty_cache()
+    return rows
+
+
+def copy_calibration(dev, mib=256, reps=5):
+    """A plain streaming kernel of known size (torch.neg: reads and writes `mib`
+    MiB per launch, easy to find by name in a counter trace), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.ones(mib * 2**20 // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    return {"kernel": "torch.neg", "bytes_read_and_written_each": mib * 2**20, "reps": reps}
+
+
+def recorded_traffic():
+    """HBM bytes per decode launch from the committed counter record, or None if
+    the decode kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "decode_cfg3b_traffic.json")
+    try:
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, "paged_gqa_decode_head_amd", "csrc", f), "rb").read()
+                       for f in ("decode.hip", "device_common.hpp"))
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def cpu_baseline(w, seconds: float):
@@ -94,6 +223,8 @@ def main():
     ap.add_argument("--waves", type=int, default=0, help="override the planner's waves per split")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--main-only", action="store_true", help="skip the per-row measurements of the other workloads")
+    ap.add_argument("--calibrate-copy", action="store_true", help="also run a 256 MiB plain copy (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -219,11 +350,18 @@ def main():
         "roofline": {
             "kernel": "decode_kernel (paged split-KV decode + fused combine)",
             "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic() if args.workload == "cfg3b" else None,
             "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(decode_ms * 1e3, 3),
         },
         "parity_sample": parity,
     }
+    if args.calibrate_copy:
+        result["copy_calibration"] = copy_calibration(dev)
+    if not args.main_only:
+        del pools, calls
+        torch.cuda.empty_cache()
+        result["rows"] = measure_rows(args, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
