@@ -196,15 +196,18 @@ pgqa_status pgqa_paged_decode_attention(
     void* out, void* stream);
 
 /*
- * Split plan of a chunk call: each group of 256 query rows (rows are (token,
- * query head) pairs of one kv head) reads its keys in splits of split_tokens
- * keys, one workgroup each, merged by a log-sum-exp combine when max_splits > 1.
+ * Split plan of a chunk call.  Rows are (token, query head) pairs of one kv
+ * head.  A segment with more than 32 rows per kv head (a prefill slice) is cut
+ * into groups of 128 rows that read their keys in splits of split_tokens keys;
+ * a segment with at most 32 rows per kv head (verify rows, single tokens) reads
+ * its keys in splits of short_split_tokens keys.  Rows with several splits are
+ * merged by a log-sum-exp combine.
  */
 typedef struct {
-  int32_t split_tokens;  /* a multiple of max(block_size, 64), at most 4096 */
-  int32_t max_splits;    /* ceil(max_context_len / split_tokens) */
-  int32_t reserved0;     /* 0 */
-  int32_t reserved1;     /* 0 */
+  int32_t split_tokens;        /* a multiple of 32, at most 4096 */
+  int32_t max_splits;          /* >= ceil(max_context_len / min(split_tokens, short_split_tokens)) */
+  int32_t short_split_tokens;  /* a multiple of 32, at most 4096; 0 = split_tokens */
+  int32_t reserved;            /* 0 */
 } pgqa_chunk_plan;
 
 /* Host-only: the plan pgqa_paged_chunk_attention uses when given plan = NULL. */
@@ -239,9 +242,12 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits
  * at position n_s - q_len_s + i and attends to keys 0 .. that position.  A
  * segment whose metadata is inconsistent gets zero output rows and sets
- * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  The call enqueues a one-workgroup
+ * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  A block id outside the pool sets
+ * PGQA_DEVERR_BLOCK_ID; the rows that read it are then unspecified (the key is
+ * read as zeros, never out of bounds).  The call enqueues a one-workgroup
  * schedule kernel (it lists the work items the device metadata calls for), the
- * attention kernel and, with more than one split, the combine.
+ * attention kernels for long and short segments and, with more than one split,
+ * the combine.
  */
 pgqa_status pgqa_paged_chunk_attention(
     pgqa_pool* pool,

@@ -100,6 +100,7 @@ pgqa_status check_group(const pgqa_pool* pool, int32_t num_q_heads) {
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int32_t kMaxSplitTokens = 4096;
+constexpr int32_t kChunkStep = 32;  // chunk splits are whole 32-key steps
 // Non-temporal K/V loads by default (K/V bytes are read once per launch).
 constexpr bool kDefaultStreamLoads = true;
 
@@ -430,28 +431,68 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
   if (num_cus <= 0 || !valid_block_size(block_size) || num_segments < 0 || total_q < 0 || num_kv_heads <= 0 ||
       num_q_heads <= 0 || max_q_len < 0 || max_context_len < 0)
     return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
-  // A work item is 8 query-row tiles of 32 rows (256 rows) of one segment and
-  // kv head over one key split.  Aim at about two items per CU over the
-  // (tile group, kv head) units the hints allow; splits of 256 .. 4096 keys.
+  // Wide items (segments of more than 32 rows per kv head) are 128 query rows
+  // (4 waves) of one kv head over one key split: aim at two per CU over the
+  // (row group, kv head) units the hints allow, splits of 256 .. 4096 keys.
+  // Short items are one wave over one key split of a short segment: aim at
+  // eight per CU over the (segment, kv head) units, splits of 128 .. 4096 keys.
   const int64_t r = num_q_heads / num_kv_heads;
-  const int64_t gran = block_size > 64 ? block_size : 64;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int64_t groups = (int64_t(total_q) * r + 255) / 256 + num_segments;
-  const int64_t units = (groups > 0 ? groups : 1) * num_kv_heads;
-  const int64_t want = (2ll * num_cus + units - 1) / units;
-  int64_t split = round_up((ctx + want - 1) / want, gran);
-  if (split < 256) split = round_up(256, gran);
-  if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
-  if (split > kMaxSplitTokens) split = kMaxSplitTokens / gran * gran;
-  out->split_tokens = int32_t(split);
-  out->max_splits = int32_t((ctx + split - 1) / split);
-  out->reserved0 = out->reserved1 = 0;
+  const int64_t cap = std::min<int64_t>(round_up(ctx, kChunkStep), kMaxSplitTokens);
+  auto pick = [&](int64_t units, int64_t per_cu, int64_t floor_keys) {
+    const int64_t want = (per_cu * num_cus + units - 1) / units;
+    int64_t split = round_up((ctx + want - 1) / want, kChunkStep);
+    split = std::max(split, floor_keys);
+    return std::min(split, cap);
+  };
+  const int64_t wide_groups = (int64_t(total_q) * r + 127) / 128;
+  const int64_t wide = pick(std::max<int64_t>(wide_groups, 1) * num_kv_heads, 2, 256);
+  // a lone segment of more than 32 rows per kv head has no short work
+  const bool lone_wide = num_segments == 1 && int64_t(total_q) * r > 32;
+  const int64_t narrow = lone_wide ? wide : pick(std::max<int64_t>(num_segments, 1) * num_kv_heads, 8, 128);
+  out->split_tokens = int32_t(wide);
+  out->short_split_tokens = int32_t(narrow);
+  out->max_splits = int32_t((ctx + std::min(wide, narrow) - 1) / std::min(wide, narrow));
+  out->reserved = 0;
   return PGQA_OK;
 }
 
+namespace {
+struct ChunkSizing {
+  int32_t split_wide, split_short, max_splits;
+  ChunkGrids grids;
+  ChunkWorkspace ws;
+};
+
+pgqa_status chunk_sizing(const pgqa_chunk_plan& p, int32_t num_segments, int32_t total_q, int32_t hkv, int32_t hq,
+                         int32_t max_q_len, int32_t max_context_len, ChunkSizing* out) {
+  const int32_t short_split = p.short_split_tokens == 0 ? p.split_tokens : p.short_split_tokens;
+  for (const int32_t sp : {p.split_tokens, short_split})
+    if (sp <= 0 || sp % kChunkStep != 0 || sp > kMaxSplitTokens)
+      return fail(PGQA_ERR_INVALID_ARG, "chunk plan split of %d keys must be a positive multiple of %d, at most %d",
+                  sp, kChunkStep, kMaxSplitTokens);
+  if (p.reserved != 0) return fail(PGQA_ERR_INVALID_ARG, "chunk plan reserved field must be 0");
+  const int32_t smallest = std::min(p.split_tokens, short_split);
+  if (p.max_splits < (int64_t(max_context_len) + smallest - 1) / smallest || p.max_splits > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
+                max_context_len);
+  out->split_wide = p.split_tokens;
+  out->split_short = short_split;
+  out->max_splits = p.max_splits;
+  out->grids = chunk_grids(num_segments, total_q, hkv, hq / hkv, max_q_len, max_context_len, p.split_tokens,
+                           short_split, p.max_splits);
+  if (out->grids.wide > 0x7fffffff || out->grids.narrow > 0x7fffffff || out->grids.combine > 0x7fffffff)
+    return fail(PGQA_ERR_INVALID_ARG, "too many chunk work items");
+  out->ws = chunk_workspace_layout(total_q, hq, p.max_splits);
+  return PGQA_OK;
+}
+}  // namespace
+
 size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, int32_t total_q, int32_t num_q_heads,
                                   int32_t max_q_len, int32_t max_context_len, const pgqa_chunk_plan* plan) {
-  if (pool == nullptr || total_q < 0 || num_q_heads <= 0 || num_q_heads % pool->cfg.num_kv_heads != 0) return 0;
+  if (pool == nullptr || num_segments < 0 || total_q < 0 || num_q_heads <= 0 ||
+      num_q_heads % pool->cfg.num_kv_heads != 0 || max_q_len < 0 || max_context_len < 0)
+    return 0;
   pgqa_chunk_plan p;
   if (plan != nullptr) {
     p = *plan;
@@ -459,7 +500,11 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
                              num_q_heads, max_q_len, max_context_len, &p) != PGQA_OK) {
     return 0;
   }
-  return chunk_workspace_layout(num_segments, total_q, pool->cfg.num_kv_heads, num_q_heads, p.max_splits).total;
+  ChunkSizing z;
+  if (chunk_sizing(p, num_segments, total_q, pool->cfg.num_kv_heads, num_q_heads, max_q_len, max_context_len, &z) !=
+      PGQA_OK)
+    return 0;
+  return z.ws.total;
 }
 
 pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
@@ -471,10 +516,8 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   const int32_t hkv = pool->cfg.num_kv_heads;
-  const int32_t r = num_q_heads / hkv;
-  if (num_segments < 0 || int64_t(num_segments) * hkv > 65535)
-    return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d (num_segments * num_kv_heads must be <= 65535)",
-                num_segments);
+  if (num_segments < 0 || num_segments > 4096)
+    return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d (at most 4096 per call)", num_segments);
   if (pool->cfg.max_batch_size > 0 && num_segments > pool->cfg.max_batch_size)
     return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d exceeds max_batch_size=%d", num_segments,
                 pool->cfg.max_batch_size);
@@ -492,26 +535,20 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
     PGQA_TRY(pgqa_plan_chunk(pool->num_cus, pool->cfg.block_size, num_segments, total_q, hkv, num_q_heads,
                              max_q_len, max_context_len, &p));
   }
-  const int32_t gran = pool->cfg.block_size > 64 ? pool->cfg.block_size : 64;
-  if (p.split_tokens <= 0 || p.split_tokens % gran != 0 || p.split_tokens > kMaxSplitTokens)
-    return fail(PGQA_ERR_INVALID_ARG, "plan.split_tokens=%d must be a positive multiple of %d, at most %d",
-                p.split_tokens, gran, kMaxSplitTokens);
-  if (p.max_splits < (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens || p.max_splits > 65535)
-    return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
-                max_context_len);
-  const ChunkWorkspace wl = chunk_workspace_layout(num_segments, total_q, hkv, num_q_heads, p.max_splits);
-  const int64_t max_items = chunk_max_items(num_segments, total_q, hkv, r, p.max_splits);
-  if (max_items > 0x7fffffff) return fail(PGQA_ERR_INVALID_ARG, "too many work items (%lld)", (long long)max_items);
+  ChunkSizing z;
+  PGQA_TRY(chunk_sizing(p, num_segments, total_q, hkv, num_q_heads, max_q_len, max_context_len, &z));
   const int dev = pool->device;
   PGQA_TRY(check_device_ptr(q, dev, "q", 16));
   PGQA_TRY(check_device_ptr(query_start_loc, dev, "query_start_loc", 4));
   PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
   PGQA_TRY(check_device_ptr(out, dev, "out", 8));
-  if (workspace == nullptr || workspace_bytes < wl.total)
-    return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", wl.total,
-                workspace == nullptr ? size_t(0) : workspace_bytes);
-  PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  if (z.ws.total > 0) {
+    if (workspace == nullptr || workspace_bytes < z.ws.total)
+      return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", z.ws.total,
+                  workspace == nullptr ? size_t(0) : workspace_bytes);
+    PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  }
   ChunkArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.qsl = query_start_loc;
@@ -524,17 +561,14 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   a.max_q_len = max_q_len;
   a.max_ctx = max_context_len;
   a.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
-  a.split_tokens = p.split_tokens;
-  a.max_splits = p.max_splits;
-  a.max_items = int32_t(max_items);
+  a.split_wide = z.split_wide;
+  a.split_short = z.split_short;
+  a.max_splits = z.max_splits;
   char* ws = static_cast<char*>(workspace);
-  a.item_count = reinterpret_cast<int32_t*>(ws + wl.count_off);
-  a.seg_off = reinterpret_cast<int32_t*>(ws + wl.seg_off_off);
-  a.items = reinterpret_cast<int4*>(ws + wl.items_off);
-  a.part_o = p.max_splits > 1 ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
-  a.part_lse = p.max_splits > 1 ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
+  a.part_o = z.ws.total > 0 ? reinterpret_cast<float*>(ws + z.ws.part_o_off) : nullptr;
+  a.part_lse = z.ws.total > 0 ? reinterpret_cast<float*>(ws + z.ws.part_lse_off) : nullptr;
   a.out = static_cast<uint16_t*>(out);
-  hipError_t e = launch_chunk(pool->geom, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_chunk(pool->geom, a, z.grids, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk launch");
   return PGQA_OK;
 }

@@ -9,19 +9,25 @@
 // holds q_len query tokens at the end of its n keys; query i sits at position
 // n - q_len + i and sees keys 0 .. that position (bottom-right causal).
 //
-// Unlike decode, QK^T and PV here are dense contractions, so both run on
+// QK^T and PV are dense contractions here, so both run on
 // v_mfma_f32_32x32x16_bf16.
 //
-// Work decomposition.  Query rows of a segment and kv head g are the pairs
-// (token, head in group), row rho = token * r + hh, cut into 32-row tiles; 8
-// tiles form a group.  A work item is (segment, g, tile group, key split).  A
-// one-workgroup schedule kernel lists exactly the items the device metadata
-// calls for (no idle workgroups in the grid), and the main kernel runs one
-// workgroup of 8 waves per item:
-//   * every 32-key step of the split is staged once in LDS by all 512 threads
-//     (K rows and V^T rows of the step, loads issued four steps ahead), and
-//   * each of the 8 waves computes one row tile from it; the waves never merge
-//     state (each owns its rows).
+// Rows.  The query rows of a segment and kv head g are the pairs (token, head
+// in group), row rho = token * r + hh, cut into 32-row tiles (one wave each).
+// Two kinds of work item, listed on the device by a one-workgroup schedule
+// kernel (so no workgroup of the grid idles on metadata it does not need):
+//   * wide (segments of more than 32 rows per kv head: prefill slices).  Item =
+//     (segment, g, group of 4 tiles, key split); 4 waves share every 32-key step,
+//     staged once in LDS by all 256 threads through a 3-deep LDS ring fed by a
+//     3-deep register ring of global loads.  Each wave issues the score MFMAs of
+//     step i+1 before the softmax of step i, so the matrix core works while the
+//     VALU does the softmax.  MFMA-bound.
+//   * narrow (at most 32 rows per kv head: verify rows, decode-like rows).  Item =
+//     (segment, g, key split), one wave, many short splits.  V^T is loaded from
+//     the cache straight into the MFMA operand registers (whole 128-byte lines per
+//     load); K goes through a per-wave LDS tile to reach the operand layout.
+//     HBM-bound.
+// Splits are merged by a log-sum-exp combine kernel when a row has several.
 //
 // Operand layouts (verified on the hardware): lane l supplies A[m][k] with
 // m = l%32, k = 8(l/32)+j and B[k][n] with n = l%32; D[i] of lane l is
@@ -45,18 +51,18 @@
 namespace pgqa {
 namespace {
 
-constexpr float kTau = 8.0f;            // log2 headroom before the running max is raised
-constexpr int kRows = 32;               // query rows per tile
-constexpr int kTilesPerGroup = 8;       // row tiles per work item (one per wave)
-constexpr int kStep = 32;               // keys per step
-constexpr int kThreads = 64 * kTilesPerGroup;
+constexpr float kTau = 8.0f;             // log2 headroom before the running max is raised
+constexpr int kRows = 32;                // query rows per tile (one wave)
+constexpr int kWideTiles = 4;            // row tiles (waves) of a wide item
+constexpr int kWideThreads = 64 * kWideTiles;
+constexpr int kStep = 32;                // keys per step
 constexpr int kSchedThreads = 256;
-constexpr int kKRow = 136;              // LDS K row stride in bf16 (128 + 8 padding)
-constexpr int kVRow = 40;               // LDS V^T row stride in bf16 (32 + 8 padding)
-constexpr int kKStage = kStep * kKRow;  // bf16 elements per stage
+constexpr int kKRow = 136;               // LDS K row stride in bf16 (128 + 8 padding)
+constexpr int kVRow = 40;                // LDS V^T row stride in bf16 (32 + 8 padding)
+constexpr int kKStage = kStep * kKRow;   // bf16 elements per stage
 constexpr int kVStage = kHeadDim * kVRow;
-constexpr int kMaxBlockIds = 4096 / 16; // block ids of one split (split <= 4096 keys)
-constexpr int kStages = 4;              // steps whose global loads are in flight
+constexpr int kRing = 3;                 // wide: LDS stages and register stages
+constexpr int kMaxBlockIds = 4096 / 16 + 1;  // block ids one split can touch
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -67,9 +73,20 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
-// Keys a tile group may attend: up to the position of the group's last query token.
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// ok ? v : 0, selected by value (a select of two lvalues would select addresses
+// and force the operands to scratch memory).
+__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Segment metadata as read on the device; bad metadata makes the segment
+// "bad": its rows are zeroed and a sticky flag raised.
 struct SegInfo {
-  int q0, qlen, n, tiles, groups;
+  int q0, qlen, n, rows, tiles;
+  int claimed_tiles;  // tiles of the q_len the offsets claim (bad segments too)
   bool bad;
   uint32_t err;
 };
@@ -85,295 +102,213 @@ __device__ __forceinline__ SegInfo seg_info(const ChunkArgs& a, int s, int r, in
   const bool c_ok = si.n <= a.max_ctx && int64_t(si.n) <= int64_t(a.bt_stride) * bs;
   si.bad = !(q_ok && c_ok);
   si.err = !q_ok ? kErrQuery : !c_ok ? kErrContext : 0u;
-  si.tiles = si.bad ? 0 : (si.qlen * r + kRows - 1) / kRows;
-  si.groups = (si.tiles + kTilesPerGroup - 1) / kTilesPerGroup;
   if (!rows_ok) si.qlen = 0;
+  si.claimed_tiles = (si.qlen * r + kRows - 1) / kRows;
+  si.rows = si.bad ? 0 : si.qlen * r;
+  si.tiles = si.bad ? 0 : si.claimed_tiles;
   return si;
 }
 
-__device__ __forceinline__ int group_kend(const SegInfo& si, int grp, int r) {
-  const int t_last = min((grp + 1) * kTilesPerGroup, si.tiles) - 1;
+__device__ __forceinline__ int wide_groups(const SegInfo& si) { return cdiv(si.tiles, kWideTiles); }
+
+// Keys a wide tile group attends: up to the position of the group's last query token.
+__device__ __forceinline__ int wide_kend(const SegInfo& si, int grp, int r) {
+  const int t_last = min((grp + 1) * kWideTiles, si.tiles) - 1;
   const int tok_last = min(si.qlen, (t_last * kRows + kRows) / r) - 1;
   return si.n - si.qlen + tok_last + 1;
 }
 
-// ---------------------------------------------------------------- schedule
-// One workgroup: per-segment item counts, a workgroup-wide exclusive scan, then
-// every thread writes the items of its own contiguous range of segments.
-// Items: {segment, kv head, tile group, split}; a segment with bad metadata
-// gets one item per kv head with tile group -1 (zero its rows, raise the flag).
-__device__ __forceinline__ int seg_items(const ChunkArgs& a, const SegInfo& si, int r, int hkv) {
-  if (si.bad) return hkv;
-  int cnt = 0;
-  for (int grp = 0; grp < si.groups; ++grp) cnt += hkv * ((group_kend(si, grp, r) + a.split_tokens - 1) / a.split_tokens);
-  return cnt;
-}
+// ---------------------------------------------------------------- work lists
+// Three lists, each in segment order:
+//   wide    {segment, kv head, tile group, split} of segments with more than one
+//           row tile per kv head; {segment, kv head, -1, 0} zeroes the rows of a
+//           bad segment that claims more than one tile;
+//   short   {segment, kv head, 0, split} of one-tile segments; {.., -1, 0} for bad
+//           one-tile segments;
+//   combine {segment, kv head, tile, 0} for every row tile with several splits.
+// No list is stored: every workgroup derives its own item from the segment
+// metadata (a wave-wide scan of per-segment counts, then a search), so no
+// schedule kernel and no dependent read of a stored list sits in front of the
+// K/V stream.
+enum ListKind { kWideList, kShortList, kCombineList };
 
-__global__ __launch_bounds__(kSchedThreads) void chunk_schedule_kernel(PoolGeom pool, ChunkArgs a) {
-  const int tid = threadIdx.x;
-  const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
-  const int N = a.num_segments;
-  const int per = (N + kSchedThreads - 1) / kSchedThreads;
-  const int s_begin = min(N, tid * per), s_end = min(N, s_begin + per);
-  __shared__ int s_scan[kSchedThreads];
-
-  // 1. item count of each segment; workgroup-wide exclusive scan -> seg_off[]
-  int mine = 0;
-  for (int s = s_begin; s < s_end; ++s) mine += seg_items(a, seg_info(a, s, r, pool.block_size), r, hkv);
-  s_scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  int pos = s_scan[tid] - mine;
-  for (int s = s_begin; s < s_end; ++s) {
-    a.seg_off[s] = pos;
-    pos += seg_items(a, seg_info(a, s, r, pool.block_size), r, hkv);
-  }
-  const int total = s_scan[kSchedThreads - 1];
-  if (tid == 0) {
-    a.seg_off[N] = total;
-    *a.item_count = min(total, a.max_items);
-    if (total > a.max_items) raise_error(pool.err, kErrQuery);
-  }
-  __threadfence_block();
-  __syncthreads();
-
-  // 2. every thread writes items tid, tid + 256, ...: find the segment by
-  // binary search over seg_off, then (tile group, split, kv head) inside it.
-  const int limit = min(total, a.max_items);
-  for (int i = tid; i < limit; i += kSchedThreads) {
-    int lo = 0, hi = N;  // seg_off[lo] <= i < seg_off[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (a.seg_off[mid] <= i) lo = mid; else hi = mid;
-    }
-    const SegInfo si = seg_info(a, lo, r, pool.block_size);
-    int li = i - a.seg_off[lo];
-    if (si.bad) {
-      a.items[i] = make_int4(lo, li, -1, 0);
-      continue;
-    }
-    for (int grp = 0; grp < si.groups; ++grp) {
-      const int cnt = hkv * ((group_kend(si, grp, r) + a.split_tokens - 1) / a.split_tokens);
-      if (li < cnt) {
-        a.items[i] = make_int4(lo, li % hkv, grp, li / hkv);
-        break;
-      }
-      li -= cnt;
-    }
+template <ListKind K>
+__device__ __forceinline__ int list_count(const ChunkArgs& a, const SegInfo& si, int r, int hkv) {
+  if (K == kWideList) {
+    if (si.bad) return si.claimed_tiles > 1 ? hkv : 0;
+    if (si.tiles <= 1) return 0;
+    int cnt = 0;
+    for (int grp = 0; grp < wide_groups(si); ++grp) cnt += cdiv(wide_kend(si, grp, r), a.split_wide);
+    return cnt * hkv;
+  } else if (K == kShortList) {
+    if (si.bad) return si.claimed_tiles == 1 ? hkv : 0;
+    return si.tiles == 1 ? hkv * cdiv(si.n, a.split_short) : 0;
+  } else {
+    if (si.tiles == 0) return 0;
+    if (si.tiles == 1) return cdiv(si.n, a.split_short) > 1 ? hkv : 0;
+    int cnt = 0;
+    for (int grp = 0; grp < wide_groups(si); ++grp)
+      if (cdiv(wide_kend(si, grp, r), a.split_wide) > 1) cnt += min(kWideTiles, si.tiles - grp * kWideTiles);
+    return cnt * hkv;
   }
 }
 
-// ---------------------------------------------------------------- main kernel
+template <ListKind K>
+__device__ __forceinline__ int4 list_item(const ChunkArgs& a, const SegInfo& si, int s, int li, int r, int hkv) {
+  if (K != kCombineList && si.bad) return make_int4(s, li, -1, 0);
+  if (K == kShortList) return make_int4(s, li % hkv, 0, li / hkv);
+  if (K == kCombineList && si.tiles == 1) return make_int4(s, li, 0, 0);
+  for (int grp = 0;; ++grp) {
+    const int ns = cdiv(wide_kend(si, grp, r), a.split_wide);
+    const int per_head = K == kWideList ? ns : ns > 1 ? min(kWideTiles, si.tiles - grp * kWideTiles) : 0;
+    if (li < per_head * hkv) {
+      const int g = li % hkv, j = li / hkv;
+      return K == kWideList ? make_int4(s, g, grp, j) : make_int4(s, g, grp * kWideTiles + j, 0);
+    }
+    li -= per_head * hkv;
+  }
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+struct Located {
+  int4 item;  // item.x < 0: past the end of the list
+  SegInfo si;
+};
+
+// Item idx of list K, computed by one whole wave (every lane gets the result).
+// Lane i counts segments [i*per, i*per + per); a second pass over the chosen
+// lane's segments finds the segment (num_segments <= 4096, so per <= 64).
+// Workgroup 0 also raises the flags of bad segments and of a list longer than
+// the grid.
+template <ListKind K>
+__device__ Located locate(const ChunkArgs& a, PoolGeom& pool, int idx, int r) {
+  const int lane = threadIdx.x & 63;
+  const int hkv = pool.num_kv_heads, bs = pool.block_size, N = a.num_segments;
+  const int per = (N + 63) >> 6;
+  int c = 0;
+  for (int k = 0; k < per; ++k) {
+    const int s = lane * per + k;
+    if (s < N) {
+      const SegInfo si = seg_info(a, s, r, bs);
+      c += list_count<K>(a, si, r, hkv);
+      if (blockIdx.x == 0 && si.bad) raise_error(pool.err, si.err);
+    }
+  }
+  const int incl = wave_incl_scan(c, lane);
+  const int total = __shfl(incl, 63);
+  if (blockIdx.x == 0 && lane == 0 && total > int(gridDim.x)) raise_error(pool.err, kErrQuery);
+  Located out;
+  out.item = make_int4(-1, 0, 0, 0);
+  if (idx >= total) return out;
+  const int L = __ffsll((unsigned long long)__ballot(incl > idx)) - 1;
+  int li = idx - (__shfl(incl, L) - __shfl(c, L));
+  int seg = L;
+  if (per > 1) {
+    const int s2 = L * per + lane;
+    const int c2 = lane < per && s2 < N ? list_count<K>(a, seg_info(a, s2, r, bs), r, hkv) : 0;
+    const int incl2 = wave_incl_scan(c2, lane);
+    const int L2 = __ffsll((unsigned long long)__ballot(incl2 > li)) - 1;
+    li -= __shfl(incl2, L2) - __shfl(c2, L2);
+    seg = L * per + L2;
+  }
+  out.si = seg_info(a, seg, r, bs);
+  out.item = list_item<K>(a, out.si, seg, li, r, hkv);
+  return out;
+}
+
+// Zero the output rows of kv head g of a bad segment.
 template <int R>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(PoolGeom pool, ChunkArgs a) {
-  if (int(blockIdx.x) >= *a.item_count) return;
-  const int4 item = a.items[blockIdx.x];
-  const int s = item.x, g = item.y, grp = item.z, sp = item.w;
-  const int hkv = pool.num_kv_heads, bs = pool.block_size, hq = a.num_q_heads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, half = lane >> 5;
-
-  __shared__ __align__(16) uint16_t s_k[2][kKStage];
-  __shared__ __align__(16) uint16_t s_v[2][kVStage];
-  __shared__ uint32_t s_valid[2];              // per stage: bit j = key j of the step is attendable
-  __shared__ int32_t s_blk[kMaxBlockIds];
-
-  const SegInfo si = seg_info(a, s, R, bs);
-  if (grp < 0 || si.bad) {
-    if (tid == 0) raise_error(pool.err, si.err ? si.err : kErrQuery);
-    for (int64_t i = tid; i < int64_t(si.qlen) * R * kHeadDim; i += kThreads) {
-      const int64_t tok = i / (R * kHeadDim), rem = i - tok * (R * kHeadDim);
-      a.out[((si.q0 + tok) * hq + g * R) * kHeadDim + rem] = 0;
-    }
-    return;
+__device__ __forceinline__ void zero_rows(const ChunkArgs& a, const SegInfo& si, int g, int tid, int nthreads) {
+  for (int64_t i = tid; i < int64_t(si.qlen) * R * kHeadDim; i += nthreads) {
+    const int64_t t = i / (R * kHeadDim), rem = i - t * (R * kHeadDim);
+    a.out[((si.q0 + t) * a.num_q_heads + g * R) * kHeadDim + rem] = 0;
   }
-  const int prefix = si.n - si.qlen;
-  const int kend = group_kend(si, grp, R);
-  const int ns = (kend + a.split_tokens - 1) / a.split_tokens;
-  const int k0 = sp * a.split_tokens;
-  const int k1 = min(kend, k0 + a.split_tokens);
-  const int nsteps = (k1 - k0 + kStep - 1) / kStep;
+}
 
-  // Block ids of the split (entries past the table row are never read).
-  const int nblk = (k1 - k0 + bs - 1) / bs;
-  for (int i = tid; i < nblk; i += kThreads) s_blk[i] = a.bt[int64_t(s) * a.bt_stride + k0 / bs + i];
-
-  // This wave's row tile and its q operands (zero for rows past the segment).
-  const int rows = si.qlen * R;
-  const int tile = grp * kTilesPerGroup + wave;
-  const bool tile_ok = tile < si.tiles;
-  const int rho = tile * kRows + col;
-  const bool row_ok = tile_ok && rho < rows;
-  const int tok = rho / R, hh = rho - tok * R;
-  const int qpos = prefix + tok;
-  uint4 qv[8];
-  {
-    const uint16_t* qp = a.q + ((int64_t(si.q0) + tok) * hq + g * R + hh) * kHeadDim + half * 64;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      qv[ks] = row_ok ? *reinterpret_cast<const uint4*>(qp + 8 * ks) : make_uint4(0, 0, 0, 0);
+// Block-table entries [b0, b0 + nblk) of segment s as (block, kv head g) tile
+// indices; an id outside the pool reads tile (0, g) and raises the flag.
+__device__ __forceinline__ void load_tiles(int32_t* s_blk, const ChunkArgs& a, const PoolGeom& pool, int s, int g,
+                                           int b0, int nblk, int tid, int nthreads) {
+  bool bad = false;
+  for (int i = tid; i < nblk; i += nthreads) {
+    const int32_t b = a.bt[int64_t(s) * a.bt_stride + b0 + i];
+    const bool ok = unsigned(b) < unsigned(pool.num_blocks);
+    bad |= !ok;
+    s_blk[i] = (ok ? b : 0) * pool.num_kv_heads + g;
   }
-  __syncthreads();
+  if (bad) raise_error(pool.err, kErrBlockId);
+}
 
-  // Staging: thread t moves 16 B of K (key t/16, 16-byte chunk t%16) and 16 B of
-  // V^T (dim t/4, keys 8*(t%4) .. +7) per step.
-  const int64_t tstride = tile_elems(pool);
-  const int64_t bstride = tstride * hkv;
-  const uint16_t* pool_g = pool.kv + int64_t(g) * tstride;
-  const int kkey = tid >> 4, kchunk = tid & 15;
-  const int vdim = tid >> 2, vq = tid & 3;
-  struct Stage {
-    uint4 k, v;
-    bool kok, vok;
-  };
-  // Loads are unconditional (an invalid key reads block 0, slot 0) and their
-  // validity is applied when the data is stored to LDS, so the compiler can
-  // count outstanding loads exactly and keep the prefetch in flight.
-  bool bad_blk = false;
-  auto fetch = [&](Stage& st, int step) {
-    const int key0 = k0 + step * kStep;
-    const int kk = key0 + kkey;
-    const int32_t bk = s_blk[min((kk - k0) / bs, nblk - 1)];
-    st.kok = kk < k1 && unsigned(bk) < unsigned(pool.num_blocks);
-    const uint16_t* kp =
-        pool_g + int64_t(st.kok ? bk : 0) * bstride + ((st.kok ? kk : 0) & (bs - 1)) * kHeadDim + kchunk * 8;
-    st.k = *reinterpret_cast<const uint4*>(kp);
-    const int kv = key0 + 8 * vq;
-    const int32_t bv = s_blk[min((kv - k0) / bs, nblk - 1)];
-    st.vok = kv < k1 && unsigned(bv) < unsigned(pool.num_blocks);
-    const uint16_t* vp = pool_g + int64_t(st.vok ? bv : 0) * bstride + int64_t(bs) * kHeadDim + int64_t(vdim) * bs +
-                         ((st.vok ? kv : 0) & (bs - 1));
-    st.v = *reinterpret_cast<const uint4*>(vp);
-    bad_blk |= (kk < k1 && unsigned(bk) >= unsigned(pool.num_blocks)) ||
-               (kv < k1 && unsigned(bv) >= unsigned(pool.num_blocks));
-  };
-  auto store = [&](const Stage& st, int step, int buf) {
-    // V entries of keys past the split end are zeroed (0 * NaN would poison O).
-    const int kv = k0 + step * kStep + 8 * vq;
-    uint4 v = st.vok ? st.v : make_uint4(0, 0, 0, 0);
-    if (kv + 8 > k1) {
-      auto keep = [&](int key) -> uint32_t {
-        return key + 1 < k1 ? 0xffffffffu : key < k1 ? 0x0000ffffu : 0u;
-      };
-      v.x &= keep(kv + 0); v.y &= keep(kv + 2); v.z &= keep(kv + 4); v.w &= keep(kv + 6);
-    }
-    *reinterpret_cast<uint4*>(&s_k[buf][kkey * kKRow + kchunk * 8]) = st.kok ? st.k : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(&s_v[buf][vdim * kVRow + 8 * vq]) = v;
-    if (tid < kStep) {
-      const int key = k0 + step * kStep + tid;
-      const int32_t b = s_blk[min((key - k0) / bs, nblk - 1)];
-      const bool ok = key < k1 && unsigned(b) < unsigned(pool.num_blocks);
-      const uint64_t msk = __ballot(ok);
-      if (tid == 0) s_valid[buf] = uint32_t(msk);
-    }
-  };
-
+// ---------------------------------------------------------------- shared per-wave math
+// Online softmax of one 32-key step for a wave's 32-row tile, then O^T += V^T P^T.
+// Scores stay in raw units (q.k); c = softmax scale * log2 e is folded into the
+// exponent, p = exp2(c s - c m).  The running max m is raised only when a score
+// exceeds it by more than kTau / c (log2 headroom kTau), so most steps skip the
+// rescale of the 64 accumulators.  l sums the same bf16-rounded weights PV uses.
+struct RowState {
   f32x16_t o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;                 // running max (raw score units) and weight sum
-  const float c = a.qk_scale_log2;
-  const float tau_raw = kTau / c;
-  const int qpos_first = prefix + (tile * kRows) / R;  // position of the tile's first token
-  const int mrow = col;
-  const int kperm = (mrow & ~12) | ((mrow & 4) << 1) | ((mrow & 8) >> 1);   // pi(m): swap bits 2, 3
+  float m, l;
+};
 
-  auto compute = [&](int step, int buf) {
-    if (!tile_ok) return;
-    const int key0 = k0 + step * kStep;
-    const uint32_t valid = s_valid[buf];
-    const uint16_t* kr = &s_k[buf][kperm * kKRow + half * 64];
-    // two independent accumulation chains (even / odd dim steps) halve the
-    // dependent-MFMA latency of the score product
-    f32x16_t sacc = f32x16_t{}, sacc2 = f32x16_t{};
+template <typename VOp>
+__device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, bool full, int key0, int klim,
+                                           int qpos, int half, float c, float tau_raw, VOp&& vop) {
+  float sv[16];
+  if (full) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ks += 2) {
-      sacc = mfma32(*reinterpret_cast<const uint4*>(kr + 8 * ks), qv[ks], sacc);
-      sacc2 = mfma32(*reinterpret_cast<const uint4*>(kr + 8 * ks + 8), qv[ks + 1], sacc2);
-    }
-    sacc += sacc2;
-    // Scores stay in raw units (q.k); the scale c = softmax scale * log2 e is
-    // folded into the exponent: p = exp2(c * s - c * m).  Steps entirely below
-    // the tile's first query position, with all keys present, need no mask.
-    float sv[16];
-    if (valid == 0xffffffffu && key0 + kStep - 1 <= qpos_first) {
+    for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+  } else {
+    // key0 + 16(i/8) + 8 half + i%8 is visible iff it is < klim and <= qpos
+    const int lim = min(qpos, klim - 1) - key0 - 8 * half;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int koff = 16 * (i >> 3) + 8 * half + (i & 7);
-        const bool okk = ((valid >> koff) & 1u) && key0 + koff <= qpos;
-        sv[i] = okk ? sacc[i] : -INFINITY;
-      }
-    }
-    float mx = sv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (__ballot(mx > m + tau_raw)) {
-      const float mn = fmaxf(m, mx);
-      const float corr = mn == -INFINITY ? 1.f : fast_exp2((m - mn) * c);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= corr;
-      l *= corr;
-      m = mn;
-    }
-    const float neg_mc = m == -INFINITY ? 0.f : -m * c;
-    constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
-#pragma unroll
-    for (int s16 = 0; s16 < 2; ++s16) {
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = fast_exp2(fmaf(sv[8 * s16 + 2 * e], c, neg_mc));
-        const float p1 = fast_exp2(fmaf(sv[8 * s16 + 2 * e + 1], c, neg_mc));
-        pk[e] = pack_bf16x2(p0, p1);
-        l = dot2_bf16(pk[e], kOnes, l);  // l sums the same rounded weights PV uses
-      }
-      const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint4 vop = *reinterpret_cast<const uint4*>(&s_v[buf][(32 * dt + col) * kVRow + 16 * s16 + 8 * half]);
-        o[dt] = mfma32(vop, pb, o[dt]);
-      }
-    }
-  };
-
-  // Pipeline: a ring of kStages register stages keeps the global loads of the
-  // next kStages steps in flight; two LDS stages alternate between the step
-  // being computed and the next one being stored.  Loads are unconditional
-  // (clamped to the last step) so the compiler can count them exactly; the
-  // barriers are uniform across the workgroup.
-  if (nsteps > 0) {
-    Stage st[kStages];
-#pragma unroll
-    for (int j = 0; j < kStages; ++j) fetch(st[j], min(j, nsteps - 1));
-    store(st[0], 0, 0);
-    fetch(st[0], min(kStages, nsteps - 1));
-    for (int base = 0; base < nsteps; base += kStages) {
-#pragma unroll
-      for (int j = 0; j < kStages; ++j) {
-        const int i = base + j;
-        __syncthreads();
-        if (i < nsteps) compute(i, j & 1);
-        if (i + 1 < nsteps) store(st[(j + 1) % kStages], i + 1, (j + 1) & 1);
-        fetch(st[(j + 1) % kStages], min(i + 1 + kStages, nsteps - 1));
-      }
-    }
+    for (int i = 0; i < 16; ++i) sv[i] = 16 * (i >> 3) + (i & 7) <= lim ? sacc[i] : -INFINITY;
   }
-  if (bad_blk) raise_error(pool.err, kErrBlockId);
+  float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
+                       fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  if (__builtin_amdgcn_ballot_w64(mx > st.m + tau_raw)) {
+    const float mn = fmaxf(st.m, mx);
+    const float corr = mn == -INFINITY ? 1.f : fast_exp2((st.m - mn) * c);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] *= corr;
+    st.l *= corr;
+    st.m = mn;
+  }
+  const float neg_mc = st.m == -INFINITY ? 0.f : -st.m * c;
+  constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
+#pragma unroll
+  for (int s16 = 0; s16 < 2; ++s16) {
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(fmaf(sv[8 * s16 + 2 * e], c, neg_mc));
+      const float p1 = fast_exp2(fmaf(sv[8 * s16 + 2 * e + 1], c, neg_mc));
+      pk[e] = pack_bf16x2(p0, p1);
+      st.l = dot2_bf16(pk[e], kOnes, st.l);
+    }
+    const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma32(vop(dt, s16), pb, st.o[dt]);
+  }
+}
 
-  // Each wave finishes its own rows.
-  if (!tile_ok) return;
-  const float L = l + __shfl_xor(l, 32);
+// Normalised rows of one tile: bf16 output when the row has a single split,
+// else fp32 partials and the split's log2-sum-exp for the combine kernel.
+template <int R>
+__device__ __forceinline__ void write_rows(const ChunkArgs& a, const RowState& st, int half, bool row_ok,
+                                           int64_t qrow, int g, int hh, int sp, int ns, float c) {
+  const float L = st.l + __shfl_xor(st.l, 32);
   if (!row_ok) return;
-  const int64_t qrow = int64_t(si.q0) + tok;
+  const int hq = a.num_q_heads;
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (ns == 1) {
     uint16_t* dst = a.out + (qrow * hq + g * R + hh) * kHeadDim;
@@ -382,8 +317,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PoolGeom pool, ChunkArg
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dt + 8 * q4 + 4 * half;
-        const uint2 pk = make_uint2(pack_bf16x2(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv),
-                                    pack_bf16x2(o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv));
+        const uint2 pk = make_uint2(pack_bf16x2(st.o[dt][4 * q4] * inv, st.o[dt][4 * q4 + 1] * inv),
+                                    pack_bf16x2(st.o[dt][4 * q4 + 2] * inv, st.o[dt][4 * q4 + 3] * inv));
         *reinterpret_cast<uint2*>(dst + d) = pk;
       }
     }
@@ -395,99 +330,395 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(PoolGeom pool, ChunkArg
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         const int d = 32 * dt + 8 * q4 + 4 * half;
-        *reinterpret_cast<float4*>(dst + d) = make_float4(o[dt][4 * q4] * inv, o[dt][4 * q4 + 1] * inv,
-                                                          o[dt][4 * q4 + 2] * inv, o[dt][4 * q4 + 3] * inv);
+        *reinterpret_cast<float4*>(dst + d) = make_float4(st.o[dt][4 * q4] * inv, st.o[dt][4 * q4 + 1] * inv,
+                                                          st.o[dt][4 * q4 + 2] * inv, st.o[dt][4 * q4 + 3] * inv);
       }
     }
-    if (half == 0) a.part_lse[prow] = L > 0.f ? m * c + __log2f(L) : -INFINITY;
+    if (half == 0) a.part_lse[prow] = L > 0.f ? st.m * c + __log2f(L) : -INFINITY;
   }
 }
 
-// Log-sum-exp combine of chunk partials: one workgroup per (query token,
-// query head), one thread per dim; splits merged in order.
-__global__ __launch_bounds__(kHeadDim) void chunk_combine_kernel(PoolGeom pool, ChunkArgs a) {
-  const int t = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
-  const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
-  const int g = h / r, hh = h - g * r;
-  // segment of token t: last s with qsl[s] <= t (qsl ascending)
-  int lo = 0, hi = a.num_segments;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (a.qsl[mid] <= t) lo = mid; else hi = mid;
+// The 8 q operands of one row (zero for rows past the segment).
+__device__ __forceinline__ void load_q(uint4 (&qv)[8], const ChunkArgs& a, bool row_ok, int64_t qrow, int head,
+                                       int half) {
+  const uint16_t* qp = a.q + (qrow * a.num_q_heads + head) * kHeadDim + half * 64;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qv[ks] = row_ok ? ld16(qp + 8 * ks) : make_uint4(0, 0, 0, 0);
+}
+
+// Keep-mask of a bf16 pair (keys key, key+1) against the split end.
+__device__ __forceinline__ uint32_t keep2(int key, int klim) {
+  return key + 1 < klim ? 0xffffffffu : key < klim ? 0x0000ffffu : 0u;
+}
+
+// ---------------------------------------------------------------- wide kernel
+template <int R>
+__global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom pool, ChunkArgs a) {
+  const Located loc = locate<kWideList>(a, pool, blockIdx.x, R);
+  if (loc.item.x < 0) return;
+  const SegInfo& si = loc.si;
+  const int s = loc.item.x, g = loc.item.y, grp = loc.item.z, sp = loc.item.w;
+  const int bs = pool.block_size, lbs = __ffs(bs) - 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  if (grp < 0) {
+    zero_rows<R>(a, si, g, tid, kWideThreads);
+    return;
   }
-  const SegInfo si = seg_info(a, lo, r, pool.block_size);
-  if (si.bad || t < si.q0 || t >= si.q0 + si.qlen) return;
-  const int tile = ((t - si.q0) * r + hh) / kRows;
-  const int kend = group_kend(si, tile / kTilesPerGroup, r);
-  const int ns = (kend + a.split_tokens - 1) / a.split_tokens;
-  if (ns <= 1) return;
-  const int64_t stride = int64_t(a.total_q) * r;     // partial rows per split
-  const int64_t base = (int64_t(g) * a.max_splits) * stride + int64_t(t) * r + hh;
+
+  __shared__ __align__(16) uint16_t s_k[kRing][kKStage];
+  __shared__ __align__(16) uint16_t s_v[kRing][kVStage];
+  __shared__ int32_t s_blk[kMaxBlockIds];
+
+  const int prefix = si.n - si.qlen;
+  const int kend = wide_kend(si, grp, R);
+  const int ns = cdiv(kend, a.split_wide);
+  const int k0 = sp * a.split_wide;
+  const int k1 = min(kend, k0 + a.split_wide);
+  const int nsteps = cdiv(k1 - k0, kStep);
+  const int b0 = k0 >> lbs;
+  load_tiles(s_blk, a, pool, s, g, b0, ((k1 - 1) >> lbs) - b0 + 1, tid, kWideThreads);
+
+  // This wave's row tile.
+  const int tile = grp * kWideTiles + wave;
+  const bool tile_ok = tile < si.tiles;
+  const int rho = tile * kRows + col;
+  const bool row_ok = tile_ok && rho < si.rows;
+  const int tok = rho / R, hh = rho - tok * R;
+  const int qpos = prefix + tok;
+  const int64_t qrow = int64_t(si.q0) + tok;
+  uint4 qv[8];
+  load_q(qv, a, row_ok, qrow, g * R + hh, half);
+  __syncthreads();
+
+  // Staging roles per step: K key kkey, 16-byte chunks kch and kch + 8 (each
+  // wave instruction reads 8 whole half rows); V^T entries idx = tid + 256u for
+  // u = 0, 1: dim idx / 4, keys 8 (idx % 4) .. +7 (whole lines for bs <= 32).
+  // A (block, head) tile holds bs << 8 bf16, V^T starting at bs << 7.
+  const int tshift = lbs + 8;
+  const int kkey = tid >> 3, kch = tid & 7;
+  struct Stage {
+    uint4 k[2], v[2];
+  };
+  // Loads are unconditional: a key past the split end re-reads the split's last
+  // key (its score is masked, its V zeroed when stored), so the compiler counts
+  // outstanding loads exactly and the ring stays full.
+  auto fetch = [&](Stage& st, int step) {
+    const int key0 = k0 + step * kStep;
+    const int kk = min(key0 + kkey, k1 - 1);
+    const uint16_t* kp = pool.kv + (int64_t(s_blk[(kk >> lbs) - b0]) << tshift) + (kk & (bs - 1)) * kHeadDim + kch * 8;
+    st.k[0] = ld16(kp);
+    st.k[1] = ld16(kp + 64);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + kWideThreads * u;
+      const int kv = min(key0 + 8 * (idx & 3), k1 - 1) & ~7;
+      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + (bs << 7) + (idx >> 2) * bs +
+                     (kv & (bs - 1)));
+    }
+  };
+  auto store = [&](Stage& st, int step, int buf) {
+    const int key0 = k0 + step * kStep;
+    uint16_t* kd = &s_k[buf][kkey * kKRow + kch * 8];
+    *reinterpret_cast<uint4*>(kd) = st.k[0];
+    *reinterpret_cast<uint4*>(kd + 64) = st.k[1];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int idx = tid + kWideThreads * u;
+      const int kv = key0 + 8 * (idx & 3);
+      if (kv + 8 > k1) {  // V of keys past the split end must be 0 (0 * NaN would poison O)
+        st.v[u].x &= keep2(kv + 0, k1); st.v[u].y &= keep2(kv + 2, k1);
+        st.v[u].z &= keep2(kv + 4, k1); st.v[u].w &= keep2(kv + 6, k1);
+      }
+      *reinterpret_cast<uint4*>(&s_v[buf][(idx >> 2) * kVRow + 8 * (idx & 3)]) = st.v[u];
+    }
+  };
+
+  RowState rs;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) rs.o[dt] = f32x16_t{};
+  rs.m = -INFINITY;
+  rs.l = 0.f;
+  const float c = a.qk_scale_log2;
+  const float tau_raw = kTau / c;
+  const int qpos_first = prefix + (tile * kRows) / R;  // position of the tile's first token
+  const int kperm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);  // pi(m): swap bits 2, 3
+
+  auto qk = [&](int buf) -> f32x16_t {
+    const uint16_t* kr = &s_k[buf][kperm * kKRow + half * 64];
+    uint4 kop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = ld16(kr + 8 * ks);
+    f32x16_t acc = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(kop[ks], qv[ks], acc);
+    return acc;
+  };
+
+  // Pipeline (iteration i): scores of step i+1 are issued from LDS stage
+  // (i+1)%3, then the softmax and PV of step i (its scores came one iteration
+  // earlier), then registers of step i+2 go to LDS stage (i+2)%3 (last read in
+  // iteration i-1) and that register slot is refilled with step i+5.  One
+  // barrier per step.  Loads are clamped to the last step, never skipped.
+  Stage st0, st1, st2;
+  fetch(st0, 0);
+  fetch(st1, min(1, nsteps - 1));
+  fetch(st2, min(2, nsteps - 1));
+  store(st0, 0, 0);
+  fetch(st0, min(3, nsteps - 1));
+  store(st1, min(1, nsteps - 1), 1);
+  fetch(st1, min(4, nsteps - 1));
+  __syncthreads();
+  f32x16_t s_cur = f32x16_t{};
+  if (tile_ok) s_cur = qk(0);
+  // buf holds step i, nbuf step i+1 (stale past the last step: its scores go unused)
+  auto iter = [&](int i, int buf, int nbuf, int sbuf, Stage& sst) {
+    if (tile_ok && i < nsteps) {
+      const f32x16_t s_next = qk(nbuf);
+      const int key0 = k0 + i * kStep;
+      const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= qpos_first;
+      softmax_pv(rs, s_cur, full, key0, k1, qpos, half, c, tau_raw, [&](int dt, int s16) {
+        return ld16(&s_v[buf][(32 * dt + col) * kVRow + 16 * s16 + 8 * half]);
+      });
+      s_cur = s_next;
+    }
+    store(sst, min(i + 2, nsteps - 1), sbuf);
+    fetch(sst, min(i + 5, nsteps - 1));
+    __syncthreads();
+  };
+  for (int base = 0; base < nsteps; base += kRing) {
+    iter(base, 0, 1, 2, st2);
+    iter(base + 1, 1, 2, 0, st0);
+    iter(base + 2, 2, 0, 1, st1);
+  }
+  if (!tile_ok) return;
+  write_rows<R>(a, rs, half, row_ok, qrow, g, hh, sp, ns, c);
+}
+
+// ---------------------------------------------------------------- narrow kernel
+// One wave per (segment, kv head, split) of a segment with at most 32 rows per
+// kv head.  Per 32-key step: K as 8 loads of 4 whole rows each (-> LDS ->
+// operand rows pi(m)), V^T as 8 loads straight into the PV operand registers;
+// two steps of loads in flight.
+template <int R>
+__global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkArgs a) {
+  const Located loc = locate<kShortList>(a, pool, blockIdx.x, R);
+  if (loc.item.x < 0) return;
+  const SegInfo& si = loc.si;
+  const int s = loc.item.x, g = loc.item.y, sp = loc.item.w;
+  const int bs = pool.block_size, lbs = __ffs(bs) - 1;
+  const int lane = threadIdx.x, col = lane & 31, half = lane >> 5;
+  if (loc.item.z < 0) {
+    zero_rows<R>(a, si, g, lane, 64);
+    return;
+  }
+
+  __shared__ __align__(16) uint16_t s_k[kKStage];
+  __shared__ int32_t s_blk[kMaxBlockIds];
+
+  const int prefix = si.n - si.qlen;
+  const int kend = si.n;
+  const int ns = cdiv(kend, a.split_short);
+  const int k0 = sp * a.split_short;
+  const int k1 = min(kend, k0 + a.split_short);
+  const int nsteps = cdiv(k1 - k0, kStep);
+  const int b0 = k0 >> lbs;
+  load_tiles(s_blk, a, pool, s, g, b0, ((k1 - 1) >> lbs) - b0 + 1, lane, 64);
+
+  const int rho = col;
+  const bool row_ok = rho < si.rows;
+  const int tok = rho / R, hh = rho - tok * R;
+  const int qpos = prefix + tok;
+  const int64_t qrow = int64_t(si.q0) + tok;
+  uint4 qv[8];
+  load_q(qv, a, row_ok, qrow, g * R + hh, half);
+  __syncthreads();
+
+  const int tshift = lbs + 8;
+  struct Stage {
+    uint4 k[8], v[8];
+  };
+  // K load u: key 4u + lane/16 of the step, 16-byte chunk lane%16.
+  // V load 2dt + s16: dim 32dt + col, keys 16 s16 + 8 half .. +7.
+  auto fetch = [&](Stage& st, int step) {
+    const int key0 = k0 + step * kStep;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = min(key0 + 4 * u + (lane >> 4), k1 - 1);
+      st.k[u] = ld16(pool.kv + (int64_t(s_blk[(kk >> lbs) - b0]) << tshift) + (kk & (bs - 1)) * kHeadDim +
+                     (lane & 15) * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int dt = u >> 1, s16 = u & 1;
+      const int kv = min(key0 + 16 * s16 + 8 * half, k1 - 1) & ~7;
+      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + (bs << 7) + (32 * dt + col) * bs +
+                     (kv & (bs - 1)));
+    }
+  };
+
+  RowState rs;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) rs.o[dt] = f32x16_t{};
+  rs.m = -INFINITY;
+  rs.l = 0.f;
+  const float c = a.qk_scale_log2;
+  const float tau_raw = kTau / c;
+  const int kperm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+
+  auto step = [&](Stage& st, int i) {
+    const int key0 = k0 + i * kStep;
+    __syncthreads();  // the previous step's reads of s_k are done
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      *reinterpret_cast<uint4*>(&s_k[(4 * u + (lane >> 4)) * kKRow + (lane & 15) * 8]) = st.k[u];
+    __syncthreads();
+    const uint16_t* kr = &s_k[kperm * kKRow + half * 64];
+    uint4 kop[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = ld16(kr + 8 * ks);
+    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) sacc = mfma32(kop[ks], qv[ks], sacc);
+    // V of keys past the split end must be 0: 0 * NaN would poison O.
+    if (key0 + kStep > k1) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int kv = key0 + 16 * (u & 1) + 8 * half;
+        st.v[u].x &= keep2(kv + 0, k1); st.v[u].y &= keep2(kv + 2, k1);
+        st.v[u].z &= keep2(kv + 4, k1); st.v[u].w &= keep2(kv + 6, k1);
+      }
+    }
+    const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= prefix;
+    softmax_pv(rs, sacc, full, key0, k1, qpos, half, c, tau_raw,
+               [&](int dt, int s16) { return st.v[2 * dt + s16]; });
+  };
+
+  Stage st0, st1;
+  fetch(st0, 0);
+  fetch(st1, min(1, nsteps - 1));
+  for (int base = 0; base < nsteps; base += 2) {
+    step(st0, base);
+    fetch(st0, min(base + 2, nsteps - 1));
+    if (base + 1 < nsteps) step(st1, base + 1);
+    fetch(st1, min(base + 3, nsteps - 1));
+  }
+  write_rows<R>(a, rs, half, row_ok, qrow, g, hh, sp, ns, c);
+}
+
+// ---------------------------------------------------------------- combine
+// Log-sum-exp combine of the split partials of one 32-row tile: thread t owns
+// row t/8 and dims 16 (t%8) .. +15; splits are merged in order.
+template <int R>
+__global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, ChunkArgs a) {
+  const Located loc = locate<kCombineList>(a, pool, blockIdx.x, R);
+  if (loc.item.x < 0) return;
+  const SegInfo& si = loc.si;
+  const int g = loc.item.y, tile = loc.item.z;
+  const int tid = threadIdx.x, row = tid >> 3, d0 = 16 * (tid & 7);
+  const int rho = tile * kRows + row;
+  if (rho >= si.rows) return;
+  int ns;
+  if (si.tiles == 1) {
+    ns = cdiv(si.n, a.split_short);
+  } else {
+    ns = cdiv(wide_kend(si, tile / kWideTiles, R), a.split_wide);
+  }
+  const int tok = rho / R, hh = rho - tok * R;
+  const int64_t qrow = int64_t(si.q0) + tok;
+  const int64_t stride = int64_t(a.total_q) * R;  // partial rows per split
+  const int64_t base = int64_t(g) * a.max_splits * stride + qrow * R + hh;
   float M = -INFINITY;
   for (int k = 0; k < ns; ++k) M = fmaxf(M, a.part_lse[base + k * stride]);
-  float o = 0.f;
+  float4 o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
   if (M != -INFINITY) {
-    float L = 0.f;
     for (int k = 0; k < ns; ++k) {
       const float lk = a.part_lse[base + k * stride];
       const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + (base + k * stride) * kHeadDim + d0);
       L += e;
-      o += e * a.part_o[(base + k * stride) * kHeadDim + d];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 v = src[j];
+        o[j].x += e * v.x; o[j].y += e * v.y; o[j].z += e * v.z; o[j].w += e * v.w;
+      }
     }
-    o /= L;
   }
-  a.out[(int64_t(t) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(o);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* dst = a.out + (qrow * a.num_q_heads + loc.item.y * R + hh) * kHeadDim + d0;
+  uint4 w[2];
+  w[0] = make_uint4(pack_bf16x2(o[0].x * inv, o[0].y * inv), pack_bf16x2(o[0].z * inv, o[0].w * inv),
+                    pack_bf16x2(o[1].x * inv, o[1].y * inv), pack_bf16x2(o[1].z * inv, o[1].w * inv));
+  w[1] = make_uint4(pack_bf16x2(o[2].x * inv, o[2].y * inv), pack_bf16x2(o[2].z * inv, o[2].w * inv),
+                    pack_bf16x2(o[3].x * inv, o[3].y * inv), pack_bf16x2(o[3].z * inv, o[3].w * inv));
+  reinterpret_cast<uint4*>(dst)[0] = w[0];
+  reinterpret_cast<uint4*>(dst)[1] = w[1];
 }
 
 template <int R>
-hipError_t launch_r(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, pool, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_kernel<R>), dim3(a.max_items), dim3(kThreads), 0, stream, pool, a);
-  e = hipGetLastError();
-  if (e != hipSuccess || a.max_splits == 1) return e;
-  hipLaunchKernelGGL(chunk_combine_kernel, dim3(a.total_q, a.num_q_heads), dim3(kHeadDim), 0, stream, pool, a);
-  return hipGetLastError();
+hipError_t launch_r(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream) {
+  if (grids.wide > 0) {
+    hipLaunchKernelGGL((chunk_wide_kernel<R>), dim3(grids.wide), dim3(kWideThreads), 0, stream, pool, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (grids.narrow > 0) {
+    hipLaunchKernelGGL((chunk_narrow_kernel<R>), dim3(grids.narrow), dim3(64), 0, stream, pool, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (grids.combine > 0) {
+    hipLaunchKernelGGL((chunk_combine_kernel<R>), dim3(grids.combine), dim3(256), 0, stream, pool, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 }  // namespace
 
-int64_t chunk_max_items(int32_t num_segments, int32_t total_q, int32_t num_kv_heads, int32_t group,
-                        int32_t max_splits) {
-  const int64_t rows_per_group = int64_t(kRows) * kTilesPerGroup;
-  const int64_t groups = (int64_t(total_q) * group + rows_per_group - 1) / rows_per_group + num_segments;
-  return groups * max_splits * num_kv_heads + int64_t(num_segments) * num_kv_heads;
+ChunkGrids chunk_grids(int32_t num_segments, int32_t total_q, int32_t num_kv_heads, int32_t group, int32_t max_q_len,
+                       int32_t max_ctx, int32_t split_wide, int32_t split_short, int32_t max_splits) {
+  ChunkGrids b;
+  const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
+  const int64_t N = num_segments, hkv = num_kv_heads;
+  // Wide work exists if some segment may have more than one row tile (a lone
+  // segment holds all total_q tokens); short work unless a lone segment has more.
+  const bool wide = int64_t(max_q_len) * group > kRows || (N == 1 && int64_t(total_q) * group > kRows);
+  const bool narrow = !(N == 1 && int64_t(total_q) * group > kRows);
+  const int64_t rows_per_group = int64_t(kRows) * kWideTiles;
+  const int64_t groups = (int64_t(total_q) * group + rows_per_group - 1) / rows_per_group + N;
+  b.wide = wide ? (groups * ((ctx + split_wide - 1) / split_wide) + N) * hkv : 0;
+  b.narrow = narrow ? N * hkv * ((ctx + split_short - 1) / split_short) : 0;
+  const int64_t tiles = (int64_t(total_q) * group + kRows - 1) / kRows + N;
+  b.combine = max_splits > 1 ? tiles * hkv : 0;
+  return b;
 }
 
-ChunkWorkspace chunk_workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_kv_heads,
-                                      int32_t num_q_heads, int32_t max_splits) {
+ChunkWorkspace chunk_workspace_layout(int32_t total_q, int32_t num_q_heads, int32_t max_splits) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   ChunkWorkspace w;
-  const int64_t items = chunk_max_items(num_segments, total_q, num_kv_heads, num_q_heads / num_kv_heads, max_splits);
-  w.count_off = 0;
-  w.seg_off_off = 256;
-  w.items_off = w.seg_off_off + up((size_t(num_segments) + 1) * sizeof(int32_t));
-  size_t end = w.items_off + up(size_t(items) * 4 * sizeof(int32_t));
-  w.part_o_off = w.part_lse_off = end;
+  w.part_o_off = w.part_lse_off = w.total = 0;
   if (max_splits > 1) {
     const size_t rows = size_t(max_splits) * total_q * num_q_heads;  // Hkv * r == Hq
-    w.part_o_off = end;
-    w.part_lse_off = w.part_o_off + up(rows * kHeadDim * sizeof(float));
-    end = w.part_lse_off + up(rows * sizeof(float));
+    w.part_lse_off = up(rows * kHeadDim * sizeof(float));
+    w.total = w.part_lse_off + up(rows * sizeof(float));
   }
-  w.total = end;
   return w;
 }
 
-hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream) {
+hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream) {
   if (a.num_segments == 0 || a.total_q == 0) return hipSuccess;
-  if (a.split_tokens > 4096 || a.max_items <= 0) return hipErrorInvalidValue;
+  if (a.split_wide > 4096 || a.split_short > 4096 || a.split_wide % kStep || a.split_short % kStep ||
+      a.num_segments > 4096)
+    return hipErrorInvalidValue;
   switch (a.num_q_heads / pool.num_kv_heads) {
-    case 1: return launch_r<1>(pool, a, stream);
-    case 2: return launch_r<2>(pool, a, stream);
-    case 4: return launch_r<4>(pool, a, stream);
-    case 8: return launch_r<8>(pool, a, stream);
+    case 1: return launch_r<1>(pool, a, grids, stream);
+    case 2: return launch_r<2>(pool, a, grids, stream);
+    case 4: return launch_r<4>(pool, a, grids, stream);
+    case 8: return launch_r<8>(pool, a, grids, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -62,23 +62,26 @@ struct ChunkArgs {
   int32_t num_segments; int32_t total_q; int32_t num_q_heads;
   int32_t max_q_len; int32_t max_ctx;
   float qk_scale_log2;
-  int32_t split_tokens; int32_t max_splits;
-  int32_t max_items;     // grid of the main kernel: an upper bound of the work items
-  int32_t* item_count;   // written by the schedule kernel
-  int32_t* seg_off;      // [num_segments + 1] first item of each segment (schedule kernel)
-  int4* items;           // {segment, kv head, tile group, split}
-  float* part_o; float* part_lse;
+  int32_t split_wide;    // keys per split, segments of more than 32 rows per kv head
+  int32_t split_short;   // keys per split, segments of at most 32 rows per kv head
+  int32_t max_splits;    // partial slots per row: covers both split sizes
+  float* part_o;         // [Hkv][max_splits][total_q][r][128]
+  float* part_lse;       // [Hkv][max_splits][total_q][r]
   uint16_t* out;
 };
 
-hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, hipStream_t stream);
+// Grid sizes (upper bounds of the device-side work lists) of the chunk kernels.
+struct ChunkGrids {
+  int64_t wide, narrow, combine;
+};
+ChunkGrids chunk_grids(int32_t num_segments, int32_t total_q, int32_t num_kv_heads, int32_t group, int32_t max_q_len,
+                       int32_t max_ctx, int32_t split_wide, int32_t split_short, int32_t max_splits);
+
+hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream);
 
 struct ChunkWorkspace {
-  size_t count_off, seg_off_off, items_off, part_o_off, part_lse_off, total;
+  size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
 };
-int64_t chunk_max_items(int32_t num_segments, int32_t total_q, int32_t num_kv_heads, int32_t group,
-                        int32_t max_splits);
-ChunkWorkspace chunk_workspace_layout(int32_t num_segments, int32_t total_q, int32_t num_kv_heads,
-                                      int32_t num_q_heads, int32_t max_splits);
+ChunkWorkspace chunk_workspace_layout(int32_t total_q, int32_t num_q_heads, int32_t max_splits);
 
 }  // namespace pgqa
