@@ -434,8 +434,7 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
   // Wide items (segments of more than 32 rows per kv head) are 128 query rows
   // (4 waves) of one kv head over one key split: aim at two per CU over the
   // (row group, kv head) units the hints allow, splits of 256 .. 4096 keys.
-  // Short items are one wave over one key split of a short segment: aim at
-  // eight per CU over the (segment, kv head) units, splits of 128 .. 4096 keys.
+  // Short items are one wave over one key split of a short segment.
   const int64_t r = num_q_heads / num_kv_heads;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
   const int64_t cap = std::min<int64_t>(round_up(ctx, kChunkStep), kMaxSplitTokens);
@@ -445,14 +444,19 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
     split = std::max(split, floor_keys);
     return std::min(split, cap);
   };
+  const ChunkLists lists = chunk_lists(num_segments, total_q, int32_t(r), max_q_len);
   const int64_t wide_groups = (int64_t(total_q) * r + 127) / 128;
   const int64_t wide = pick(std::max<int64_t>(wide_groups, 1) * num_kv_heads, 2, 256);
-  // a lone segment of more than 32 rows per kv head has no short work
-  const bool lone_wide = num_segments == 1 && int64_t(total_q) * r > 32;
-  const int64_t narrow = lone_wide ? wide : pick(std::max<int64_t>(num_segments, 1) * num_kv_heads, 8, 128);
+  // Short splits: 256 keys (8 steps) unless that would list more than 16 items
+  // per CU, then as many keys as keep it at 16.
+  const int64_t units_s = std::max<int64_t>(num_segments, 1) * num_kv_heads;
+  const int64_t narrow =
+      lists.narrow ? std::min(cap, std::max<int64_t>(256, round_up(ctx * units_s / (16ll * num_cus) + 1, kChunkStep)))
+                   : wide;
+  const int64_t smallest = lists.wide ? std::min(wide, narrow) : narrow;
   out->split_tokens = int32_t(wide);
   out->short_split_tokens = int32_t(narrow);
-  out->max_splits = int32_t((ctx + std::min(wide, narrow) - 1) / std::min(wide, narrow));
+  out->max_splits = int32_t((ctx + smallest - 1) / smallest);
   out->reserved = 0;
   return PGQA_OK;
 }
@@ -472,7 +476,9 @@ pgqa_status chunk_sizing(const pgqa_chunk_plan& p, int32_t num_segments, int32_t
       return fail(PGQA_ERR_INVALID_ARG, "chunk plan split of %d keys must be a positive multiple of %d, at most %d",
                   sp, kChunkStep, kMaxSplitTokens);
   if (p.reserved != 0) return fail(PGQA_ERR_INVALID_ARG, "chunk plan reserved field must be 0");
-  const int32_t smallest = std::min(p.split_tokens, short_split);
+  const ChunkLists lists = chunk_lists(num_segments, total_q, hq / hkv, max_q_len);
+  const int32_t smallest = !lists.narrow ? p.split_tokens : !lists.wide ? short_split
+                                                                         : std::min(p.split_tokens, short_split);
   if (p.max_splits < (int64_t(max_context_len) + smallest - 1) / smallest || p.max_splits > 65535)
     return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
                 max_context_len);

@@ -56,13 +56,15 @@ constexpr int kRows = 32;                // query rows per tile (one wave)
 constexpr int kWideTiles = 4;            // row tiles (waves) of a wide item
 constexpr int kWideThreads = 64 * kWideTiles;
 constexpr int kStep = 32;                // keys per step
-constexpr int kSchedThreads = 256;
 constexpr int kKRow = 136;               // LDS K row stride in bf16 (128 + 8 padding)
 constexpr int kVRow = 40;                // LDS V^T row stride in bf16 (32 + 8 padding)
 constexpr int kKStage = kStep * kKRow;   // bf16 elements per stage
 constexpr int kVStage = kHeadDim * kVRow;
 constexpr int kRing = 3;                 // wide: LDS stages and register stages
 constexpr int kMaxBlockIds = 4096 / 16 + 1;  // block ids one split can touch
+constexpr int kCombineRows = 8;          // rows per combine workgroup (32 lanes each)
+constexpr int kCombineParts = kRows / kCombineRows;
+constexpr int kCombineChunk = 256;       // splits whose weights are staged in LDS at a time
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -125,7 +127,8 @@ __device__ __forceinline__ int wide_kend(const SegInfo& si, int grp, int r) {
 //           bad segment that claims more than one tile;
 //   short   {segment, kv head, 0, split} of one-tile segments; {.., -1, 0} for bad
 //           one-tile segments;
-//   combine {segment, kv head, tile, 0} for every row tile with several splits.
+//   combine {segment, kv head, tile, part} for every row tile with several splits,
+//           in kCombineParts parts of 8 rows.
 // No list is stored: every workgroup derives its own item from the segment
 // metadata (a wave-wide scan of per-segment counts, then a search), so no
 // schedule kernel and no dependent read of a stored list sits in front of the
@@ -145,11 +148,11 @@ __device__ __forceinline__ int list_count(const ChunkArgs& a, const SegInfo& si,
     return si.tiles == 1 ? hkv * cdiv(si.n, a.split_short) : 0;
   } else {
     if (si.tiles == 0) return 0;
-    if (si.tiles == 1) return cdiv(si.n, a.split_short) > 1 ? hkv : 0;
+    if (si.tiles == 1) return cdiv(si.n, a.split_short) > 1 ? hkv * kCombineParts : 0;
     int cnt = 0;
     for (int grp = 0; grp < wide_groups(si); ++grp)
       if (cdiv(wide_kend(si, grp, r), a.split_wide) > 1) cnt += min(kWideTiles, si.tiles - grp * kWideTiles);
-    return cnt * hkv;
+    return cnt * hkv * kCombineParts;
   }
 }
 
@@ -157,13 +160,14 @@ template <ListKind K>
 __device__ __forceinline__ int4 list_item(const ChunkArgs& a, const SegInfo& si, int s, int li, int r, int hkv) {
   if (K != kCombineList && si.bad) return make_int4(s, li, -1, 0);
   if (K == kShortList) return make_int4(s, li % hkv, 0, li / hkv);
-  if (K == kCombineList && si.tiles == 1) return make_int4(s, li, 0, 0);
+  if (K == kCombineList && si.tiles == 1) return make_int4(s, li % hkv, 0, li / hkv);
+  const int parts = K == kCombineList ? kCombineParts : 1;
   for (int grp = 0;; ++grp) {
     const int ns = cdiv(wide_kend(si, grp, r), a.split_wide);
-    const int per_head = K == kWideList ? ns : ns > 1 ? min(kWideTiles, si.tiles - grp * kWideTiles) : 0;
+    const int per_head = K == kWideList ? ns : ns > 1 ? min(kWideTiles, si.tiles - grp * kWideTiles) * parts : 0;
     if (li < per_head * hkv) {
       const int g = li % hkv, j = li / hkv;
-      return K == kWideList ? make_int4(s, g, grp, j) : make_int4(s, g, grp * kWideTiles + j, 0);
+      return K == kWideList ? make_int4(s, g, grp, j) : make_int4(s, g, grp * kWideTiles + j / parts, j % parts);
     }
     li -= per_head * hkv;
   }
@@ -607,55 +611,71 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
 }
 
 // ---------------------------------------------------------------- combine
-// Log-sum-exp combine of the split partials of one 32-row tile: thread t owns
-// row t/8 and dims 16 (t%8) .. +15; splits are merged in order.
+// Log-sum-exp combine of the split partials of 8 rows of one tile: 32 lanes
+// per row, each owning 4 dims.  The lanes of a row first reduce the row's
+// split lse values (lane j takes splits j, j+32, ...), then the split weights
+// go through LDS and every lane sums its 4 dims over the splits in order.
 template <int R>
 __global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, ChunkArgs a) {
   const Located loc = locate<kCombineList>(a, pool, blockIdx.x, R);
   if (loc.item.x < 0) return;
   const SegInfo& si = loc.si;
-  const int g = loc.item.y, tile = loc.item.z;
-  const int tid = threadIdx.x, row = tid >> 3, d0 = 16 * (tid & 7);
-  const int rho = tile * kRows + row;
-  if (rho >= si.rows) return;
-  int ns;
-  if (si.tiles == 1) {
-    ns = cdiv(si.n, a.split_short);
-  } else {
-    ns = cdiv(wide_kend(si, tile / kWideTiles, R), a.split_wide);
-  }
+  const int g = loc.item.y, tile = loc.item.z, part = loc.item.w;
+  const int tid = threadIdx.x, row = tid >> 5, j = tid & 31;
+  const int rho = tile * kRows + part * kCombineRows + row;
+  const int ns = si.tiles == 1 ? cdiv(si.n, a.split_short) : cdiv(wide_kend(si, tile / kWideTiles, R), a.split_wide);
+  const bool row_ok = rho < si.rows;
   const int tok = rho / R, hh = rho - tok * R;
   const int64_t qrow = int64_t(si.q0) + tok;
   const int64_t stride = int64_t(a.total_q) * R;  // partial rows per split
   const int64_t base = int64_t(g) * a.max_splits * stride + qrow * R + hh;
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, a.part_lse[base + k * stride]);
-  float4 o[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) o[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int k = 0; k < ns; ++k) {
+  __shared__ float s_w[kCombineRows][kCombineChunk];
+
+  // Row max and weight sum in one pass over the split lse values (lanes of a
+  // row are 32 consecutive threads): each lane keeps a running (max, sum) of
+  // its splits, then the 32 pairs are merged.
+  float M = -INFINITY, L = 0.f;
+  if (row_ok)
+    for (int k = j; k < ns; k += 32) {
       const float lk = a.part_lse[base + k * stride];
-      const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + (base + k * stride) * kHeadDim + d0);
-      L += e;
+      if (lk > M) {
+        L = L * fast_exp2(M - lk) + 1.f;
+        M = lk;
+      } else if (lk != -INFINITY) {
+        L += fast_exp2(lk - M);
+      }
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 v = src[j];
-        o[j].x += e * v.x; o[j].y += e * v.y; o[j].z += e * v.z; o[j].w += e * v.w;
+  for (int o = 16; o >= 1; o >>= 1) {
+    const float Mo = __shfl_xor(M, o), Lo = __shfl_xor(L, o);
+    const float Mn = fmaxf(M, Mo);
+    L = (M == -INFINITY ? 0.f : L * fast_exp2(M - Mn)) + (Mo == -INFINITY ? 0.f : Lo * fast_exp2(Mo - Mn));
+    M = Mn;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* src = a.part_o + base * kHeadDim + 4 * j;
+  for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
+    const int cn = min(kCombineChunk, ns - c0);
+    __syncthreads();
+    for (int k = j; k < cn; k += 32) {
+      const float lk = row_ok ? a.part_lse[base + (c0 + k) * stride] : -INFINITY;
+      s_w[row][k] = lk == -INFINITY || M == -INFINITY ? 0.f : fast_exp2(lk - M) * inv;
+    }
+    __syncthreads();
+    if (row_ok) {
+#pragma unroll 8
+      for (int k = 0; k < cn; ++k) {
+        const float w = s_w[row][k];
+        const float4 v = *reinterpret_cast<const float4*>(src + (c0 + k) * stride * kHeadDim);
+        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
       }
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* dst = a.out + (qrow * a.num_q_heads + loc.item.y * R + hh) * kHeadDim + d0;
-  uint4 w[2];
-  w[0] = make_uint4(pack_bf16x2(o[0].x * inv, o[0].y * inv), pack_bf16x2(o[0].z * inv, o[0].w * inv),
-                    pack_bf16x2(o[1].x * inv, o[1].y * inv), pack_bf16x2(o[1].z * inv, o[1].w * inv));
-  w[1] = make_uint4(pack_bf16x2(o[2].x * inv, o[2].y * inv), pack_bf16x2(o[2].z * inv, o[2].w * inv),
-                    pack_bf16x2(o[3].x * inv, o[3].y * inv), pack_bf16x2(o[3].z * inv, o[3].w * inv));
-  reinterpret_cast<uint4*>(dst)[0] = w[0];
-  reinterpret_cast<uint4*>(dst)[1] = w[1];
+  if (!row_ok) return;
+  uint16_t* dst = a.out + (qrow * a.num_q_heads + g * R + hh) * kHeadDim + 4 * j;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
 }
 
 template <int R>
@@ -684,16 +704,14 @@ ChunkGrids chunk_grids(int32_t num_segments, int32_t total_q, int32_t num_kv_hea
   ChunkGrids b;
   const int64_t ctx = max_ctx > 0 ? max_ctx : 1;
   const int64_t N = num_segments, hkv = num_kv_heads;
-  // Wide work exists if some segment may have more than one row tile (a lone
-  // segment holds all total_q tokens); short work unless a lone segment has more.
-  const bool wide = int64_t(max_q_len) * group > kRows || (N == 1 && int64_t(total_q) * group > kRows);
-  const bool narrow = !(N == 1 && int64_t(total_q) * group > kRows);
+  const ChunkLists lists = chunk_lists(num_segments, total_q, group, max_q_len);
+  const bool wide = lists.wide, narrow = lists.narrow;
   const int64_t rows_per_group = int64_t(kRows) * kWideTiles;
   const int64_t groups = (int64_t(total_q) * group + rows_per_group - 1) / rows_per_group + N;
   b.wide = wide ? (groups * ((ctx + split_wide - 1) / split_wide) + N) * hkv : 0;
   b.narrow = narrow ? N * hkv * ((ctx + split_short - 1) / split_short) : 0;
   const int64_t tiles = (int64_t(total_q) * group + kRows - 1) / kRows + N;
-  b.combine = max_splits > 1 ? tiles * hkv : 0;
+  b.combine = max_splits > 1 ? tiles * hkv * kCombineParts : 0;
   return b;
 }
 

@@ -70,6 +70,17 @@ struct ChunkArgs {
   uint16_t* out;
 };
 
+// Which chunk work lists a call can have: wide (segments of more than 32 rows
+// per kv head) if some segment may be that long (a lone segment holds all
+// total_q tokens), short unless a lone segment is longer.
+struct ChunkLists {
+  bool wide, narrow;
+};
+inline ChunkLists chunk_lists(int32_t num_segments, int32_t total_q, int32_t group, int32_t max_q_len) {
+  const bool lone_wide = num_segments == 1 && int64_t(total_q) * group > 32;
+  return ChunkLists{int64_t(max_q_len) * group > 32 || lone_wide, !lone_wide};
+}
+
 // Grid sizes (upper bounds of the device-side work lists) of the chunk kernels.
 struct ChunkGrids {
   int64_t wide, narrow, combine;
