@@ -140,11 +140,148 @@ def measure_rows(args, dev):
                 res[label] = {"us": round(med, 2), "tflops": round(flops / med / 1e6, 1),
                               "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                               "kv_gbs": round(kv / med / 1e3, 1), "flops": flops, "kv_bytes": kv,
-                              "plan": [cp.split_tokens, cp.max_splits]}
+                              "plan": {"split_tokens": cp.split_tokens, "short_split_tokens": cp.short_split_tokens,
+                                       "max_splits": cp.max_splits}}
             rows["chunk_cfg5"] = res
         del pools
         torch.cuda.empty_cache()
     return rows
+
+
+def measure_graphs(dev, iters=50):
+    """Decode step (cache write + decode over L layer pools) issued eagerly
+    through pre-bound calls vs replayed from one captured HIP graph:
+      *_gpu_us_per_layer   steps issued back to back, events around each step
+                           (GPU time, the host runs ahead);
+      *_sync_us_per_step   wall clock of one step issued and waited for (the
+                           latency a serving loop sees when the next step needs
+                           this one's output)."""
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_head_amd as pg
+    from paged_gqa_decode_head_amd.graphs import DecodeGraphs
+    from paged_gqa_decode_head_amd.workloads import SPECS, make_step
+
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    res = {}
+    for name, layers in (("cfg1", 28), ("cfg2", 4), ("cfg3b", 4)):
+        w = make_step(SPECS[name])
+        s = w.spec
+        B = w.num_decode
+        pools = []
+        for _ in range(layers):
+            p = pg.Pool(s.num_blocks, s.block_size, s.num_kv_heads, device=dev)
+            p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
+                           blocks=w.used_blocks)
+            pools.append(p)
+        pad = int(np.setdiff1d(np.arange(s.num_blocks), w.used_blocks)[0])
+        tok = w.dec_tok
+        g = DecodeGraphs(pools, s.num_q_heads, w.block_tables.shape[1], pad, to_bf16(w.wq), to_bf16(w.wk), s.eps,
+                         s.rope_theta, 1.0 / math.sqrt(128), max_batch=B, buckets=[B])
+        inp = g.inputs(B)
+        for l in range(layers):
+            inp.q[l].copy_(to_bf16(w.tok_q[tok]))
+            inp.k[l].copy_(to_bf16(w.tok_k[tok]))
+            inp.v[l].copy_(to_bf16(w.tok_v[tok]))
+        inp.positions.copy_(to_i32(w.tok_pos[tok]))
+        inp.context_lens.copy_(to_i32(w.dec_ctx))
+        inp.block_tables.copy_(to_i32(w.dec_block_tables))
+        eager = g.eager_calls(B)  # the calls the graph captured, issued one by one on this stream
+
+        def run_eager():
+            for c in eager:
+                c()
+
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        out = {"batch": B, "layers": layers}
+        for label, run in (("eager", run_eager), ("graph", lambda: g.replay(B))):
+            for _ in range(5):
+                run()
+            torch.cuda.synchronize()
+            for e0, e1 in ev:
+                e0.record()
+                run()
+                e1.record()
+            torch.cuda.synchronize()
+            ts = sorted(e0.elapsed_time(e1) * 1e3 / layers for e0, e1 in ev)
+            out[label + "_gpu_us_per_layer"] = round(ts[len(ts) // 2], 2)
+            wall = []
+            for _ in range(iters):
+                t0 = time.perf_counter()
+                run()
+                torch.cuda.synchronize()
+                wall.append((time.perf_counter() - t0) * 1e6)
+            out[label + "_sync_us_per_step"] = round(sorted(wall)[len(wall) // 2], 1)
+        res[name] = out
+        del g, pools, eager
+        torch.cuda.empty_cache()
+    return res
+
+
+def measure_block_sizes(dev, sizes=(16, 32, 64, 128, 256)):
+    """Decode on the batch-64 step and chunk attention on the mixed step at each
+    block size, with the pool's token capacity held fixed."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_head_amd as pg
+    from paged_gqa_decode_head_amd.workloads import SPECS, make_step
+
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    scale = 1.0 / math.sqrt(128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for bs in sizes:
+        row = {}
+        for name in ("cfg3b", "cfg5"):
+            base = SPECS[name]
+            spec = dataclasses.replace(base, block_size=bs, num_blocks=base.num_blocks * base.block_size // bs)
+            w = make_step(spec)
+            pools = []
+            for _ in range(2):
+                p = pg.Pool(spec.num_blocks, bs, spec.num_kv_heads, device=dev)
+                p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
+                               blocks=w.used_blocks)
+                pools.append(p)
+            q_out = torch.empty((w.num_tokens, spec.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+            writes = [pg.bind_cache_write(p, to_bf16(w.tok_q), to_bf16(w.tok_k), to_bf16(w.tok_v), to_bf16(w.wq),
+                                          to_bf16(w.wk), to_i32(w.tok_pos), to_i32(w.tok_seq),
+                                          to_i32(w.block_tables), spec.eps, spec.rope_theta, q_out) for p in pools]
+            med, _ = time_calls(writes, 20)
+            row[f"{name}_write_us"] = round(med, 2)
+            qd = q_out[torch.from_numpy(w.dec_tok.astype(np.int64)).to(dev)].contiguous()
+            mx = int(w.dec_ctx.max())
+            out = torch.empty((w.num_decode, spec.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+            plan = pg.plan_decode(cus, bs, w.num_decode, spec.num_kv_heads, spec.num_q_heads, mx)
+            calls = [pg.bind_decode(p, qd, to_i32(w.dec_ctx), to_i32(w.dec_block_tables), mx, scale, out, plan=plan)
+                     for p in pools]
+            med, _ = time_calls(calls, 30)
+            nb = decode_alg_bytes(w)
+            row[f"{name}_decode_us"] = round(med, 2)
+            row[f"{name}_decode_frac_hbm_peak"] = round(nb / med / 1e3 / HBM_PEAK_GBS, 4)
+            if name == "cfg5":
+                qc = q_out[w.chk_tok0:].contiguous()
+                qs, cx = w.chk_qsl, w.chk_ctx
+                mq, mc = int(np.diff(qs).max()), int(cx.max())
+                o2 = torch.empty((qc.shape[0], spec.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+                cp = pg.plan_chunk(cus, bs, len(cx), qc.shape[0], spec.num_kv_heads, spec.num_q_heads, mq, mc)
+                calls = [pg.bind_chunk(p, qc, to_i32(qs), to_i32(cx), to_i32(w.chk_block_tables), mq, mc, scale, o2,
+                                       plan=cp) for p in pools]
+                med, _ = time_calls(calls, 20)
+                flops, kv = chunk_alg(w, qs, cx)
+                row["cfg5_chunk_us"] = round(med, 2)
+                row["cfg5_chunk_frac_mfma_bf16_peak"] = round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)
+            for p in pools:
+                assert p.check_errors() == 0
+            del pools
+            torch.cuda.empty_cache()
+        res[str(bs)] = row
+    return res
 
 
 def copy_calibration(dev, mib=256, reps=5):
@@ -362,6 +499,8 @@ def main():
         del pools, calls
         torch.cuda.empty_cache()
         result["rows"] = measure_rows(args, dev)
+        result["rows"]["decode_graph"] = measure_graphs(dev)
+        result["rows"]["block_size"] = measure_block_sizes(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

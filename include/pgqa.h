@@ -152,7 +152,8 @@ typedef struct {
   int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64), <= 1024 * waves_per_split */
   int32_t max_splits;       /* ceil(max_context_len / split_tokens) */
   int32_t waves_per_split;  /* 64-lane waves per workgroup: 1, 2, 4 or 8 */
-  int32_t load_hint;        /* K/V loads: 0 library default, 1 cached, 2 streaming (non-temporal) */
+  int32_t load_hint;        /* K/V loads: 0 library default (streaming up to 32-token blocks, cached above),
+                               1 cached, 2 streaming (non-temporal) */
 } pgqa_decode_plan;
 
 /* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,
