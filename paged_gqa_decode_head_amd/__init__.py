@@ -22,6 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpgqa.so")
 
 PGQA_OK = 0
+PGQA_ERR_INVALID_ARG = 1
 STATUS_NAMES = {
     0: "PGQA_OK", 1: "PGQA_ERR_INVALID_ARG", 2: "PGQA_ERR_UNSUPPORTED", 3: "PGQA_ERR_POINTER_KIND",
     4: "PGQA_ERR_WORKSPACE", 5: "PGQA_ERR_HIP", 6: "PGQA_ERR_DEVICE",
@@ -59,6 +60,14 @@ class ChunkPlan(ctypes.Structure):
                 f"short_split_tokens={self.short_split_tokens})")
 
 
+class SchedConfig(ctypes.Structure):
+    _fields_ = [("token_budget", ctypes.c_int32), ("max_segments", ctypes.c_int32),
+                ("chunked_prefill", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32)]
+
+
+SEG_DECODE, SEG_VERIFY, SEG_PREFILL = 0, 1, 2
+
 _lib = None
 
 _P, _I32, _I64, _SZ, _F32, _F64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t,
@@ -84,6 +93,14 @@ _SIGNATURES = {
     "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)], _SZ),
     "pgqa_paged_chunk_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32,
                                     ctypes.POINTER(ChunkPlan), _P, _SZ, _P, _P], ctypes.c_int),
+    # host producers (include/pgqa_sched.h)
+    "pgqa_prompt_lookup": ([_P, _I32, _I32, _I32, _I32, _P], _I32),
+    "pgqa_accept_greedy": ([_P, _I32, _P, _P], _I32),
+    "pgqa_sched_plan_step": ([ctypes.POINTER(SchedConfig), _P, _I32, _P, _P, ctypes.POINTER(_I32), _P, _P, _P, _P,
+                              _P, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32)], ctypes.c_int),
+    "pgqa_sched_commit": ([_P, _I32, _P, _I32, _P], ctypes.c_int),
+    "pgqa_sched_release": ([ctypes.POINTER(SchedConfig), _P, _I32, _I32, _P, _P, ctypes.POINTER(_I32), _I32],
+                           ctypes.c_int),
 }
 
 
@@ -406,3 +423,98 @@ def bind_chunk(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q
             block_tables.shape[1], N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), pp,
             _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream))
     return BoundCall(lib().pgqa_paged_chunk_attention, args, keep)
+
+
+# ---------------------------------------------------------------- host producers
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+def _i32_array(x, name):
+    import numpy as np
+
+    a = np.ascontiguousarray(x, dtype=np.int32)
+    if a.ndim != 1:
+        raise ValueError(f"{name} must be 1-D")
+    return a
+
+
+def prompt_lookup(tokens, min_ngram: int, max_ngram: int, k: int):
+    """Draft of up to k tokens for a token history (pgqa_prompt_lookup); int32 array."""
+    import numpy as np
+
+    t = _i32_array(tokens, "tokens")
+    draft = np.zeros(max(k, 1), dtype=np.int32)
+    n = lib().pgqa_prompt_lookup(_np_ptr(t), t.size, min_ngram, max_ngram, k, _np_ptr(draft))
+    if n < 0:
+        raise PgqaError(PGQA_ERR_INVALID_ARG, lib().pgqa_last_error().decode())
+    return draft[:n]
+
+
+def accept_greedy(draft, target):
+    """Accepted draft prefix plus the target's next token (pgqa_accept_greedy); int32 array."""
+    import numpy as np
+
+    d, t = _i32_array(draft, "draft"), _i32_array(target, "target")
+    if t.size != d.size + 1:
+        raise ValueError("target needs len(draft) + 1 tokens")
+    out = np.zeros(d.size + 1, dtype=np.int32)
+    n = lib().pgqa_accept_greedy(_np_ptr(d), d.size, _np_ptr(t), _np_ptr(out))
+    if n < 0:
+        raise PgqaError(PGQA_ERR_INVALID_ARG, lib().pgqa_last_error().decode())
+    return out[:n]
+
+
+class StepPlanner:
+    """Chunked-prefill step planner over host state (pgqa_sched_*).
+
+    seqs: int32 [N, 4] rows (cached, prompt_left, num_draft, num_blocks);
+    block_tables: int32 [N, max_blocks_per_seq]; free_list: int32 stack of free
+    block ids (top = last of the first free_count entries)."""
+
+    def __init__(self, token_budget: int, max_segments: int, chunked_prefill: bool, block_size: int,
+                 max_blocks_per_seq: int, num_seqs: int, free_blocks):
+        import numpy as np
+
+        self.config = SchedConfig(token_budget, max_segments, int(bool(chunked_prefill)), block_size,
+                                  max_blocks_per_seq)
+        self.seqs = np.zeros((num_seqs, 4), dtype=np.int32)
+        self.block_tables = np.full((num_seqs, max_blocks_per_seq), -1, dtype=np.int32)
+        fb = np.ascontiguousarray(free_blocks, dtype=np.int32)
+        self.free_list = fb.copy()
+        self.free_count = ctypes.c_int32(fb.size)
+
+    def plan(self, token_capacity: int):
+        """One step: dict of segs [S, 4] (seq, kind, q_len, context_len), query_start_loc [S+1],
+        context_lens [S], token_pos [T], token_seq [T]."""
+        import numpy as np
+
+        ms = self.config.max_segments
+        segs = np.zeros((ms, 4), dtype=np.int32)
+        qsl = np.zeros(ms + 1, dtype=np.int32)
+        ctx = np.zeros(ms, dtype=np.int32)
+        pos = np.zeros(max(token_capacity, 1), dtype=np.int32)
+        sq = np.zeros(max(token_capacity, 1), dtype=np.int32)
+        nseg, ntok = ctypes.c_int32(0), ctypes.c_int32(0)
+        _check(lib().pgqa_sched_plan_step(ctypes.byref(self.config), _np_ptr(self.seqs), self.seqs.shape[0],
+                                          _np_ptr(self.block_tables), _np_ptr(self.free_list),
+                                          ctypes.byref(self.free_count), _np_ptr(segs), _np_ptr(qsl), _np_ptr(ctx),
+                                          _np_ptr(pos), _np_ptr(sq), token_capacity, ctypes.byref(nseg),
+                                          ctypes.byref(ntok)))
+        S, T = nseg.value, ntok.value
+        return {"segs": segs[:S].copy(), "query_start_loc": qsl[:S + 1].copy(), "context_lens": ctx[:S].copy(),
+                "token_pos": pos[:T].copy(), "token_seq": sq[:T].copy()}
+
+    def commit(self, segs, accepted=None):
+        import numpy as np
+
+        segs = np.ascontiguousarray(segs, dtype=np.int32)
+        acc = None if accepted is None else np.ascontiguousarray(accepted, dtype=np.int32)
+        _check(lib().pgqa_sched_commit(_np_ptr(self.seqs), self.seqs.shape[0], _np_ptr(segs), segs.shape[0],
+                                       _np_ptr(acc)))
+
+    def release(self, seq: int):
+        _check(lib().pgqa_sched_release(ctypes.byref(self.config), _np_ptr(self.seqs), self.seqs.shape[0], seq,
+                                        _np_ptr(self.block_tables), _np_ptr(self.free_list),
+                                        ctypes.byref(self.free_count), self.free_list.size))
+

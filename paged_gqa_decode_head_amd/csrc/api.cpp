@@ -19,6 +19,7 @@
 #include <new>
 
 #include "../../include/pgqa.h"
+#include "errors.hpp"
 #include "launch.hpp"
 
 using namespace pgqa;
@@ -35,16 +36,6 @@ struct pgqa_pool {
 };
 
 namespace {
-
-thread_local char g_err[512] = "";
-
-pgqa_status fail(pgqa_status s, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof(g_err), fmt, ap);
-  va_end(ap);
-  return s;
-}
 
 pgqa_status hip_fail(hipError_t e, const char* what) {
   return fail(PGQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -133,7 +124,7 @@ extern "C" {
 
 const char* pgqa_version(void) { return "0.1.0"; }
 
-const char* pgqa_last_error(void) { return g_err; }
+const char* pgqa_last_error(void) { return pgqa::last_error(); }
 
 const char* pgqa_status_string(pgqa_status s) {
   switch (s) {
@@ -156,7 +147,7 @@ size_t pgqa_pool_bytes(const pgqa_pool_config* cfg) {
 }
 
 pgqa_status pgqa_pool_create(const pgqa_pool_config* cfg, void* kv_storage, pgqa_pool** out) {
-  g_err[0] = 0;
+  clear_error();
   if (out == nullptr) return fail(PGQA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   if (cfg == nullptr) return fail(PGQA_ERR_INVALID_ARG, "cfg is NULL");
@@ -253,7 +244,7 @@ pgqa_status pgqa_rms_norm_rope_cache_write(pgqa_pool* pool, const void* q, int64
                                            const int32_t* block_tables, int32_t bt_stride, int32_t num_seqs,
                                            int32_t num_tokens, int32_t num_q_heads, float eps, double rope_theta,
                                            void* q_out, void* stream) {
-  g_err[0] = 0;
+  clear_error();
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   const int64_t hkv = pool->cfg.num_kv_heads;
@@ -376,7 +367,7 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
                                         int32_t num_q_heads, int32_t max_context_len, float scale,
                                         const pgqa_decode_plan* plan, void* workspace, size_t workspace_bytes,
                                         void* out, void* stream) {
-  g_err[0] = 0;
+  clear_error();
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   if (batch < 0 || batch > 65535) return fail(PGQA_ERR_INVALID_ARG, "batch=%d", batch);
@@ -523,7 +514,7 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
                                        int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t max_q_len,
                                        int32_t max_context_len, float scale, const pgqa_chunk_plan* plan,
                                        void* workspace, size_t workspace_bytes, void* out, void* stream) {
-  g_err[0] = 0;
+  clear_error();
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   const int32_t hkv = pool->cfg.num_kv_heads;

@@ -1,5 +1,6 @@
-"""The C-ABI library builds for gfx950, loads and exports what include/pgqa.h
-declares; host-side checks and the split planner work without a GPU."""
+"""The C-ABI library builds for gfx950, loads and exports what include/pgqa.h and
+include/pgqa_sched.h declare; host-side checks and the split planner work
+without a GPU."""
 import ctypes
 import os
 import re
@@ -12,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "pgqa.h")).read()
+    src = "".join(open(os.path.join(ROOT, "include", h)).read() for h in ("pgqa.h", "pgqa_sched.h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(pgqa_[a-z_]+)\s*\(", src)))
 
