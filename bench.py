@@ -284,6 +284,102 @@ def measure_block_sizes(dev, sizes=(16, 32, 64, 128, 256)):
     return res
 
 
+def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, tail=3):
+    """The decode-stall workload shape: `streams` decode streams (contexts
+    U[2048, 8192] already cached) and one prompt of `prompt_len` tokens injected
+    at step `inject_at`.  The step planner (host producers) feeds one fused
+    write and one attention call per step (the decode call when every segment
+    is a single token, else the chunk call); GPU time per step from events.
+    Chunked (token budget `budget`) vs whole-prompt prefill: worst and median
+    step time seen by the decode streams, and the prompt's time to its first
+    token.  Attention and cache write only: no projections or MLP."""
+    import numpy as np
+    import torch
+
+    import paged_gqa_decode_head_amd as pg
+
+    rng = np.random.default_rng(606)
+    bs, hkv, hq = 16, 8, 16
+    width = (8192 + 64 + 8) // bs + 1
+    ctx0 = rng.integers(2048, 8193, size=streams)
+    nb = int(sum(-(-int(c + 64) // bs) for c in ctx0) + -(-prompt_len // bs) + 64)
+    scale = 1.0 / math.sqrt(128)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    pool = pg.Pool(nb, bs, hkv, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    pool.storage.normal_(generator=g)
+    wq = torch.ones(128, dtype=torch.bfloat16, device=dev)
+    wk = torch.ones(128, dtype=torch.bfloat16, device=dev)
+    qkv_cap = prompt_len + streams * 8
+    q_all = torch.randn((qkv_cap, hq, 128), device=dev, generator=g).to(torch.bfloat16)
+    k_all = torch.randn((qkv_cap, hkv, 128), device=dev, generator=g).to(torch.bfloat16)
+    v_all = torch.randn((qkv_cap, hkv, 128), device=dev, generator=g).to(torch.bfloat16)
+    q_buf = torch.empty((qkv_cap, hq, 128), dtype=torch.bfloat16, device=dev)
+    o_buf = torch.empty((qkv_cap, hq, 128), dtype=torch.bfloat16, device=dev)
+    res = {}
+    for label, chunked in (("chunked", True), ("whole_prompt", False)):
+        planner = pg.StepPlanner(budget, streams + 1, chunked, bs, width, streams + 1, np.arange(nb)[::-1])
+        for i in range(streams):  # streams whose prefix is already cached (blocks taken directly)
+            need = -(-int(ctx0[i]) // bs)
+            planner.block_tables[i, :need] = planner.free_list[planner.free_count.value - need:
+                                                                planner.free_count.value][::-1]
+            planner.free_count.value -= need
+            planner.seqs[i] = [int(ctx0[i]), 0, 0, need]
+        step_us, decode_gap_us = [], []
+        prompt_done_us, t_inject = None, None
+        elapsed = 0.0
+        step = 0
+        while True:
+            if step == inject_at:
+                planner.seqs[streams] = [0, prompt_len, 0, 0]
+                t_inject = elapsed
+            plan = planner.plan(token_capacity=qkv_cap)
+            segs = plan["segs"]
+            T = plan["token_pos"].size
+            bt_seg = np.ascontiguousarray(planner.block_tables[segs[:, 0]])
+            ctx, qsl = plan["context_lens"], plan["query_start_loc"]
+            args = (to_i32(plan["token_pos"]), to_i32(plan["token_seq"]), to_i32(planner.block_tables),
+                    to_i32(qsl), to_i32(ctx), to_i32(bt_seg))
+            q_out = q_buf[:T]
+            out = o_buf[:T]
+            calls = [pg.bind_cache_write(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[0], args[1], args[2],
+                                         1e-6, 1e6, q_out)]
+            if (segs[:, 2] == 1).all():  # host routing: single decode tokens only -> the decode call
+                calls.append(pg.bind_decode(pool, q_out, args[4], args[5], int(ctx.max()), scale, out))
+            else:
+                calls.append(pg.bind_chunk(pool, q_out, args[3], args[4], args[5], int(segs[:, 2].max()),
+                                           int(ctx.max()), scale, out))
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for c in calls:
+                c()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3
+            elapsed += us
+            step_us.append(round(us, 1))
+            planner.commit(segs, None)
+            if t_inject is not None and prompt_done_us is None and planner.seqs[streams, 1] == 0 and \
+                    planner.seqs[streams, 0] > 0:
+                prompt_done_us = elapsed - t_inject
+                done_step = step
+            step += 1
+            if prompt_done_us is not None and step > done_step + tail:
+                break
+        assert pool.check_errors() == 0
+        res[label] = {"steps": len(step_us), "worst_step_us": max(step_us),
+                      "median_step_us": float(np.median(step_us)), "prompt_ttft_us": round(prompt_done_us, 1),
+                      "step_us": step_us}
+    res["worst_step_ratio_whole_over_chunked"] = round(res["whole_prompt"]["worst_step_us"] /
+                                                       res["chunked"]["worst_step_us"], 2)
+    res["config"] = {"streams": streams, "stream_contexts": ctx0.tolist(), "prompt_len": prompt_len,
+                     "token_budget": budget, "block_size": bs, "heads": [hq, hkv]}
+    return res
+
+
 def copy_calibration(dev, mib=256, reps=5):
     """A plain streaming kernel of known size (torch.neg: reads and writes `mib`
     MiB per launch, easy to find by name in a counter trace), for scaling the
@@ -501,6 +597,7 @@ def main():
         result["rows"] = measure_rows(args, dev)
         result["rows"]["decode_graph"] = measure_graphs(dev)
         result["rows"]["block_size"] = measure_block_sizes(dev)
+        result["rows"]["serving_decode_stall"] = measure_serving(dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
