@@ -43,7 +43,7 @@ SEGS = [(0, 7), (20, 5), (33, 1), (3, 40), (9, 0), (100, 64), (250, 33), (1, 1),
 
 
 @pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
-                                       (16, 4, 256)])
+                                       (16, 4, 256), (8, 1, 16)])
 @pytest.mark.parametrize("split", [None, 64, 256, 4096])
 def test_chunk_small_ragged(hq, hkv, bs, split):
     spec = _chunk_spec(f"chunk-{hq}-{hkv}-{bs}", 700 + hq + bs, hq, hkv, bs, SEGS, 256 if bs < 256 else 16)
@@ -193,3 +193,37 @@ def test_chunk_bad_metadata_flags_and_zero_rows():
     pg.paged_chunk_attention(run.pool, q[:0], run.chk_qsl[:1], run.chk_ctx[:0], run.chk_bt[:0], 0, 0, SCALE,
                              out=out[:0])
     assert run.pool.check_errors() == 0
+
+
+@pytest.mark.parametrize("q_len", [5, 40])  # a short (verify-sized) and a wide segment
+def test_chunk_addressing_probe_one_hot_every_position(q_len):
+    """Only key j* matches every query strongly: each query that sees j* must
+    return V_j* bit-exactly, for every logical position j* (every block-table
+    entry and offset), for a short and a wide segment, with one and many splits."""
+    bs, hkv, hq = 16, 2, 4
+    prefix = 60
+    n = prefix + q_len
+    nb = 24
+    rng = np.random.default_rng(17 + q_len)
+    perm = rng.permutation(nb)
+    nblk = -(-n // bs)
+    bt = np.full((1, nblk), -1, dtype=np.int32)
+    bt[0] = perm[:nblk]
+    pool = pg.Pool(nb, bs, hkv)
+    u = np.zeros(128)
+    u[:32] = 1.0
+    vk = O.f64_to_bf16_bits(rng.standard_normal((nb, bs, hkv, 128)))
+    q = dev_bf16(np.broadcast_to(O.f64_to_bf16_bits(u), (q_len, hq, 128)).copy())
+    hot = O.f64_to_bf16_bits(15.0 * u)
+    qsl, ctx, bt_d = dev_i32(np.array([0, q_len])), dev_i32(np.array([n])), dev_i32(bt)
+    for jstar in range(n):
+        kk = np.zeros((nb, bs, hkv, 128), dtype=np.uint16)
+        kk[bt[0, jstar // bs], jstar % bs] = hot
+        pool.fill_logical(kk.view(np.int16), vk.view(np.int16))
+        for plan in (pg.ChunkPlan(32, -(-n // 32), 32, 0), pg.ChunkPlan(4096, 1, 4096, 0)):
+            out = bits_of(pg.paged_chunk_attention(pool, q, qsl, ctx, bt_d, q_len, n, SCALE, plan=plan))
+            for i in range(q_len):
+                if jstar <= prefix + i:  # query i sees key j*
+                    for h in range(hq):
+                        assert np.array_equal(out[i, h], vk[bt[0, jstar // bs], jstar % bs, h // 2]), (jstar, i, h)
+

@@ -92,7 +92,7 @@ def test_cfg1_end_to_end_chain():
 
 
 @pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
-                                       (16, 4, 256)])
+                                       (16, 4, 256), (8, 1, 16), (2, 1, 128)])
 @pytest.mark.parametrize("plan", [None, (64, 1), (128, 2), (256, 4), (512, 8), (4096, 4)])
 def test_decode_small_shapes_and_plans(hq, hkv, bs, plan):
     spec = StepSpec(f"small-{hq}-{hkv}-{bs}", 901 + hq + bs, hq, hkv, 256 if bs < 256 else 32,
@@ -255,3 +255,20 @@ def test_decode_ignores_garbage_past_the_context():
     for plan in (None, pg.DecodePlan(64, 5, 1, 0), pg.DecodePlan(4096, 1, 8, 0)):
         out = run.decode(plan=plan, q=q)
         compare(out, run.oracle_decode_on_gpu_inputs(q), f"garbage plan={plan}")
+
+
+def test_unsupported_group_size_is_rejected():
+    """r = Hq / Hkv outside {1, 2, 4, 8}, or Hq not a multiple of Hkv: an error
+    status before anything is enqueued, never a fallback."""
+    w = make_step(StepSpec("grp", 975, 16, 8, 16, decode=(Group(2, 5, 5),)))
+    run = StepRun(w)
+    run.write()
+    for hq in (128, 12):  # r = 16; Hq not a multiple of Hkv
+        q = torch.zeros((2, hq, 128), dtype=torch.bfloat16, device="cuda")
+        with pytest.raises(pg.PgqaError) as e:
+            pg.paged_decode_attention(run.pool, q, run.dec_ctx, run.dec_bt, 8, SCALE)
+        assert e.value.status in (pg.PGQA_ERR_INVALID_ARG, 2)
+        with pytest.raises(pg.PgqaError):
+            pg.paged_chunk_attention(run.pool, q, dev_i32(np.array([0, 1, 2], dtype=np.int32)), run.dec_ctx,
+                                     run.dec_bt, 1, 8, SCALE)
+
