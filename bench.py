@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Paged GQA decode step benchmark on one MI355X.
 
-A step is one pass of the decode hot path over one batch: the fused per-head
-RMSNorm + rotary + paged K/V cache write of the batch's new tokens, then paged
-split-KV GQA decode attention with the log-sum-exp combine.  The default
+A step is one pass of the decode hot path over one batch: per-head RMSNorm +
+rotary of the batch's new tokens, their paged K/V cache write, and paged
+split-KV GQA decode attention with the log-sum-exp combine, issued as the one
+fused launch ``pgqa_decode_step`` (the same step as the two calls cache write +
+decode attention, which are timed beside it as ``two_call_step``).  The default
 workload is the Qwen3-1.7B decode shape at batch 64 (16 q heads, 8 kv heads,
 head_dim 128, block size 16, contexts uniform in [1024, 2048], shuffled block
 tables, N(0,1) bf16 inputs).
@@ -39,6 +41,15 @@ def decode_alg_bytes(w) -> int:
     qo = 2 * w.num_decode * s.num_q_heads * 128 * 2
     bt = int((-(-n // s.block_size)).sum()) * 4
     return kv + qo + bt + w.num_decode * 4
+
+
+def step_alg_bytes(w) -> int:
+    """The fused step: decode's bytes (every key's K and V row, raw q in, out) plus
+    the new tokens' raw k and v in, their normed k and v into the cache, and the
+    two weight vectors."""
+    s = w.spec
+    kv_rows = w.num_decode * s.num_kv_heads * 128 * 2
+    return decode_alg_bytes(w) + 2 * kv_rows + 2 * kv_rows + 2 * 128 * 2
 
 
 def write_alg_bytes(w) -> int:
@@ -403,7 +414,7 @@ def recorded_traffic():
     try:
         rec = json.load(open(path))
         src = b"".join(open(os.path.join(ROOT, "paged_gqa_decode_head_amd", "csrc", f), "rb").read()
-                       for f in ("decode.hip", "device_common.hpp"))
+                       for f in ("decode.hip", "device_common.hpp", "norm_rope.hpp"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
@@ -503,46 +514,66 @@ def main():
     ws = torch.zeros(pg.decode_workspace_bytes(pools[0], w.num_decode, s.num_q_heads, max_ctx, plan),
                      dtype=torch.uint8, device=dev)
     assert w.num_tokens == w.num_decode and np.array_equal(w.dec_tok, np.arange(w.num_decode))
-    calls = []
-    for p in pools:
-        calls.append((pg.bind_cache_write(p, q, k, v, wq, wk, pos, seq, bt, s.eps, s.rope_theta, q_out),
-                      pg.bind_decode(p, q_out, ctx, bt, max_ctx, scale, out, plan=plan, workspace=ws)))
+    assert np.array_equal(w.tok_pos, w.dec_ctx - 1)
+    fused = [pg.bind_decode_step(p, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, out, plan=plan,
+                                 workspace=ws) for p in pools]
+    two = [(pg.bind_cache_write(p, q, k, v, wq, wk, pos, seq, bt, s.eps, s.rope_theta, q_out),
+            pg.bind_decode(p, q_out, ctx, bt, max_ctx, scale, out, plan=plan, workspace=ws)) for p in pools]
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.warmup):
-        wr, dc = calls[i % args.layers]
+    def timed(issue, marks):
+        """Run warmup + steps; returns (wall ms per step, [per-step event lists])."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(args.steps)]
+        for i in range(args.warmup):
+            issue(i, None)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            issue(i, ev[i])
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps, ev
+
+    def issue_fused(i, e):
+        if e:
+            e[0].record()
+        fused[i % args.layers]()
+        if e:
+            e[1].record()
+
+    def issue_two(i, e):
+        wr, dc = two[i % args.layers]
+        if e:
+            e[0].record()
         wr()
+        if e:
+            e[1].record()
         dc()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        wr, dc = calls[i % args.layers]
-        e0, e1, e2 = ev[i]
-        e0.record()
-        wr()
-        e1.record()
-        dc()
-        e2.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+        if e:
+            e[2].record()
+
+    ms_two, ev_two = timed(issue_two, 3)
+    ms_step, ev = timed(issue_fused, 2)
     for p in pools:
         assert p.check_errors() == 0
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    write_ms = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / args.steps
-    decode_ms = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / args.steps
+    step_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    write_ms = sum(e[0].elapsed_time(e[1]) for e in ev_two) / args.steps
+    decode_ms = sum(e[1].elapsed_time(e[2]) for e in ev_two) / args.steps
     dec_bytes = decode_alg_bytes(w)
     wr_bytes = write_alg_bytes(w)
-    step_bytes = dec_bytes + wr_bytes
+    step_bytes = step_alg_bytes(w)
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    dec_gbs = dec_bytes / (decode_ms * 1e-3) / 1e9
+    launch_gbs = step_bytes / (step_ms * 1e-3) / 1e9
+    two_bytes = dec_bytes + wr_bytes
 
-    # sampled parity of the last step's output against the fp64 reference
+    # sampled parity of one fused step (q_out requested so the reference sees the q the kernel used)
     import oracle as O
 
+    fused_pool = pools[0]
+    pg.decode_step(fused_pool, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, plan=plan,
+                   workspace=ws, out=out, q_out=q_out)
+    torch.cuda.synchronize()
     rows = [0, w.num_decode // 2, w.num_decode - 1]
-    k_all, v_all = pools[(args.steps - 1) % args.layers].read_logical(blocks=w.used_blocks)
+    k_all, v_all = fused_pool.read_logical(blocks=w.used_blocks)
     inv = np.full(s.num_blocks, -1, dtype=np.int64)
     inv[w.used_blocks] = np.arange(len(w.used_blocks))
     bt_c = np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1)
@@ -578,21 +609,27 @@ def main():
         "seqs_per_s": round(w.num_decode / (ms_step * 1e-3), 1),
         "tokens_per_s": round(w.num_decode / (ms_step * 1e-3), 1),
         "step_alg_bytes": step_bytes,
-        "decode_us": round(decode_ms * 1e3, 3),
-        "write_us": round(write_ms * 1e3, 3),
+        "step_us_events": round(step_ms * 1e3, 3),
         "roofline": {
-            "kernel": "decode_kernel (paged split-KV decode + fused combine)",
-            "bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+            "kernel": "decode_kernel<2, 4, true, true> (fused decode step: norm + rotary + cache write + decode)",
+            "bound": "hbm", "achieved": round(launch_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(launch_gbs / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic() if args.workload == "cfg3b" else None,
-            "alg_bytes_per_launch": dec_bytes, "avg_launch_us": round(decode_ms * 1e3, 3),
+            "alg_bytes_per_launch": step_bytes, "avg_launch_us": round(step_ms * 1e3, 3),
+        },
+        "two_call_step": {
+            "calls": "pgqa_rms_norm_rope_cache_write + pgqa_paged_decode_attention",
+            "ms_per_step": round(ms_two, 5), "alg_bytes": two_bytes,
+            "value_gbs": round(two_bytes / (ms_two * 1e-3) / 1e9, 2),
+            "write_us": round(write_ms * 1e3, 3), "decode_us": round(decode_ms * 1e3, 3),
+            "decode_gbs": round(dec_bytes / (decode_ms * 1e-3) / 1e9, 2),
         },
         "parity_sample": parity,
     }
     if args.calibrate_copy:
         result["copy_calibration"] = copy_calibration(dev)
     if not args.main_only:
-        del pools, calls
+        del pools, fused, two, fused_pool
         torch.cuda.empty_cache()
         result["rows"] = measure_rows(args, dev)
         result["rows"]["decode_graph"] = measure_graphs(dev)

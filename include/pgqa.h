@@ -197,6 +197,39 @@ pgqa_status pgqa_paged_decode_attention(
     void* out, void* stream);
 
 /*
+ * a1..a5 in one launch for a pure decode batch: each sequence b has one new
+ * token at position context_lens[b] - 1 (its cached tokens come first, [P1]
+ * Summary item 1's decode route).  The token's raw q, k, v rows are normed
+ * (per-head RMSNorm, weights q_norm_weight / k_norm_weight, eps) and rotated
+ * (neox, rope_theta) exactly as pgqa_rms_norm_rope_cache_write does (same device
+ * code, identical bits), k and v are written into the token's cache slot, and
+ * paged decode attention over keys 0 .. context_lens[b] - 1 follows, as in
+ * pgqa_paged_decode_attention with the same plan and workspace rules.  The
+ * separate write launch and its round trip of q through memory disappear.
+ *
+ *   q, k, v       device bf16 rows per sequence: [batch][row stride], heads
+ *                 contiguous from the row start ([Hq][128] / [Hkv][128])
+ *   q_out         device bf16 [batch][Hq][128] for the normed, rotated q, or NULL
+ *   out           device bf16 [batch][Hq][128]
+ *
+ * A sequence with context_lens[b] == 0 has no new token: nothing is written
+ * and its output rows are zero.  Metadata errors behave as in the two calls it
+ * replaces (flags in the pool's error word, no out-of-bounds access).
+ */
+pgqa_status pgqa_decode_step(
+    pgqa_pool* pool,
+    const void* q, int64_t q_row_stride,
+    const void* k, int64_t k_row_stride,
+    const void* v, int64_t v_row_stride,
+    const void* q_norm_weight, const void* k_norm_weight,
+    float eps, double rope_theta,
+    const int32_t* context_lens, const int32_t* block_tables, int32_t bt_stride,
+    int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+    float scale, const pgqa_decode_plan* plan,
+    void* workspace, size_t workspace_bytes,
+    void* q_out, void* out, void* stream);
+
+/*
  * Split plan of a chunk call.  Rows are (token, query head) pairs of one kv
  * head.  A segment with more than 32 rows per kv head (a prefill slice) is cut
  * into groups of 128 rows that read their keys in splits of split_tokens keys;

@@ -88,6 +88,8 @@ _SIGNATURES = {
     "pgqa_decode_workspace_bytes": ([_P, _I32, _I32, _I32, ctypes.POINTER(DecodePlan)], _SZ),
     "pgqa_paged_decode_attention": ([_P, _P, _P, _P, _I32, _I32, _I32, _I32, _F32, ctypes.POINTER(DecodePlan),
                                      _P, _SZ, _P, _P], ctypes.c_int),
+    "pgqa_decode_step": ([_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _F32, _F64, _P, _P, _I32, _I32, _I32, _I32,
+                          _F32, ctypes.POINTER(DecodePlan), _P, _SZ, _P, _P, _P], ctypes.c_int),
     "pgqa_plan_chunk": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)],
                         ctypes.c_int),
     "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)], _SZ),
@@ -330,6 +332,37 @@ def paged_decode_attention(pool: Pool, q, context_lens, block_tables, max_contex
     return out
 
 
+def decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens, block_tables, max_context_len: int,
+                eps: float, rope_theta: float, scale: float, plan: DecodePlan = None, workspace=None, out=None,
+                q_out=None, stream=None):
+    """Fused decode step: norm + rotary of each sequence's new token (at position
+    context_lens[b] - 1), its cache write, and decode attention; returns out
+    [B, Hq, 128] bf16.  q/k/v: [B, H, 128] bf16 (or row-strided 2-D views)."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
+        if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != 128):
+            raise ValueError(f"{name}: heads must be contiguous 128-element rows")
+    _require(context_lens, "context_lens", torch.int32, pool.device)
+    _require(block_tables, "block_tables", torch.int32, pool.device)
+    B, hq = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device=pool.device)
+    _require(out, "out", torch.bfloat16, pool.device)
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
+    if workspace is None:
+        workspace = pool.workspace(need, "decode")
+    _check(lib().pgqa_decode_step(
+        pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
+        _ptr(k_norm_weight), float(eps), float(rope_theta), _ptr(context_lens), _ptr(block_tables),
+        block_tables.shape[1], B, hq, int(max_context_len), float(scale), pp, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), None if q_out is None else _ptr(q_out), _ptr(out),
+        _stream(stream)))
+    return out
+
+
 def plan_chunk(num_cus, block_size, num_segments, total_q, num_kv_heads, num_q_heads, max_q_len,
                max_context_len) -> ChunkPlan:
     p = ChunkPlan()
@@ -408,6 +441,23 @@ def bind_decode(pool: Pool, q, context_lens, block_tables, max_context_len: int,
             int(max_context_len), float(scale), pp, _ptr(workspace), workspace.numel() * workspace.element_size(),
             _ptr(out), _stream(stream))
     return BoundCall(lib().pgqa_paged_decode_attention, args, keep)
+
+
+def bind_decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens, block_tables,
+                     max_context_len: int, eps: float, rope_theta: float, scale: float, out, plan: DecodePlan = None,
+                     workspace=None, q_out=None, stream=None) -> BoundCall:
+    B, hq = q.shape[0], q.shape[1]
+    pp = None if plan is None else ctypes.byref(plan)
+    need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
+    if workspace is None:
+        workspace = pool.workspace(need, "decode")
+    keep = (q, k, v, q_norm_weight, k_norm_weight, context_lens, block_tables, out, workspace, plan, q_out)
+    args = (pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
+            _ptr(k_norm_weight), float(eps), float(rope_theta), _ptr(context_lens), _ptr(block_tables),
+            block_tables.shape[1], B, hq, int(max_context_len), float(scale), pp, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), None if q_out is None else _ptr(q_out), _ptr(out),
+            _stream(stream))
+    return BoundCall(lib().pgqa_decode_step, args, keep)
 
 
 def bind_chunk(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int, max_context_len: int,

@@ -118,6 +118,16 @@ pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t
   return PGQA_OK;
 }
 
+// Rotary turn frequencies of rope_theta (host fp64), cached in the pool.
+void rope_table(pgqa_pool* pool, double rope_theta, double (&out)[64]) {
+  std::lock_guard<std::mutex> lock(pool->rope_mu);
+  if (pool->rope_theta != rope_theta) {
+    for (int i = 0; i < 64; ++i) pool->rev_freq[i] = std::pow(rope_theta, -2.0 * i / 128.0) / (2.0 * M_PI);
+    pool->rope_theta = rope_theta;
+  }
+  std::memcpy(out, pool->rev_freq, sizeof(out));
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,14 +302,7 @@ pgqa_status pgqa_rms_norm_rope_cache_write(pgqa_pool* pool, const void* q, int64
   a.num_tokens = num_tokens;
   a.num_q_heads = num_q_heads;
   a.eps = eps;
-  {
-    std::lock_guard<std::mutex> lock(pool->rope_mu);
-    if (pool->rope_theta != rope_theta) {
-      for (int i = 0; i < 64; ++i) pool->rev_freq[i] = std::pow(rope_theta, -2.0 * i / 128.0) / (2.0 * M_PI);
-      pool->rope_theta = rope_theta;
-    }
-    std::memcpy(a.rev_freq, pool->rev_freq, sizeof(a.rev_freq));
-  }
+  rope_table(pool, rope_theta, a.rev_freq);
   a.q_out = static_cast<uint16_t*>(q_out);
   hipError_t e = launch_cache_write(pool->geom, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache write launch");
@@ -362,12 +365,13 @@ size_t pgqa_decode_workspace_bytes(const pgqa_pool* pool, int32_t batch, int32_t
       .total;
 }
 
-pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const int32_t* context_lens,
-                                        const int32_t* block_tables, int32_t bt_stride, int32_t batch,
-                                        int32_t num_q_heads, int32_t max_context_len, float scale,
-                                        const pgqa_decode_plan* plan, void* workspace, size_t workspace_bytes,
-                                        void* out, void* stream) {
-  clear_error();
+namespace {
+
+// Shared by the plain decode call and the fused decode step (st != nullptr).
+pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, const int32_t* context_lens,
+                          const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
+                          int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
+                          size_t workspace_bytes, void* out, void* stream, const StepArgs* st) {
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   if (batch < 0 || batch > 65535) return fail(PGQA_ERR_INVALID_ARG, "batch=%d", batch);
@@ -376,6 +380,9 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   if (bt_stride <= 0) return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d", bt_stride);
   if (max_context_len < 0) return fail(PGQA_ERR_INVALID_ARG, "max_context_len=%d", max_context_len);
   if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PGQA_ERR_INVALID_ARG, "scale=%g", double(scale));
+  if (q_row_stride < int64_t(num_q_heads) * 128 || q_row_stride % 8)
+    return fail(PGQA_ERR_INVALID_ARG, "q row stride %lld (at least num_q_heads * 128, a multiple of 8)",
+                (long long)q_row_stride);
   if (batch == 0) return PGQA_OK;
   pgqa_decode_plan p;
   if (plan != nullptr) {
@@ -400,6 +407,7 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   }
   DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
+  a.q_stride = q_row_stride;
   a.ctx = context_lens;
   a.bt = block_tables;
   a.bt_stride = bt_stride;
@@ -415,9 +423,60 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
   a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
   a.out = static_cast<uint16_t*>(out);
-  hipError_t e = launch_decode(pool->geom, a, static_cast<hipStream_t>(stream));
+  hipError_t e = launch_decode(pool->geom, a, st, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PGQA_OK;
+}
+
+}  // namespace
+
+pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const int32_t* context_lens,
+                                        const int32_t* block_tables, int32_t bt_stride, int32_t batch,
+                                        int32_t num_q_heads, int32_t max_context_len, float scale,
+                                        const pgqa_decode_plan* plan, void* workspace, size_t workspace_bytes,
+                                        void* out, void* stream) {
+  clear_error();
+  PGQA_TRY(check_pool(pool));
+  return decode_common(pool, q, int64_t(num_q_heads) * 128, context_lens, block_tables, bt_stride, batch,
+                       num_q_heads, max_context_len, scale, plan, workspace, workspace_bytes, out, stream, nullptr);
+}
+
+pgqa_status pgqa_decode_step(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
+                             int64_t k_row_stride, const void* v, int64_t v_row_stride, const void* q_norm_weight,
+                             const void* k_norm_weight, float eps, double rope_theta, const int32_t* context_lens,
+                             const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
+                             int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
+                             size_t workspace_bytes, void* q_out, void* out, void* stream) {
+  clear_error();
+  PGQA_TRY(check_pool(pool));
+  PGQA_TRY(check_group(pool, num_q_heads));
+  const int64_t hkv = pool->cfg.num_kv_heads;
+  if (k_row_stride < hkv * 128 || v_row_stride < hkv * 128 || k_row_stride % 8 || v_row_stride % 8)
+    return fail(PGQA_ERR_INVALID_ARG, "k/v row strides (%lld, %lld): at least num_kv_heads * 128, multiples of 8",
+                (long long)k_row_stride, (long long)v_row_stride);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(PGQA_ERR_INVALID_ARG, "eps=%g", double(eps));
+  if (!(rope_theta > 0.0) || !std::isfinite(rope_theta))
+    return fail(PGQA_ERR_INVALID_ARG, "rope_theta=%g", rope_theta);
+  if (batch > 0) {
+    const int dev = pool->device;
+    PGQA_TRY(check_device_ptr(k, dev, "k", 16));
+    PGQA_TRY(check_device_ptr(v, dev, "v", 16));
+    PGQA_TRY(check_device_ptr(q_norm_weight, dev, "q_norm_weight", 16));
+    PGQA_TRY(check_device_ptr(k_norm_weight, dev, "k_norm_weight", 16));
+    if (q_out != nullptr) PGQA_TRY(check_device_ptr(q_out, dev, "q_out", 16));
+  }
+  StepArgs st;
+  st.k = static_cast<const uint16_t*>(k);
+  st.k_stride = k_row_stride;
+  st.v = static_cast<const uint16_t*>(v);
+  st.v_stride = v_row_stride;
+  st.wq = static_cast<const uint16_t*>(q_norm_weight);
+  st.wk = static_cast<const uint16_t*>(k_norm_weight);
+  st.eps = eps;
+  st.q_out = static_cast<uint16_t*>(q_out);
+  rope_table(pool, rope_theta, st.rev_freq);
+  return decode_common(pool, q, q_row_stride, context_lens, block_tables, bt_stride, batch, num_q_heads,
+                       max_context_len, scale, plan, workspace, workspace_bytes, out, stream, &st);
 }
 
 pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_segments, int32_t total_q,

@@ -15,14 +15,14 @@
 // bound by latency, not bandwidth.
 //
 // Rotation angles: pair i of a token at position p turns by p * theta^(-2i/128)
-// radians.  At p near 32768 an fp32 product is already off by ~2e-3 rad, so the
-// angle is reduced in fp64 as a fraction of a turn, frac(p * f_i / 2pi), and
-// only that fraction (exact to ~1e-12) goes to an fp32 sincos.  The 64 values
-// f_i / 2pi come from the host in fp64.
+// radians, reduced in fp64 as a fraction of a turn (norm_rope.hpp); the 64
+// values f_i / 2pi come from the host in fp64.  The norm and rotation are the
+// same device code the fused decode step uses, so both give identical bits.
 #include <math.h>
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "norm_rope.hpp"
 
 namespace pgqa {
 namespace {
@@ -56,10 +56,8 @@ __global__ __launch_bounds__(1024) void cache_write_kernel(PoolGeom pool, WriteA
     }
   }
   if (tid < 64) {
-    const double turns = double(pos) * a.rev_freq[tid];
-    const float ang = float((turns - floor(turns)) * 6.283185307179586);
-    float sn, cs;
-    sincosf(ang, &sn, &cs);
+    float cs, sn;
+    rope_angle(pos, a.rev_freq[tid], cs, sn);
     s_cos[tid] = cs;
     s_sin[tid] = sn;
   }
@@ -95,41 +93,14 @@ __global__ __launch_bounds__(1024) void cache_write_kernel(PoolGeom pool, WriteA
     return;
   }
 
-  float y0[8], y1[8];
-  const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
-  float ss = 0.f;
+  float cs[8], sn[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    y0[2 * e] = bf16_lo(a0[e]);
-    y0[2 * e + 1] = bf16_hi(a0[e]);
-    y1[2 * e] = bf16_lo(a1[e]);
-    y1[2 * e + 1] = bf16_hi(a1[e]);
+  for (int j = 0; j < 8; ++j) {
+    cs[j] = s_cos[8 * s + j];
+    sn[j] = s_sin[8 * s + j];
   }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ss += y0[e] * y0[e] + y1[e] * y1[e];
-  const float ms = sum8(ss) * (1.0f / kHeadDim);
-  const float inv = 1.0f / sqrtf(ms + a.eps);
-  const uint32_t g0[4] = {w0.x, w0.y, w0.z, w0.w}, g1[4] = {w1.x, w1.y, w1.z, w1.w};
-  uint32_t o0[4], o1[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    float r0[2], r1[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = 8 * s + 2 * e + u;  // rotary pair (i, i + 64)
-      const float wa = u ? bf16_hi(g0[e]) : bf16_lo(g0[e]);
-      const float wb = u ? bf16_hi(g1[e]) : bf16_lo(g1[e]);
-      const float ya = y0[2 * e + u] * inv * wa;
-      const float yb = y1[2 * e + u] * inv * wb;
-      const float cs = s_cos[i], sn = s_sin[i];
-      r0[u] = ya * cs - yb * sn;
-      r1[u] = yb * cs + ya * sn;
-    }
-    o0[e] = pack_bf16x2(r0[0], r0[1]);
-    o1[e] = pack_bf16x2(r1[0], r1[1]);
-  }
-  const uint4 out0 = make_uint4(o0[0], o0[1], o0[2], o0[3]);
-  const uint4 out1 = make_uint4(o1[0], o1[1], o1[2], o1[3]);
+  uint4 out0, out1;
+  norm_rope_lane(x0, x1, w0, w1, cs, sn, a.eps, out0, out1);
   if (is_q) {
     uint16_t* dst = a.q_out + (int64_t(t) * hq + h) * kHeadDim;
     *reinterpret_cast<uint4*>(dst + 8 * s) = out0;

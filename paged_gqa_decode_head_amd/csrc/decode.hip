@@ -42,6 +42,7 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "norm_rope.hpp"
 
 namespace pgqa {
 namespace {
@@ -65,8 +66,8 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int R, int W, bool kStream>
-__global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a) {
+template <int R, int W, bool kStream, bool kFused>
+__global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a, StepArgs st) {
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 3, sub = lane & 7, khalf = lane & 1;
@@ -75,6 +76,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   __shared__ __align__(16) uint32_t s_p[W][R][8];
   __shared__ float s_m[W][R], s_l[W][R];
   __shared__ __align__(16) float s_acc[W][R][kHeadDim];
+  __shared__ __align__(16) uint16_t s_newk[kFused ? kHeadDim : 1];  // fused step: the new token's k and v
+  __shared__ __align__(16) uint16_t s_newv[kFused ? kHeadDim : 1];
 
   // Issue the context length, this wave's block ids and q together: lane i
   // fetches the block id of the wave's i-th tile (tile wave + i*W of the
@@ -92,11 +95,28 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   uint32_t qv[R][8];
 #pragma unroll
   for (int h = 0; h < R; ++h) {
-    const uint16_t* qrow = a.q + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 8;
+    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + h) * kHeadDim + sub * 8;
     const uint4 x = *reinterpret_cast<const uint4*>(qrow);
     const uint4 y = *reinterpret_cast<const uint4*>(qrow + 64);
     qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
     qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
+  }
+
+  // Fused step: lanes 0..7 of every wave fetch the new token's raw k, v and the
+  // k norm weight now, before the context length is known (one of these waves
+  // will write the token; see below).
+  uint4 nk0, nk1, nv0, nv1, nw0, nw1;
+  if constexpr (kFused) {
+    if (lane < 8) {
+      const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
+      const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
+      nk0 = *reinterpret_cast<const uint4*>(kr);
+      nk1 = *reinterpret_cast<const uint4*>(kr + 64);
+      nv0 = *reinterpret_cast<const uint4*>(vr);
+      nv1 = *reinterpret_cast<const uint4*>(vr + 64);
+      nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
+      nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
+    }
   }
 
   const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;
@@ -111,6 +131,79 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (sp >= ns) return;
   const int k1 = min(n, k0 + a.split_tokens);
+
+  // Fused step: the new token sits at position n - 1.  Every workgroup norms and
+  // rotates its own q rows (the same device code as the cache-write kernel, so
+  // identical bits).  In the workgroup whose split holds key n - 1, the wave
+  // that computes the last tile norms and rotates the token's k and keeps it
+  // and v in LDS for its own use when it reaches that tile; it stores them into
+  // the cache slot only after its tile loop, so the stores hold up no tile
+  // load (the slot is read again only after this kernel).
+  const int patch_tile = kFused && sp == ns - 1 ? (n - 1 - k0) >> 4 : -1;
+  const bool writer = kFused && patch_tile >= 0 && wave == patch_tile % W;
+  auto fused_prologue = [&]() {
+    if constexpr (kFused) {
+      float cs[8], sn[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rope_angle(n - 1, st.rev_freq[8 * sub + j], cs[j], sn[j]);
+      const uint4 w0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
+      const uint4 w1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        uint4 o0, o1;
+        norm_rope_lane(make_uint4(qv[h][0], qv[h][1], qv[h][2], qv[h][3]),
+                       make_uint4(qv[h][4], qv[h][5], qv[h][6], qv[h][7]), w0, w1, cs, sn, st.eps, o0, o1);
+        qv[h][0] = o0.x; qv[h][1] = o0.y; qv[h][2] = o0.z; qv[h][3] = o0.w;
+        qv[h][4] = o1.x; qv[h][5] = o1.y; qv[h][6] = o1.z; qv[h][7] = o1.w;
+        if (st.q_out != nullptr && sp == 0 && tid < 8) {
+          uint16_t* dst = st.q_out + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 8;
+          *reinterpret_cast<uint4*>(dst) = o0;
+          *reinterpret_cast<uint4*>(dst + 64) = o1;
+        }
+      }
+      if (writer) {
+        if (lane < 8) {
+          uint4 o0, o1;
+          norm_rope_lane(nk0, nk1, nw0, nw1, cs, sn, st.eps, o0, o1);
+          *reinterpret_cast<uint4*>(&s_newk[8 * sub]) = o0;
+          *reinterpret_cast<uint4*>(&s_newk[64 + 8 * sub]) = o1;
+          *reinterpret_cast<uint4*>(&s_newv[8 * sub]) = nv0;
+          *reinterpret_cast<uint4*>(&s_newv[64 + 8 * sub]) = nv1;
+        }
+        // the wave's own LDS rows are read back in compute(): order them
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+  };
+  // The slot write of the new token, from the LDS rows, after the tile loop.
+  auto fused_epilogue = [&]() {
+    if constexpr (kFused) {
+      if (writer) {
+        // block id of the token's slot: this wave's tile patch_tile / W
+        const int32_t blk = __builtin_amdgcn_readlane(lane_blk, patch_tile / W);
+        if (lane < 8) {
+          if (unsigned(blk) < unsigned(pool.num_blocks)) {
+            const int off = (n - 1) & (bs - 1);
+            uint16_t* tile = pool.kv + (int64_t(blk) * hkv + g) * tile_elems(pool);
+            *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + sub * 8) =
+                *reinterpret_cast<const uint4*>(&s_newk[8 * sub]);
+            *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + 64 + sub * 8) =
+                *reinterpret_cast<const uint4*>(&s_newk[64 + 8 * sub]);
+            uint16_t* vt = tile + int64_t(bs) * kHeadDim + off;  // V^T[dim][slot]
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              vt[int64_t(8 * sub + e) * bs] = s_newv[8 * sub + e];
+              vt[int64_t(64 + 8 * sub + e) * bs] = s_newv[64 + 8 * sub + e];
+            }
+          } else if (sub == 0) {
+            raise_error(pool.err, kErrBlockId);
+          }
+        }
+      }
+    }
+  };
 
   const int64_t tstride = tile_elems(pool);
   const int64_t bstride = tstride * hkv;
@@ -166,8 +259,49 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     }
   };
 
+  // Fused step: the new key (tile offset o of the last tile) taken from LDS.
+  // K: the 8-lane group o/2 holds it (k[0..1] for even o, k[2..3] for odd).
+  // V: lanes with (lane & 1) == o/8 hold keys 8(lane&1).. of dims 32j + lane/2;
+  // key o is the low or high half of pair (o%8)/2.
+  auto patch = [&](Tile& tb) {
+    const int o = (n - 1 - k0) & 15;
+    {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(&s_newk[8 * sub]);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(&s_newk[64 + 8 * sub]);
+      const bool ke = grp == (o >> 1) && !(o & 1), ko = grp == (o >> 1) && (o & 1);
+      auto sel = [](bool c, const uint4& a, const uint4& b) {
+        return make_uint4(c ? a.x : b.x, c ? a.y : b.y, c ? a.z : b.z, c ? a.w : b.w);
+      };
+      tb.k[0] = sel(ke, x0, tb.k[0]);
+      tb.k[1] = sel(ke, x1, tb.k[1]);
+      tb.k[2] = sel(ko, x0, tb.k[2]);
+      tb.k[3] = sel(ko, x1, tb.k[3]);
+    }
+    // Selects only, no runtime component index (that would put the tile in scratch).
+    const bool mine = khalf == (o >> 3);
+    const int t = (o & 7) >> 1;
+    const uint32_t keep = (o & 1) ? 0x0000ffffu : 0xffff0000u;
+    const int shift = (o & 1) ? 16 : 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t nv = uint32_t(s_newv[32 * j + (lane >> 1)]) << shift;
+      tb.v[j].x = mine && t == 0 ? (tb.v[j].x & keep) | nv : tb.v[j].x;
+      tb.v[j].y = mine && t == 1 ? (tb.v[j].y & keep) | nv : tb.v[j].y;
+      tb.v[j].z = mine && t == 2 ? (tb.v[j].z & keep) | nv : tb.v[j].z;
+      tb.v[j].w = mine && t == 3 ? (tb.v[j].w & keep) | nv : tb.v[j].w;
+    }
+  };
+
   bool bad_blk = false;
   auto compute = [&](Tile& tb, int tt) {
+    if constexpr (kFused) {
+      if (tt == patch_tile) {
+        // an opaque statement keeps this a branch: the patch must not be
+        // turned into selects executed on every tile
+        asm volatile("");
+        patch(tb);
+      }
+    }
     bad_blk |= !tb.ok;
     if (!tb.ok || k0 + tt * 16 + 16 > k1) mask_v(tb, tt);
     const int key = k0 + tt * 16 + 2 * grp;
@@ -242,6 +376,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     auto at = [&](int i) { return min(i, my_tiles - 1); };
     Tile ta, tb;
     load(ta, 0);
+    fused_prologue();  // fused step: while the first tile is in flight
     for (int i = 0; i < my_tiles; i += 2) {
       load(tb, at(i + 1));
       compute(ta, wave + i * W);
@@ -249,6 +384,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
       if (i + 1 < my_tiles) compute(tb, wave + (i + 1) * W);
     }
   }
+  fused_epilogue();
   if (bad_blk && lane == 0) raise_error(pool.err, kErrBlockId);
 
   // Wave totals: each 8-lane group summed the weights of its own keys; each
@@ -339,9 +475,13 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
 }
 
 template <int R, int W, bool kStream>
-hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
   const dim3 grid(a.max_splits, pool.num_kv_heads, a.batch);
-  hipLaunchKernelGGL((decode_kernel<R, W, kStream>), grid, dim3(64 * W), 0, stream, pool, a);
+  if (st != nullptr) {
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a, StepArgs{});
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.num_q_heads, a.batch), dim3(kHeadDim), 0, stream, pool, a);
@@ -349,18 +489,18 @@ hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, hipStream_t str
 }
 
 template <int R, int W>
-hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
-  if (a.stream_loads) return launch_rws<R, W, true>(pool, a, stream);
-  return launch_rws<R, W, false>(pool, a, stream);
+hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+  if (a.stream_loads) return launch_rws<R, W, true>(pool, a, st, stream);
+  return launch_rws<R, W, false>(pool, a, st, stream);
 }
 
 template <int R>
-hipError_t launch_r(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_r(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
   switch (a.waves) {
-    case 1: return launch_rw<R, 1>(pool, a, stream);
-    case 2: return launch_rw<R, 2>(pool, a, stream);
-    case 4: return launch_rw<R, 4>(pool, a, stream);
-    case 8: return launch_rw<R, 8>(pool, a, stream);
+    case 1: return launch_rw<R, 1>(pool, a, st, stream);
+    case 2: return launch_rw<R, 2>(pool, a, st, stream);
+    case 4: return launch_rw<R, 4>(pool, a, st, stream);
+    case 8: return launch_rw<R, 8>(pool, a, st, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -381,14 +521,14 @@ DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int
   return w;
 }
 
-hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   if (a.split_tokens > kMaxTilesPerWave * 16 * a.waves) return hipErrorInvalidValue;
   switch (a.num_q_heads / pool.num_kv_heads) {
-    case 1: return launch_r<1>(pool, a, stream);
-    case 2: return launch_r<2>(pool, a, stream);
-    case 4: return launch_r<4>(pool, a, stream);
-    case 8: return launch_r<8>(pool, a, stream);
+    case 1: return launch_r<1>(pool, a, st, stream);
+    case 2: return launch_r<2>(pool, a, st, stream);
+    case 4: return launch_r<4>(pool, a, st, stream);
+    case 8: return launch_r<8>(pool, a, st, stream);
     default: return hipErrorInvalidValue;
   }
 }

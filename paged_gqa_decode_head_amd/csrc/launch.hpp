@@ -35,7 +35,7 @@ struct WriteArgs {
 hipError_t launch_cache_write(const PoolGeom& pool, const WriteArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
-  const uint16_t* q;
+  const uint16_t* q; int64_t q_stride;  // q row stride per sequence, elements
   const int32_t* ctx;
   const int32_t* bt; int32_t bt_stride;
   int32_t batch; int32_t num_q_heads; int32_t max_ctx;
@@ -47,7 +47,20 @@ struct DecodeArgs {
   uint16_t* out;
 };
 
-hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream);
+// The fused decode step (norm + rotary of the new token's q and k, its cache
+// write, and decode attention in one launch): raw rows of the one new token of
+// each sequence, at position context_len - 1.
+struct StepArgs {
+  const uint16_t* k; int64_t k_stride;
+  const uint16_t* v; int64_t v_stride;
+  const uint16_t* wq; const uint16_t* wk;
+  float eps;
+  uint16_t* q_out;       // optional: the normed, rotated q (bf16 [batch][Hq][128])
+  double rev_freq[64];   // theta^(-2i/128) / (2 pi): turns per position of rotary pair i
+};
+
+// st == nullptr: plain decode attention over q as given.
+hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream);
 
 // Workspace carve-up shared by the host API and the launchers.
 struct DecodeWorkspace {
