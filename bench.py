@@ -14,7 +14,11 @@ Consecutive steps use different layers' caches (``--layers`` pools of the same
 shape, cycled), as a model's decode step does, so a layer's K/V has been
 evicted from the 256 MB Infinity Cache before it is read again.
 
-Prints ONE JSON line.  value = algorithmic bytes of the step / step time.
+Prints ONE JSON line.  value = algorithmic bytes of the step / wall-clock step
+time of the timed region (synchronised on both sides).  roofline.achieved
+divides the same bytes by the kernel's average launch duration: one HIP event
+pair on the launch stream around the timed region, over the number of steps
+(back-to-back launches, so the launch gaps are included).
 """
 from __future__ import annotations
 
@@ -520,42 +524,45 @@ def main():
     two = [(pg.bind_cache_write(p, q, k, v, wq, wk, pos, seq, bt, s.eps, s.rope_theta, q_out),
             pg.bind_decode(p, q_out, ctx, bt, max_ctx, scale, out, plan=plan, workspace=ws)) for p in pools]
 
-    def timed(issue, marks):
-        """Run warmup + steps; returns (wall ms per step, [per-step event lists])."""
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(marks)] for _ in range(args.steps)]
+    def timed(issue):
+        """Warmup, then exactly args.steps steps between two synchronisations,
+        with one HIP event pair on the launch stream bracketing the region.
+        Returns (wall ms per step, event ms per step)."""
         for i in range(args.warmup):
-            issue(i, None)
+            issue(i)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        e0.record()
         for i in range(args.steps):
-            issue(i, ev[i])
+            issue(i)
+        e1.record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / args.steps, ev
+        return (time.perf_counter() - t0) * 1e3 / args.steps, e0.elapsed_time(e1) / args.steps
 
-    def issue_fused(i, e):
-        if e:
-            e[0].record()
+    def issue_fused(i):
         fused[i % args.layers]()
-        if e:
-            e[1].record()
 
-    def issue_two(i, e):
+    def issue_two(i):
         wr, dc = two[i % args.layers]
-        if e:
-            e[0].record()
         wr()
-        if e:
-            e[1].record()
         dc()
-        if e:
-            e[2].record()
 
-    ms_two, ev_two = timed(issue_two, 3)
-    ms_step, ev = timed(issue_fused, 2)
+    ms_two, _ = timed(issue_two)
+    ms_step, step_ms = timed(issue_fused)
+    # the two-call step's split between its launches: events around each call, in a loop of its own
+    ev_two = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i, e in enumerate(ev_two):
+        wr, dc = two[i % args.layers]
+        e[0].record()
+        wr()
+        e[1].record()
+        dc()
+        e[2].record()
+    torch.cuda.synchronize()
     for p in pools:
         assert p.check_errors() == 0
 
-    step_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
     write_ms = sum(e[0].elapsed_time(e[1]) for e in ev_two) / args.steps
     decode_ms = sum(e[1].elapsed_time(e[2]) for e in ev_two) / args.steps
     dec_bytes = decode_alg_bytes(w)
