@@ -88,13 +88,17 @@ pgqa_status pgqa_pool_destroy(pgqa_pool* pool);
 
 /*
  * Element strides (and element offsets from kv_storage) of the logical views
- * K[num_blocks][block_size][num_kv_heads][head_dim] and the same for V, so that
- * a caller can build strided views of the cache.  Within one (block, kv head)
- * the library stores K row-major [slot][dim] followed by V transposed
- * [dim][slot]; strides are ordered (block, slot, head, dim).
+ * K[num_blocks][block_size][num_kv_heads][head_dim] (k_strides ordered block,
+ * slot, head, dim) and V[num_blocks][block_size / 16][16][num_kv_heads][head_dim]
+ * (v_strides ordered block, slot / 16, slot % 16, head, dim: slot = 16 * piece
+ * + j), so that a caller can build strided views of the cache.  Within one
+ * (block, kv head) the library stores K row-major [slot][dim] followed by V
+ * transposed in 16-slot pieces [slot / 16][dim][slot % 16], so that 16
+ * consecutive keys of one dim are 32 contiguous bytes and the V of 16
+ * consecutive keys is one contiguous 4 KiB run at every block size.
  */
 pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_t* k_offset,
-                             int64_t v_strides[4], int64_t* v_offset);
+                             int64_t v_strides[5], int64_t* v_offset);
 
 /*
  * Synchronise `stream`, read and clear the pool's sticky device error word.
@@ -152,8 +156,7 @@ typedef struct {
   int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64), <= 1024 * waves_per_split */
   int32_t max_splits;       /* ceil(max_context_len / split_tokens) */
   int32_t waves_per_split;  /* 64-lane waves per workgroup: 1, 2, 4 or 8 */
-  int32_t load_hint;        /* K/V loads: 0 library default (streaming up to 32-token blocks, cached above),
-                               1 cached, 2 streaming (non-temporal) */
+  int32_t load_hint;        /* K/V loads: 0 library default (streaming), 1 cached, 2 streaming (non-temporal) */
 } pgqa_decode_plan;
 
 /* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,

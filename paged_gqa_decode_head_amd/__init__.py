@@ -186,7 +186,7 @@ class Pool:
         self.handle = h
         self.num_blocks, self.block_size, self.num_kv_heads = num_blocks, block_size, num_kv_heads
         self.head_dim = head_dim
-        ks, vs = (_I64 * 4)(), (_I64 * 4)()
+        ks, vs = (_I64 * 4)(), (_I64 * 5)()
         ko, vo = _I64(), _I64()
         _check(lib().pgqa_pool_layout(self.handle, ks, ctypes.byref(ko), vs, ctypes.byref(vo)))
         self.k_strides, self.k_offset = tuple(ks), ko.value
@@ -199,7 +199,9 @@ class Pool:
         return self.storage.as_strided(shape, self.k_strides, self.k_offset)
 
     def v_view(self):
-        shape = (self.num_blocks, self.block_size, self.num_kv_heads, self.head_dim)
+        """V cache as a strided bf16 view [num_blocks, block_size / 16, 16, num_kv_heads, head_dim]
+        (the slot index split as slot = 16 * piece + j; reshape a copy to get [.., block_size, ..])."""
+        shape = (self.num_blocks, self.block_size // 16, 16, self.num_kv_heads, self.head_dim)
         return self.storage.as_strided(shape, self.v_strides, self.v_offset)
 
     def fill_logical(self, k, v, blocks=None):
@@ -214,13 +216,14 @@ class Pool:
             return x.to(self.device)
 
         kv, vv = self.k_view(), self.v_view()
+        pieces = lambda x: x.reshape(x.shape[0], self.block_size // 16, 16, *x.shape[2:])
         if blocks is None:
             kv.copy_(as_bf16(k))
-            vv.copy_(as_bf16(v))
+            vv.copy_(pieces(as_bf16(v)))
         else:
             idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
             kv[idx] = as_bf16(k)
-            vv[idx] = as_bf16(v)
+            vv[idx] = pieces(as_bf16(v))
 
     def read_logical(self, blocks=None):
         """(K, V) as CPU int16 bit patterns [n, block_size, Hkv, 128] in logical order."""
@@ -230,7 +233,8 @@ class Pool:
         if blocks is not None:
             idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
             kv, vv = kv[idx], vv[idx]
-        return (kv.contiguous().view(torch.int16).cpu(), vv.contiguous().view(torch.int16).cpu())
+        vv = vv.contiguous().reshape(vv.shape[0], self.block_size, *vv.shape[3:])
+        return (kv.contiguous().view(torch.int16).cpu(), vv.view(torch.int16).cpu())
 
     def check_errors(self, stream=None) -> int:
         """Synchronise the stream and return (and clear) the device error bits."""

@@ -92,13 +92,9 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 constexpr int32_t kMaxSplitTokens = 4096;
 constexpr int32_t kChunkStep = 32;  // chunk splits are whole 32-key steps
-// Non-temporal K/V loads by default (K/V bytes are read once per launch).
-// Default K/V load kind of decode: non-temporal (streaming) up to 32-token
-// blocks, where each tile load covers whole 128-byte lines of the V^T rows;
-// cached above, where a 16-key tile reads a quarter of each line and the other
-// quarters, read by other waves, then come from L2 (measured: 85 vs 99 us on
-// the batch-64 step at 64-token blocks).
-constexpr int32_t kStreamMaxBlockSize = 32;
+// Decode K/V loads are non-temporal (streaming) by default: K/V bytes are read
+// once per launch, and V^T is stored in 16-slot pieces, so every 16-key tile
+// load covers whole 128-byte lines at every block size.
 
 pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t max_context_len) {
   const int32_t gran = block_size > 64 ? block_size : 64;
@@ -211,7 +207,7 @@ pgqa_status pgqa_pool_destroy(pgqa_pool* pool) {
   return PGQA_OK;
 }
 
-pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_t* k_offset, int64_t v_strides[4],
+pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_t* k_offset, int64_t v_strides[5],
                              int64_t* v_offset) {
   if (pool == nullptr || k_strides == nullptr || k_offset == nullptr || v_strides == nullptr || v_offset == nullptr)
     return fail(PGQA_ERR_INVALID_ARG, "NULL argument");
@@ -223,10 +219,12 @@ pgqa_status pgqa_pool_layout(const pgqa_pool* pool, int64_t k_strides[4], int64_
   k_strides[2] = tile;
   k_strides[3] = 1;
   *k_offset = 0;
+  // order (block, slot / 16, slot % 16, head, dim): V^T in 16-slot pieces
   v_strides[0] = tile * hkv;
-  v_strides[1] = 1;
-  v_strides[2] = tile;
-  v_strides[3] = bs;
+  v_strides[1] = 16 * D;
+  v_strides[2] = 1;
+  v_strides[3] = tile;
+  v_strides[4] = 16;
   *v_offset = bs * D;
   return PGQA_OK;
 }
@@ -418,7 +416,7 @@ pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, 
   a.split_tokens = p.split_tokens;
   a.max_splits = p.max_splits;
   a.waves = p.waves_per_split;
-  a.stream_loads = p.load_hint == 2 || (p.load_hint == 0 && pool->cfg.block_size <= kStreamMaxBlockSize);
+  a.stream_loads = p.load_hint != 1;
   char* ws = wl.total > 0 ? static_cast<char*>(workspace) : nullptr;
   a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;

@@ -80,15 +80,15 @@ __global__ __launch_bounds__(1024) void cache_write_kernel(PoolGeom pool, WriteA
   uint16_t* kv_tile = pool.kv + (int64_t(blk) * hkv + h) * tile_elems(pool);
   if (!is_q && !is_k) {
     if (bad) return;
-    // v goes into the cache as it came, transposed: V^T[dim][slot].
-    uint16_t* dst = kv_tile + int64_t(bs) * kHeadDim + off;
+    // v goes into the cache as it came, transposed: V^T piece [dim][slot % 16].
+    uint16_t* dst = kv_tile + v_elem(bs, off, 0);
     const uint32_t lo[4] = {x0.x, x0.y, x0.z, x0.w}, hi[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dst[int64_t(8 * s + 2 * e) * bs] = uint16_t(lo[e]);
-      dst[int64_t(8 * s + 2 * e + 1) * bs] = uint16_t(lo[e] >> 16);
-      dst[int64_t(64 + 8 * s + 2 * e) * bs] = uint16_t(hi[e]);
-      dst[int64_t(64 + 8 * s + 2 * e + 1) * bs] = uint16_t(hi[e] >> 16);
+      dst[(8 * s + 2 * e) * kVSub] = uint16_t(lo[e]);
+      dst[(8 * s + 2 * e + 1) * kVSub] = uint16_t(lo[e] >> 16);
+      dst[(64 + 8 * s + 2 * e) * kVSub] = uint16_t(hi[e]);
+      dst[(64 + 8 * s + 2 * e + 1) * kVSub] = uint16_t(hi[e] >> 16);
     }
     return;
   }

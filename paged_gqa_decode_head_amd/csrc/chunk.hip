@@ -37,8 +37,9 @@
 //     key 16(i/8) + 8(l/32) + i%8, so the 8 weights a lane needs as its PV
 //     operand for keys 16s + 8(l/32) .. +7 are its own D[8s .. 8s+7].
 //   * O^T += V^T P^T (M = dims, N = query rows, K = keys): the cache keeps V
-//     transposed per block, so a lane's 8 keys of one dim are 16 contiguous
-//     bytes, in the cache and in LDS.  Nothing is transposed at run time.
+//     transposed in 16-slot pieces, so a lane's 8 keys of one dim are 16
+//     contiguous bytes, in the cache and in LDS.  Nothing is transposed at run
+//     time.
 //   * dims of the S product are split between the lane halves as
 //     (l/32)*64 + 8*kstep + j: a lane reads 128 contiguous bytes of its q row.
 //   * LDS rows are padded (K: 272 bytes, V^T: 80 bytes) so that the 16 lanes
@@ -397,8 +398,8 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
 
   // Staging roles per step: K key kkey, 16-byte chunks kch and kch + 8 (each
   // wave instruction reads 8 whole half rows); V^T entries idx = tid + 256u for
-  // u = 0, 1: dim idx / 4, keys 8 (idx % 4) .. +7 (whole lines for bs <= 32).
-  // A (block, head) tile holds bs << 8 bf16, V^T starting at bs << 7.
+  // u = 0, 1: dim idx / 4, keys 8 (idx % 4) .. +7 (two 16-slot pieces of 16 dims
+  // each: whole lines).  A (block, head) tile holds bs << 8 bf16.
   const int tshift = lbs + 8;
   const int kkey = tid >> 3, kch = tid & 7;
   struct Stage {
@@ -417,8 +418,7 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + kWideThreads * u;
       const int kv = min(key0 + 8 * (idx & 3), k1 - 1) & ~7;
-      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + (bs << 7) + (idx >> 2) * bs +
-                     (kv & (bs - 1)));
+      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), idx >> 2));
     }
   };
   auto store = [&](Stage& st, int step, int buf) {
@@ -556,8 +556,7 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
     for (int u = 0; u < 8; ++u) {
       const int dt = u >> 1, s16 = u & 1;
       const int kv = min(key0 + 16 * s16 + 8 * half, k1 - 1) & ~7;
-      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + (bs << 7) + (32 * dt + col) * bs +
-                     (kv & (bs - 1)));
+      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), 32 * dt + col));
     }
   };
 

@@ -23,9 +23,10 @@
 //     wave-wide ballot detects; otherwise no max reduction and no rescale is
 //     done.  The weights exp2(s - m) (at most 2^kTau) are packed to bf16 pairs
 //     and broadcast through LDS.
-//   * values: the cache stores each V tile transposed, [dim][slot], so lane l
-//     reads dims 32j + l/2 (j = 0..3) for keys 8(l&1)..8(l&1)+7: consecutive
-//     lanes read consecutive 16-byte pieces of the 4 KiB tile (block size 16).
+//   * values: the cache stores V transposed in 16-slot pieces, [dim][slot % 16],
+//     so lane l reads dims 32j + l/2 (j = 0..3) for keys 8(l&1)..8(l&1)+7:
+//     consecutive lanes read consecutive 16-byte pieces of the tile's 4 KiB
+//     piece, at every block size.
 //     The weighted sum over key pairs is again v_dot2_f32_bf16; the two key
 //     halves of a dim meet once, at the end of the split.
 //   * the next tile is loaded while the current one is computed (two register
@@ -191,11 +192,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
                 *reinterpret_cast<const uint4*>(&s_newk[8 * sub]);
             *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + 64 + sub * 8) =
                 *reinterpret_cast<const uint4*>(&s_newk[64 + 8 * sub]);
-            uint16_t* vt = tile + int64_t(bs) * kHeadDim + off;  // V^T[dim][slot]
+            uint16_t* vt = tile + v_elem(bs, off, 0);  // V^T piece [dim][slot % 16]
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              vt[int64_t(8 * sub + e) * bs] = s_newv[8 * sub + e];
-              vt[int64_t(64 + 8 * sub + e) * bs] = s_newv[64 + 8 * sub + e];
+              vt[(8 * sub + e) * kVSub] = s_newv[8 * sub + e];
+              vt[(64 + 8 * sub + e) * kVSub] = s_newv[64 + 8 * sub + e];
             }
           } else if (sub == 0) {
             raise_error(pool.err, kErrBlockId);
@@ -233,9 +234,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     tb.k[1] = ld16<kStream>(kp + 64);
     tb.k[2] = ld16<kStream>(kp + kHeadDim);
     tb.k[3] = ld16<kStream>(kp + kHeadDim + 64);
-    const uint16_t* vp = base + int64_t(bs) * kHeadDim + int64_t(lane >> 1) * bs + sub16 * 16 + khalf * 8;
+    const uint16_t* vp = base + v_elem(bs, sub16 * 16 + khalf * 8, lane >> 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tb.v[j] = ld16<kStream>(vp + int64_t(32 * j) * bs);
+    for (int j = 0; j < 4; ++j) tb.v[j] = ld16<kStream>(vp + 32 * j * kVSub);
   };
 
   // Zero the V entries of keys that are not attended (past the split end, or

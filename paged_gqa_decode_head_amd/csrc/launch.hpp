@@ -19,6 +19,14 @@ struct PoolGeom {
 
 __host__ __device__ inline int64_t tile_elems(const PoolGeom& p) { return 2ll * p.block_size * 128; }
 
+// Inside one (block, kv head) tile: K row-major [slot][128], then V transposed
+// in 16-slot pieces [slot / 16][128][16], so that 16 consecutive keys of V^T are
+// one contiguous 4 KiB run (whole 128-byte lines) at every block size.
+constexpr int kVSub = 16;  // slots per V^T piece
+__host__ __device__ inline int64_t v_elem(int bs, int slot, int dim) {
+  return (int64_t(bs) << 7) + (int64_t(slot >> 4) << 11) + dim * kVSub + (slot & (kVSub - 1));
+}
+
 struct WriteArgs {
   const uint16_t* q; int64_t q_stride;
   const uint16_t* k; int64_t k_stride;
