@@ -418,7 +418,7 @@ def recorded_traffic():
     try:
         rec = json.load(open(path))
         src = b"".join(open(os.path.join(ROOT, "paged_gqa_decode_head_amd", "csrc", f), "rb").read()
-                       for f in ("decode.hip", "device_common.hpp", "norm_rope.hpp"))
+                       for f in ("decode.hip", "device_common.hpp", "norm_rope.hpp", "launch.hpp"))
     except OSError:
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("kernel_source_sha256"):
