@@ -94,7 +94,7 @@ def time_calls(calls, iters, warmup=3):
     return ts[len(ts) // 2], sum(ts) / len(ts)
 
 
-def measure_rows(args, dev):
+def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
     """Every hot-path row on its own synthetic workload: decode on each decode
     workload, chunk attention (slice, verify rows, both) on the mixed step."""
     import numpy as np
@@ -108,7 +108,7 @@ def measure_rows(args, dev):
     scale = 1.0 / math.sqrt(128)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     rows = {"decode": {}, "cache_write": {}}
-    for name in ("cfg2", "cfg3a", "cfg4", "cfg5"):
+    for name in names:
         w = make_step(SPECS[name])
         s = w.spec
         pools = []
@@ -426,6 +426,52 @@ def recorded_traffic():
     return rec["traffic_bytes_per_launch"]
 
 
+def percentiles(us):
+    """median, p10 and p90 of a list of per-launch times (µs)."""
+    import numpy as np
+
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 3), "p10": round(float(np.percentile(a, 10)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3)}
+
+
+def per_launch_us(call, n, cycle=1):
+    """Event pair around each of n launches (after a short warm-up); returns the µs list."""
+    import torch
+
+    for i in range(5):
+        call(i % cycle)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        call(i % cycle)
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in ev]
+
+
+def stream_read_ceiling(dev, nbytes: int, copies: int = 4):
+    """The library's plain streaming-read kernel over nbytes, cycling `copies`
+    buffers (so reads come from HBM, not the 256 MB Infinity Cache): the
+    achievable read rate of one launch of this size."""
+    import torch
+    import paged_gqa_decode_head_amd as pg
+
+    nbytes = nbytes // 16 * 16
+    bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device=dev) for _ in range(copies)]
+    grid = 3 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    calls = [pg.bind_stream_read(b, sink, grid) for b in bufs]
+    us = per_launch_us(lambda i: calls[i](), 40, copies)
+    pct = percentiles(us)
+    del bufs, calls
+    torch.cuda.empty_cache()
+    return {"kernel": "pgqa_stream_read (16-byte non-temporal loads, grid-stride, 3 workgroups per CU)",
+            "bytes": nbytes, "us": pct, "gbs": round(nbytes / pct["median"] / 1e3, 1),
+            "frac_hbm_peak": round(nbytes / pct["median"] / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, seconds: float):
     """The fp64 reference decode, timed on the host on a bounded sample of sequences."""
     import numpy as np
@@ -440,23 +486,38 @@ def cpu_baseline(w, seconds: float):
     s = w.spec
     scale = 1.0 / math.sqrt(128)
     q = O.bf16_bits_to_f64(w.tok_q[w.dec_tok])
-    done, t0 = 0, time.perf_counter()
-    nbytes = 0
-    while True:
-        b = done % w.num_decode
-        O.decode_attention(q[b:b + 1], w.prefix_k, w.prefix_v, w.dec_block_tables[b:b + 1], w.dec_ctx[b:b + 1],
-                           scale)
-        n = int(w.dec_ctx[b])
-        nbytes += n * s.num_kv_heads * 128 * 4 + 2 * s.num_q_heads * 128 * 2 + 4 * (-(-n // s.block_size)) + 4
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def run(limit):
+        done, t0 = 0, time.perf_counter()
+        nbytes = 0
+        while True:
+            b = done % w.num_decode
+            O.decode_attention(q[b:b + 1], w.prefix_k, w.prefix_v, w.dec_block_tables[b:b + 1],
+                               w.dec_ctx[b:b + 1], scale)
+            n = int(w.dec_ctx[b])
+            nbytes += n * s.num_kv_heads * 128 * 4 + 2 * s.num_q_heads * 128 * 2 + 4 * (-(-n // s.block_size)) + 4
+            done += 1
+            el = time.perf_counter() - t0
+            if el >= limit:
+                return done, nbytes, el
+
+    done, nbytes, el = run(seconds)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+
+        with threadpool_limits(limits=1):
+            d1, b1, e1 = run(seconds / 2)
+        single = {"value": b1 / e1 / 1e9, "seqs_per_s": d1 / e1, "cores": 1,
+                  "sample": f"{d1} sequences, BLAS limited to 1 thread, {e1:.1f} s wall"}
+    except Exception:
+        pass
     return {
         "value": nbytes / el / 1e9, "unit": "GB/s", "seqs_per_s": done / el, "cores": int(threads),
         "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
         "sample": f"{done} sequences of this step's decode batch (cycled), fp64 numpy reference, "
                   f"{el:.1f} s wall",
+        "single_thread": single,
     }
 
 
@@ -472,6 +533,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-row measurements of the other workloads")
+    ap.add_argument("--only", choices=["chunk"], default=None,
+                    help="profiling aid: run only the mixed workload's rows (chunk attention) and print them")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 256 MiB plain copy (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -488,6 +551,10 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    if args.only == "chunk":
+        # profiling aid: only the mixed workload's rows (its decode, write and chunk calls)
+        print(json.dumps({"rows": measure_rows(args, dev, ("cfg5",))}), flush=True)
+        return
     w = make_step(SPECS[args.workload])
     s = w.spec
     to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -591,6 +658,9 @@ def main():
     d = np.abs(got - ref)
     parity = {"rows": rows, "max_abs": float(d.max()), "mean_rel": float(d.sum() / np.abs(ref).sum())}
 
+    launch_dist = percentiles(per_launch_us(lambda i: fused[i % args.layers](), args.steps, args.layers))
+    ceiling = stream_read_ceiling(dev, step_bytes) if not args.main_only else None
+
     result = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -623,7 +693,10 @@ def main():
             "frac": round(launch_gbs / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic() if args.workload == "cfg3b" else None,
             "alg_bytes_per_launch": step_bytes, "avg_launch_us": round(step_ms * 1e3, 3),
+            "launch_us_events_each": launch_dist,
+            "frac_of_stream_read": round(launch_gbs / ceiling["gbs"], 4) if ceiling else None,
         },
+        "stream_read_ceiling": ceiling,
         "two_call_step": {
             "calls": "pgqa_rms_norm_rope_cache_write + pgqa_paged_decode_attention",
             "ms_per_step": round(ms_two, 5), "alg_bytes": two_bytes,

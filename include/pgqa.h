@@ -272,8 +272,8 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  *   max_q_len, max_context_len  host hints >= the device values
  *   plan            host, optional (NULL = pgqa_plan_chunk for this device)
  *   workspace       device scratch of >= pgqa_chunk_workspace_bytes(...) bytes for
- *                   the device-built work list and the split partials (no initial
- *                   contents needed)
+ *                   the split partials (no initial contents needed; NULL when that
+ *                   is 0)
  *   out             device bf16 [total_q][num_q_heads][128]
  *
  * Query i of segment s (q_len_s = qsl[s+1] - qsl[s], n_s = context_lens[s]) sits
@@ -281,10 +281,9 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  * segment whose metadata is inconsistent gets zero output rows and sets
  * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  A block id outside the pool sets
  * PGQA_DEVERR_BLOCK_ID; the rows that read it are then unspecified (the key is
- * read as zeros, never out of bounds).  The call enqueues a one-workgroup
- * schedule kernel (it lists the work items the device metadata calls for), the
- * attention kernels for long and short segments and, with more than one split,
- * the combine.
+ * read as zeros, never out of bounds).  The call enqueues the attention kernels
+ * for long and short segments (each workgroup derives its own work item from
+ * the device metadata) and, with more than one split, the combine.
  */
 pgqa_status pgqa_paged_chunk_attention(
     pgqa_pool* pool,
@@ -295,6 +294,22 @@ pgqa_status pgqa_paged_chunk_attention(
     float scale, const pgqa_chunk_plan* plan,
     void* workspace, size_t workspace_bytes,
     void* out, void* stream);
+
+/*
+ * Measurement helper, not part of the attention path: a plain streaming read of
+ * `bytes` bytes at src (device, 16-byte aligned, bytes a multiple of 16) with
+ * 16-byte non-temporal loads in a grid-stride loop, two per thread in flight.
+ * Each of the grid * 256 threads writes the XOR of the 32-bit words it read to
+ * sink (device, >= grid * 256 * 4 bytes = sink_bytes), so the XOR of all sink
+ * words is the XOR of all words of the buffer.  grid: 256-thread workgroups,
+ * 1 .. 65535, or 0 for three per CU of the current device.  Its rate is the
+ * achievable HBM read bandwidth of one launch of that size, the reference for
+ * the decode kernels' bandwidth.  Asynchronous on `stream` (a hipStream_t, NULL
+ * = default stream); no allocation.  PGQA_ERR_INVALID_ARG / POINTER_KIND for bad
+ * arguments.
+ */
+pgqa_status pgqa_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t grid,
+                             void* stream);
 
 /* Static description of a status code. */
 const char* pgqa_status_string(pgqa_status s);

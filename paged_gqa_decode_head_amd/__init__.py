@@ -74,6 +74,7 @@ _P, _I32, _I64, _SZ, _F32, _F64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
                                    ctypes.c_float, ctypes.c_double)
 _SIGNATURES = {
     "pgqa_version": ([], ctypes.c_char_p),
+    "pgqa_stream_read": ([_P, _SZ, _P, _SZ, _I32, _P], ctypes.c_int),
     "pgqa_last_error": ([], ctypes.c_char_p),
     "pgqa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pgqa_pool_bytes": ([ctypes.POINTER(PoolConfig)], _SZ),
@@ -409,6 +410,15 @@ def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_ta
         N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), pp, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
     return out
+
+def bind_stream_read(src, sink, grid: int = 0, stream=None) -> "BoundCall":
+    """pgqa_stream_read over all of ``src`` (a device tensor of a multiple of 16
+    bytes); ``sink`` must hold grid * 256 uint32 words (grid 0: three per CU)."""
+    nbytes = src.numel() * src.element_size()
+    keep = (src, sink)
+    args = (_ptr(src), nbytes, _ptr(sink), sink.numel() * sink.element_size(), int(grid), _stream(stream))
+    return BoundCall(lib().pgqa_stream_read, args, keep)
+
 
 class BoundCall:
     """A C-ABI call with its arguments marshalled once; calling it re-issues the

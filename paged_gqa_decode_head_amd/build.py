@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpgqa.so")
 
-SOURCES = ["errors.cpp", "api.cpp", "sched.cpp", "cache_write.hip", "decode.hip", "chunk.hip"]
+SOURCES = ["errors.cpp", "api.cpp", "sched.cpp", "cache_write.hip", "decode.hip", "chunk.hip", "stream_read.hip"]
 
 ARCH = "gfx950"
 COMMON = [

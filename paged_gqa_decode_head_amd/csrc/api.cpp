@@ -130,6 +130,28 @@ extern "C" {
 
 const char* pgqa_version(void) { return "0.1.0"; }
 
+pgqa_status pgqa_stream_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, int32_t grid,
+                             void* stream) {
+  clear_error();
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PGQA_ERR_HIP, "no current HIP device");
+  if (bytes == 0 || bytes % 16 != 0) return fail(PGQA_ERR_INVALID_ARG, "bytes=%zu (a positive multiple of 16)", bytes);
+  if (grid == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      return fail(PGQA_ERR_HIP, "cannot read the CU count");
+    grid = 3 * cus;
+  }
+  if (grid < 1 || grid > 65535) return fail(PGQA_ERR_INVALID_ARG, "grid=%d", grid);
+  if (sink_bytes < size_t(grid) * 256 * 4)
+    return fail(PGQA_ERR_INVALID_ARG, "sink of %zu bytes, %zu needed", sink_bytes, size_t(grid) * 256 * 4);
+  PGQA_TRY(check_device_ptr(src, dev, "src", 16));
+  PGQA_TRY(check_device_ptr(sink, dev, "sink", 4));
+  const hipError_t e = pgqa::launch_stream_read(src, int64_t(bytes / 16), sink, grid, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PGQA_ERR_HIP, "stream read launch: %s", hipGetErrorString(e));
+  return PGQA_OK;
+}
+
 const char* pgqa_last_error(void) { return pgqa::last_error(); }
 
 const char* pgqa_status_string(pgqa_status s) {

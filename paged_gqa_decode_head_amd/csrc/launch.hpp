@@ -111,6 +111,9 @@ ChunkGrids chunk_grids(int32_t num_segments, int32_t total_q, int32_t num_kv_hea
 
 hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream);
 
+// Plain streaming read of words16 16-byte words (the achievable-bandwidth reference).
+hipError_t launch_stream_read(const void* src, int64_t words16, void* sink, int grid, hipStream_t stream);
+
 struct ChunkWorkspace {
   size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
 };
