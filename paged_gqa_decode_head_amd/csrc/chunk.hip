@@ -356,6 +356,11 @@ __device__ __forceinline__ uint32_t keep2(int key, int klim) {
   return key + 1 < klim ? 0xffffffffu : key < klim ? 0x0000ffffu : 0u;
 }
 
+// Wide-kernel V staging: entry e (0 .. 511) of a 32-key step is 8 keys of one
+// V^T row: dim (e % 8) + 8 (e / 32), keys 8 ((e / 8) % 4) .. +7.
+__device__ __forceinline__ int v_dim(int e) { return (e & 7) + 8 * (e >> 5); }
+__device__ __forceinline__ int v_chunk(int e) { return (e >> 3) & 3; }
+
 // ---------------------------------------------------------------- wide kernel
 template <int R>
 __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom pool, ChunkArgs a) {
@@ -398,8 +403,12 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
 
   // Staging roles per step: K key kkey, 16-byte chunks kch and kch + 8 (each
   // wave instruction reads 8 whole half rows); V^T entries idx = tid + 256u for
-  // u = 0, 1: dim idx / 4, keys 8 (idx % 4) .. +7 (two 16-slot pieces of 16 dims
-  // each: whole lines).  A (block, head) tile holds bs << 8 bf16.
+  // u = 0, 1: dim v_dim(idx), keys 8 v_chunk(idx) .. +7.  A wave instruction
+  // covers 16 dims x 32 keys (two 16-slot pieces: whole lines), and each group
+  // of 8 lanes stores 8 different dims of one 8-key chunk, which the 80-byte
+  // LDS row stride spreads over 8 different 16-byte bank groups (LDS stores are
+  // served 8 lanes at a time; two dims 128 bytes apart in one group would
+  // conflict).  A (block, head) tile holds bs << 8 bf16.
   const int tshift = lbs + 8;
   const int kkey = tid >> 3, kch = tid & 7;
   struct Stage {
@@ -417,8 +426,8 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + kWideThreads * u;
-      const int kv = min(key0 + 8 * (idx & 3), k1 - 1) & ~7;
-      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), idx >> 2));
+      const int kv = min(key0 + 8 * v_chunk(idx), k1 - 1) & ~7;
+      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), v_dim(idx)));
     }
   };
   auto store = [&](Stage& st, int step, int buf) {
@@ -429,12 +438,12 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int idx = tid + kWideThreads * u;
-      const int kv = key0 + 8 * (idx & 3);
+      const int kv = key0 + 8 * v_chunk(idx);
       if (kv + 8 > k1) {  // V of keys past the split end must be 0 (0 * NaN would poison O)
         st.v[u].x &= keep2(kv + 0, k1); st.v[u].y &= keep2(kv + 2, k1);
         st.v[u].z &= keep2(kv + 4, k1); st.v[u].w &= keep2(kv + 6, k1);
       }
-      *reinterpret_cast<uint4*>(&s_v[buf][(idx >> 2) * kVRow + 8 * (idx & 3)]) = st.v[u];
+      *reinterpret_cast<uint4*>(&s_v[buf][v_dim(idx) * kVRow + 8 * v_chunk(idx)]) = st.v[u];
     }
   };
 
