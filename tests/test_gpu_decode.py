@@ -31,10 +31,20 @@ def _note(msg):
 
 
 # ---------------------------------------------------------------- write (a1-a3)
-@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5"])
+@pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5",
+                                  "cfg5@32", "cfg5@64", "cfg5@128", "cfg5@256"])
 def test_cache_write_parity_and_exact_slots(name):
+    """name@bs: the same step with bs-token blocks (same token capacity), where V^T
+    is stored in several 16-slot pieces per block."""
     _note(f"[write] {name}")
-    w = workload(name)
+    if "@" in name:
+        import dataclasses
+
+        base, bs = name.split("@")
+        b = SPECS[base]
+        w = make_step(dataclasses.replace(b, block_size=int(bs), num_blocks=b.num_blocks * b.block_size // int(bs)))
+    else:
+        w = workload(name)
     run = StepRun(w, fill_prefix=False)
     s = w.spec
     shape = (len(run.used), s.block_size, s.num_kv_heads, 128)
