@@ -164,8 +164,10 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
 
 
 def measure_graphs(dev, iters=50):
-    """Decode step (cache write + decode over L layer pools) issued eagerly
-    through pre-bound calls vs replayed from one captured HIP graph:
+    """Decode step over L layer pools, as the two calls per layer (cache write +
+    decode) or the one fused pgqa_decode_step launch per layer ("fused_"),
+    issued eagerly through pre-bound calls vs replayed from one captured HIP
+    graph:
       *_gpu_us_per_layer   steps issued back to back, events around each step
                            (GPU time, the host runs ahead);
       *_sync_us_per_step   wall clock of one step issued and waited for (the
@@ -193,25 +195,31 @@ def measure_graphs(dev, iters=50):
             pools.append(p)
         pad = int(np.setdiff1d(np.arange(s.num_blocks), w.used_blocks)[0])
         tok = w.dec_tok
-        g = DecodeGraphs(pools, s.num_q_heads, w.block_tables.shape[1], pad, to_bf16(w.wq), to_bf16(w.wk), s.eps,
-                         s.rope_theta, 1.0 / math.sqrt(128), max_batch=B, buckets=[B])
-        inp = g.inputs(B)
-        for l in range(layers):
-            inp.q[l].copy_(to_bf16(w.tok_q[tok]))
-            inp.k[l].copy_(to_bf16(w.tok_k[tok]))
-            inp.v[l].copy_(to_bf16(w.tok_v[tok]))
-        inp.positions.copy_(to_i32(w.tok_pos[tok]))
-        inp.context_lens.copy_(to_i32(w.dec_ctx))
-        inp.block_tables.copy_(to_i32(w.dec_block_tables))
-        eager = g.eager_calls(B)  # the calls the graph captured, issued one by one on this stream
+        graphs = {}
+        for fused in (False, True):
+            g = DecodeGraphs(pools, s.num_q_heads, w.block_tables.shape[1], pad, to_bf16(w.wq), to_bf16(w.wk),
+                             s.eps, s.rope_theta, 1.0 / math.sqrt(128), max_batch=B, buckets=[B], fused=fused)
+            inp = g.inputs(B)
+            for l in range(layers):
+                inp.q[l].copy_(to_bf16(w.tok_q[tok]))
+                inp.k[l].copy_(to_bf16(w.tok_k[tok]))
+                inp.v[l].copy_(to_bf16(w.tok_v[tok]))
+            inp.positions.copy_(to_i32(w.tok_pos[tok]))
+            inp.context_lens.copy_(to_i32(w.dec_ctx))
+            inp.block_tables.copy_(to_i32(w.dec_block_tables))
+            graphs[fused] = (g, g.eager_calls(B))  # the captured calls, issued one by one on this stream
 
-        def run_eager():
-            for c in eager:
-                c()
+        def eager_of(calls):
+            def run():
+                for c in calls:
+                    c()
+            return run
 
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
         out = {"batch": B, "layers": layers}
-        for label, run in (("eager", run_eager), ("graph", lambda: g.replay(B))):
+        runs = (("eager", eager_of(graphs[False][1])), ("graph", lambda: graphs[False][0].replay(B)),
+                ("fused_eager", eager_of(graphs[True][1])), ("fused_graph", lambda: graphs[True][0].replay(B)))
+        for label, run in runs:
             for _ in range(5):
                 run()
             torch.cuda.synchronize()
@@ -230,7 +238,7 @@ def measure_graphs(dev, iters=50):
                 wall.append((time.perf_counter() - t0) * 1e6)
             out[label + "_sync_us_per_step"] = round(sorted(wall)[len(wall) // 2], 1)
         res[name] = out
-        del g, pools, eager
+        del graphs, pools
         torch.cuda.empty_cache()
     return res
 

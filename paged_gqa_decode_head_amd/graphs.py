@@ -7,14 +7,17 @@ maximum batch), and any other shape runs eagerly.  Here a step of B
 sequences replays the graph of the smallest captured bucket >= B; rows
 B .. bucket-1 are padding.
 
-One captured step is, for each layer pool in turn, the fused norm + rotary +
-cache write of one new token per sequence followed by paged decode attention
-over the cache (the C-ABI calls ``pgqa_rms_norm_rope_cache_write`` and
-``pgqa_paged_decode_attention``).  Buffers, plans and workspaces are fixed at
+One captured step is, for each layer pool in turn, the norm + rotary + cache
+write of one new token per sequence and paged decode attention over the
+cache: by default one ``pgqa_decode_step`` launch per layer (the new token sits
+at position context_len - 1), or with ``fused=False`` the two calls
+``pgqa_rms_norm_rope_cache_write`` (at ``positions``) and
+``pgqa_paged_decode_attention``.  Buffers, plans and workspaces are fixed at
 capture time: the caller writes a step's inputs into the views ``inputs(B)``
-returns and calls ``replay(B)``.  Padding rows write their k/v into slot 0 of
-a reserved pad block and attend over zero keys, so their outputs are zero rows
-and no sequence's cache is touched.
+returns and calls ``replay(B)``.  Padding rows attend over zero keys, so their
+outputs are zero rows; the fused step writes nothing for them, the two-call
+step writes their k/v into slot 0 of a reserved pad block, so no sequence's
+cache is touched either way.
 
 This module is host plumbing (torch's graph capture around the library's
 launches); every operation of the step runs in libpgqa's kernels.
@@ -23,7 +26,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (DecodePlan, Pool, bind_cache_write, bind_decode, decode_workspace_bytes, plan_decode)
+from . import (DecodePlan, Pool, bind_cache_write, bind_decode, bind_decode_step, decode_workspace_bytes,
+               plan_decode)
 
 
 def default_buckets(max_batch: int) -> list[int]:
@@ -43,7 +47,7 @@ class StepInputs:
     q: object          # [L, B, Hq, 128] bf16: per layer, the new token's q projection
     k: object          # [L, B, Hkv, 128] bf16
     v: object          # [L, B, Hkv, 128] bf16
-    positions: object  # [B] int32: position of the new token (= keys before it)
+    positions: object  # [B] int32: position of the new token (= keys before it); read by the two-call step only
     context_lens: object  # [B] int32: keys attended, the new token included
     block_tables: object  # [B, max_blocks_per_seq] int32
 
@@ -53,7 +57,7 @@ class DecodeGraphs:
 
     def __init__(self, pools: list[Pool], num_q_heads: int, max_blocks_per_seq: int, pad_block: int,
                  q_norm_weight, k_norm_weight, eps: float, rope_theta: float, scale: float, max_batch: int,
-                 buckets: list[int] | None = None):
+                 buckets: list[int] | None = None, fused: bool = True):
         import torch
 
         if not pools:
@@ -67,7 +71,7 @@ class DecodeGraphs:
                 raise ValueError(f"max_batch {max_batch} exceeds the pool's max_batch_size")
         if not 0 <= pad_block < p0.config.num_blocks:
             raise ValueError("pad_block must be a block id of the pools")
-        self.pools, self.pad_block = list(pools), pad_block
+        self.pools, self.pad_block, self.fused = list(pools), pad_block, bool(fused)
         self.buckets = sorted(set(buckets if buckets is not None else default_buckets(max_batch)))
         if self.buckets[0] < 1 or self.buckets[-1] > max_batch:
             raise ValueError("buckets must lie in 1 .. max_batch")
@@ -113,6 +117,12 @@ class DecodeGraphs:
     def _bind(self, B: int, plan: DecodePlan, ws):
         calls = []
         for l, p in enumerate(self.pools):
+            if self.fused:
+                calls.append(bind_decode_step(p, self.q[l, :B], self.k[l, :B], self.v[l, :B], self._wq, self._wk,
+                                              self.context_lens[:B], self.block_tables[:B], self.max_ctx, self._eps,
+                                              self._theta, self._scale, self.out[l, :B], plan=plan, workspace=ws[l],
+                                              q_out=self.q_out[l, :B]))
+                continue
             calls.append(bind_cache_write(p, self.q[l, :B], self.k[l, :B], self.v[l, :B], self._wq, self._wk,
                                           self.positions[:B], self.seq_ids[:B], self.block_tables[:B], self._eps,
                                           self._theta, self.q_out[l, :B]))

@@ -34,7 +34,10 @@ def _pools(rng, n):
     return out
 
 
-def test_decode_graph_replays_match_eager_calls():
+@pytest.mark.parametrize("fused", [True, False])
+def test_decode_graph_replays_match_eager_calls(fused):
+    """Graphs of the fused step (one launch per layer) or of the two calls,
+    against the two eager calls: the fused step is bit-identical to them."""
     rng = np.random.default_rng(31)
     L = 2
     state = rng.bit_generator.state
@@ -44,11 +47,11 @@ def test_decode_graph_replays_match_eager_calls():
     wq = torch.from_numpy(1 + 0.1 * rng.standard_normal(128)).to(torch.bfloat16).cuda()
     wk = torch.from_numpy(1 + 0.1 * rng.standard_normal(128)).to(torch.bfloat16).cuda()
     pad = NB - 1
-    graphs = DecodeGraphs(pools_g, HQ, MBS, pad, wq, wk, EPS, THETA, SCALE, MAXB, buckets=[1, 2, 4])
+    graphs = DecodeGraphs(pools_g, HQ, MBS, pad, wq, wk, EPS, THETA, SCALE, MAXB, buckets=[1, 2, 4], fused=fused)
     assert graphs.bucket_for(3) == 4 and graphs.bucket_for(5) is None
     perm = rng.permutation(NB - 1)  # block ids for the sequences; the pad block is never dealt
     for step, B in enumerate([3, 4, 1, 3, 2]):
-        print(f"[graph] step {step} batch {B}", flush=True)
+        print(f"[graph] fused={fused} step {step} batch {B}", flush=True)
         bucket = graphs.bucket_for(B)
         ctx = rng.integers(1, MBS * BS + 1, size=B).astype(np.int32)
         bt = np.full((B, MBS), -1, dtype=np.int32)
