@@ -14,8 +14,8 @@
 //
 // Rows.  The query rows of a segment and kv head g are the pairs (token, head
 // in group), row rho = token * r + hh, cut into 32-row tiles (one wave each).
-// Two kinds of work item, listed on the device by a one-workgroup schedule
-// kernel (so no workgroup of the grid idles on metadata it does not need):
+// Two kinds of work item; every workgroup derives its own item from the
+// device metadata (see the work lists below):
 //   * wide (segments of more than 32 rows per kv head: prefill slices).  Item =
 //     (segment, g, group of 4 tiles, key split); 4 waves share every 32-key step,
 //     staged once in LDS by all 256 threads through a 3-deep LDS ring fed by a
