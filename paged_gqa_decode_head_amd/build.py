@@ -66,7 +66,32 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"linking libpgqa.so failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_c_consumer(verbose)
     return LIB
+
+
+def build_c_consumer(verbose: bool = False) -> str:
+    """tests/c_decode_step.c (the C-ABI decode step driven from C with the HIP
+    runtime) -> tests/bin/c_decode_step, linked to the in-tree libpgqa.so."""
+    src = os.path.join(ROOT, "tests", "c_decode_step.c")
+    out = os.path.join(ROOT, "tests", "bin", "c_decode_step")
+    if not os.path.exists(src):
+        return ""
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        raise RuntimeError("no C compiler found for tests/c_decode_step.c")
+    cmd = [cc, "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{os.path.join(rocm, 'include')}", f"-I{os.path.join(ROOT, 'include')}", src,
+           f"-L{PKG}", "-lpgqa", f"-L{os.path.join(rocm, 'lib')}", "-lamdhip64",
+           f"-Wl,-rpath,{os.path.join(rocm, 'lib')}", "-Wl,-rpath,$ORIGIN/../../paged_gqa_decode_head_amd", "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {src} failed:\n{r.stdout}\n{r.stderr}")
+    return out
 
 
 if __name__ == "__main__":
