@@ -66,6 +66,7 @@ constexpr int kMaxBlockIds = 4096 / 16 + 1;  // block ids one split can touch
 constexpr int kCombineRows = 8;          // rows per combine workgroup (32 lanes each)
 constexpr int kCombineParts = kRows / kCombineRows;
 constexpr int kCombineChunk = 256;       // splits whose weights are staged in LDS at a time
+constexpr int kCombineFast = 16;         // rows with at most this many splits: all partial loads up front
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -620,9 +621,11 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
 
 // ---------------------------------------------------------------- combine
 // Log-sum-exp combine of the split partials of 8 rows of one tile: 32 lanes
-// per row, each owning 4 dims.  The lanes of a row first reduce the row's
-// split lse values (lane j takes splits j, j+32, ...), then the split weights
-// go through LDS and every lane sums its 4 dims over the splits in order.
+// per row, each owning 4 dims.  Rows with at most 16 splits load every partial
+// at once and exchange the split weights by shuffle.  Longer rows first reduce
+// the row's split lse values (lane j takes splits j, j+32, ...), then the split
+// weights go through LDS and every lane sums its 4 dims over the splits in
+// order.
 template <int R>
 __global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, ChunkArgs a) {
   const Located loc = locate<kCombineList>(a, pool, blockIdx.x, R);
@@ -638,6 +641,39 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, Chunk
   const int64_t stride = int64_t(a.total_q) * R;  // partial rows per split
   const int64_t base = int64_t(g) * a.max_splits * stride + qrow * R + hh;
   __shared__ float s_w[kCombineRows][kCombineChunk];
+  const float* src = a.part_o + base * kHeadDim + 4 * j;
+
+  if (ns <= kCombineFast) {
+    // Up to 16 splits: every partial load is issued first, beside the one lse
+    // value lane j (< ns) reads; the weights then travel between the row's 32
+    // lanes by shuffle, and the partials are summed in split order.
+    float4 v[kCombineFast];
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k)
+      v[k] = row_ok && k < ns ? *reinterpret_cast<const float4*>(src + k * stride * kHeadDim)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float lk = row_ok && j < ns ? a.part_lse[base + j * stride] : -INFINITY;
+    float M = lk;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+    float L = e;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) {
+      const float w = __shfl(e, k, 32) * inv;  // lane k of this row's 32
+      if (k < ns) {
+        acc.x += w * v[k].x; acc.y += w * v[k].y; acc.z += w * v[k].z; acc.w += w * v[k].w;
+      }
+    }
+    if (!row_ok) return;
+    uint16_t* dst = a.out + (qrow * a.num_q_heads + g * R + hh) * kHeadDim + 4 * j;
+    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    return;
+  }
 
   // Row max and weight sum in one pass over the split lse values (lanes of a
   // row are 32 consecutive threads): each lane keeps a running (max, sum) of
@@ -663,7 +699,6 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, Chunk
   const float inv = L > 0.f ? 1.f / L : 0.f;
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* src = a.part_o + base * kHeadDim + 4 * j;
   for (int c0 = 0; c0 < ns; c0 += kCombineChunk) {
     const int cn = min(kCombineChunk, ns - c0);
     __syncthreads();

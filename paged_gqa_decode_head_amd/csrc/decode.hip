@@ -50,6 +50,7 @@ namespace {
 
 constexpr float kTau = 8.0f;              // log2 headroom before the running max is raised
 constexpr int kMaxTilesPerWave = 64;      // block ids of a wave's tiles live one per lane
+constexpr int kCombineFast = 32;          // plans with at most this many splits: one-shot combine
 
 struct Tile {
   uint4 k[4];  // key 2G: k[0] dims 8s.., k[1] dims 64+8s..;  key 2G+1: k[2], k[3]
@@ -446,19 +447,52 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
 // Log-sum-exp combine of the split partials: one workgroup per (sequence,
 // query head), one thread per dim.  Partials are merged in split order, so
 // the result does not depend on the order in which split workgroups ran.
+// Plans of up to 32 splits issue every load at once (one round trip).
 // A separate launch: the kernel boundary makes the partials visible without
 // per-workgroup cache write-back fences.
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, DecodeArgs a) {
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
   const int g = h / r, hh = h - g * r;
+  const int64_t unit = int64_t(b) * hkv + g;
+  const float* pl = a.part_lse + unit * a.max_splits * r + hh;
+  const float* po = a.part_o + (unit * a.max_splits * r + hh) * kHeadDim + d;
+
+  if (a.max_splits <= kCombineFast) {
+    // Every load at once: the context length, the partials of all the plan's
+    // split slots (slots past this sequence's splits are read but unused) and
+    // one lse per lane; the weights then go between lanes by shuffle.
+    const int n = a.ctx[b];
+    float v[kCombineFast];
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) v[k] = k < a.max_splits ? po[int64_t(k) * r * kHeadDim] : 0.f;
+    const int lane = d & 63;
+    const float lraw = lane < a.max_splits ? pl[lane * r] : -INFINITY;
+    if (n <= 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * pool.block_size) return;
+    const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+    if (ns <= 1) return;  // written directly by the split kernel
+    const float lk = lane < ns ? lraw : -INFINITY;
+    float M = lk;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+    float L = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) {
+      const float ek = __shfl(e, k);
+      if (k < ns) acc += ek * v[k];
+    }
+    a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+    return;
+  }
+
   const int n = a.ctx[b];
   if (n <= 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * pool.block_size) return;
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (ns <= 1) return;  // written directly by the split kernel
-  const int64_t unit = int64_t(b) * hkv + g;
-  const float* pl = a.part_lse + unit * a.max_splits * r + hh;
-  const float* po = a.part_o + (unit * a.max_splits * r + hh) * kHeadDim + d;
   float M = -INFINITY;
   for (int k = 0; k < ns; ++k) M = fmaxf(M, pl[k * r]);
   float o = 0.f;
