@@ -264,10 +264,11 @@ struct RowState {
   float m, l;
 };
 
-template <typename VOp>
-__device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, bool full, int key0, int klim,
-                                           int qpos, int half, float c, float tau_raw, VOp&& vop) {
-  float sv[16];
+// Phase 1 of one step's online softmax: the masked scores sv and the row max;
+// the running max is raised (and o, l rescaled) only when a score exceeds it
+// by more than the headroom.
+__device__ __forceinline__ void softmax_max(RowState& st, const f32x16_t& sacc, bool full, int key0, int klim,
+                                            int qpos, int half, float c, float tau_raw, float (&sv)[16]) {
   if (full) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
@@ -289,6 +290,12 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, b
     st.l *= corr;
     st.m = mn;
   }
+}
+
+// Phase 2: the bf16 weights as the PV operand, pb[s16] holding keys
+// 16 s16 + 8 half .. +7 of the lane's row, and their sum into l (the same
+// rounded weights PV uses).
+__device__ __forceinline__ void softmax_exp(RowState& st, const float (&sv)[16], float c, uint4 (&pb)[2]) {
   const float neg_mc = st.m == -INFINITY ? 0.f : -st.m * c;
   constexpr uint32_t kOnes = 0x3f803f80u;  // bf16 pair (1, 1)
 #pragma unroll
@@ -301,9 +308,21 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, b
       pk[e] = pack_bf16x2(p0, p1);
       st.l = dot2_bf16(pk[e], kOnes, st.l);
     }
-    const uint4 pb = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    pb[s16] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  }
+}
+
+template <typename VOp>
+__device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, bool full, int key0, int klim,
+                                           int qpos, int half, float c, float tau_raw, VOp&& vop) {
+  float sv[16];
+  softmax_max(st, sacc, full, key0, klim, qpos, half, c, tau_raw, sv);
+  uint4 pb[2];
+  softmax_exp(st, sv, c, pb);
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma32(vop(dt, s16), pb, st.o[dt]);
+  for (int s16 = 0; s16 < 2; ++s16) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) st.o[dt] = mfma32(vop(dt, s16), pb[s16], st.o[dt]);
   }
 }
 
@@ -488,12 +507,20 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
   // buf holds step i, nbuf step i+1 (stale past the last step: its scores go unused)
   auto iter = [&](int i, int buf, int nbuf, int sbuf, Stage& sst) {
     if (tile_ok && i < nsteps) {
-      const f32x16_t s_next = qk(nbuf);
       const int key0 = k0 + i * kStep;
       const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= qpos_first;
-      softmax_pv(rs, s_cur, full, key0, k1, qpos, half, c, tau_raw, [&](int dt, int s16) {
-        return ld16(&s_v[buf][(32 * dt + col) * kVRow + 16 * s16 + 8 * half]);
-      });
+      float sv[16];
+      softmax_max(rs, s_cur, full, key0, k1, qpos, half, c, tau_raw, sv);
+      // next step's scores, issued beside this step's exponentials (independent work in one block)
+      const f32x16_t s_next = qk(nbuf);
+      uint4 pb[2];
+      softmax_exp(rs, sv, c, pb);
+#pragma unroll
+      for (int s16 = 0; s16 < 2; ++s16) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          rs.o[dt] = mfma32(ld16(&s_v[buf][(32 * dt + col) * kVRow + 16 * s16 + 8 * half]), pb[s16], rs.o[dt]);
+      }
       s_cur = s_next;
     }
     store(sst, min(i + 2, nsteps - 1), sbuf);
