@@ -7,7 +7,8 @@
 // laid out for CDNA4.
 //
 // Work decomposition.  One workgroup per (sequence b, kv head g, split sp); a
-// split is split_tokens consecutive keys.  All r = Hq / Hkv query heads of the
+// split is split_tokens consecutive keys.  The grid is ordered (g, b, sp), the
+// split slowest, so that each split level spreads over all XCDs.  All r = Hq / Hkv query heads of the
 // group are processed by the same workgroup, so each K/V byte is read from HBM
 // once.  The W waves of the workgroup take the split's 16-key tiles in turn
 // (wave w: tiles w, w+W, ...), each wave keeping its own online softmax state.
@@ -70,7 +71,11 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
 
 template <int R, int W, bool kStream, bool kFused>
 __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a, StepArgs st) {
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  // grid (kv head, sequence, split): the split index varies slowest, so every
+  // split level is dealt over all 8 XCDs (workgroups go to XCDs round-robin by
+  // linear id; with the split fastest, 2 or 4 splits would pin each split level,
+  // and the always-present first splits, to a quarter or half of the XCDs)
+  const int g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 3, sub = lane & 7, khalf = lane & 1;
   const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
 
 template <int R, int W, bool kStream>
 hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
-  const dim3 grid(a.max_splits, pool.num_kv_heads, a.batch);
+  const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
   if (st != nullptr) {
     hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
   } else {
