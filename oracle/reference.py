@@ -36,7 +36,8 @@ Conventions of this module:
     ``K[num_blocks][block_size][Hkv][D]`` (the "BSHD" cache of [P1] Summary
     item 1), independent of whatever physical layout the GPU library uses.
   * A sequence with zero visible keys yields a zero output row (the softmax over
-    an empty set is undefined; zero is the convention of this build).
+    an empty set is undefined; zero is the convention taken here, and the library
+    does the same).
 """
 from __future__ import annotations
 

@@ -190,7 +190,7 @@ def make_step(spec: StepSpec, rep: int = 0) -> StepWorkload:
 
 
 # ---------------------------------------------------------------------------
-# The five Qwen3-shaped workloads (sizes in the design doc's input recipe)
+# The five Qwen3-shaped workloads: shapes, batch and context draws of each
 # ---------------------------------------------------------------------------
 SPECS = {
     "cfg1": StepSpec(
