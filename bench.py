@@ -342,7 +342,8 @@ def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, ta
     q_buf = torch.empty((qkv_cap, hq, 128), dtype=torch.bfloat16, device=dev)
     o_buf = torch.empty((qkv_cap, hq, 128), dtype=torch.bfloat16, device=dev)
     res = {}
-    for label, chunked in (("chunked", True), ("whole_prompt", False)):
+    # a first, untimed pass of the chunked run loads every kernel it uses
+    for label, chunked in (("warmup", True), ("chunked", True), ("whole_prompt", False)):
         planner = pg.StepPlanner(budget, streams + 1, chunked, bs, width, streams + 1, np.arange(nb)[::-1])
         for i in range(streams):  # streams whose prefix is already cached (blocks taken directly)
             need = -(-int(ctx0[i]) // bs)
@@ -367,13 +368,14 @@ def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, ta
                     to_i32(qsl), to_i32(ctx), to_i32(bt_seg))
             q_out = q_buf[:T]
             out = o_buf[:T]
-            calls = [pg.bind_cache_write(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[0], args[1], args[2],
-                                         1e-6, 1e6, q_out)]
-            if (segs[:, 2] == 1).all():  # host routing: single decode tokens only -> the decode call
-                calls.append(pg.bind_decode(pool, q_out, args[4], args[5], int(ctx.max()), scale, out))
+            if (segs[:, 2] == 1).all():  # host routing: single decode tokens only -> one fused decode step
+                calls = [pg.bind_decode_step(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[4], args[5],
+                                             int(ctx.max()), 1e-6, 1e6, scale, out, q_out=q_out)]
             else:
-                calls.append(pg.bind_chunk(pool, q_out, args[3], args[4], args[5], int(segs[:, 2].max()),
-                                           int(ctx.max()), scale, out))
+                calls = [pg.bind_cache_write(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[0], args[1],
+                                             args[2], 1e-6, 1e6, q_out),
+                         pg.bind_chunk(pool, q_out, args[3], args[4], args[5], int(segs[:, 2].max()),
+                                       int(ctx.max()), scale, out)]
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -393,6 +395,8 @@ def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, ta
             if prompt_done_us is not None and step > done_step + tail:
                 break
         assert pool.check_errors() == 0
+        if label == "warmup":
+            continue
         res[label] = {"steps": len(step_us), "worst_step_us": max(step_us),
                       "median_step_us": float(np.median(step_us)), "prompt_ttft_us": round(prompt_done_us, 1),
                       "step_us": step_us}

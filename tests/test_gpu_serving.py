@@ -1,7 +1,8 @@
 """Serving steps driven by the host producers (include/pgqa_sched.h): the step
 planner feeds the fused norm + rotary + cache write and ONE attention call per
 step for the whole mixed batch (prefill chunks, decode rows and prompt-lookup
-verify rows together); a step of single decode tokens goes to the decode call.
+verify rows together); a step of single decode tokens goes to the fused decode
+step (norm + rotary + cache write + decode in one launch).
 Every step's output is checked against the fp64 reference on the read-back
 cache and the GPU-produced q."""
 import numpy as np
@@ -60,13 +61,15 @@ def test_planned_steps_match_reference(chunked):
         print(f"[serving] chunked={chunked} step {step}: segments {segs.tolist()}", flush=True)
         q, k, v = _bf16(rng, (T, HQ, 128)), _bf16(rng, (T, HKV, 128)), _bf16(rng, (T, HKV, 128))
         bt_full = dev_i32(planner.block_tables)
-        q_out = pg.rms_norm_rope_cache_write(pool, q, k, v, wq, wk, dev_i32(plan["token_pos"]),
-                                             dev_i32(plan["token_seq"]), bt_full, EPS, THETA)
         bt_seg = np.ascontiguousarray(planner.block_tables[segs[:, 0]])
         ctx, qsl = plan["context_lens"], plan["query_start_loc"]
-        if (segs[:, 2] == 1).all():  # host routing: only single decode tokens -> the decode call
-            out = pg.paged_decode_attention(pool, q_out, dev_i32(ctx), dev_i32(bt_seg), int(ctx.max()), SCALE)
+        if (segs[:, 2] == 1).all():  # host routing: only single decode tokens -> one fused decode step
+            q_out = torch.empty_like(q)
+            out = pg.decode_step(pool, q, k, v, wq, wk, dev_i32(ctx), dev_i32(bt_seg), int(ctx.max()), EPS, THETA,
+                                 SCALE, q_out=q_out)
         else:
+            q_out = pg.rms_norm_rope_cache_write(pool, q, k, v, wq, wk, dev_i32(plan["token_pos"]),
+                                                 dev_i32(plan["token_seq"]), bt_full, EPS, THETA)
             out = pg.paged_chunk_attention(pool, q_out, dev_i32(qsl), dev_i32(ctx), dev_i32(bt_seg),
                                            int(segs[:, 2].max()), int(ctx.max()), SCALE)
         kk, vv = pool.read_logical()
