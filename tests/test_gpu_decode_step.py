@@ -108,3 +108,44 @@ def test_fused_step_zero_context_and_bad_block():
     assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
     assert torch.all(out[1] == 0)
     assert torch.all(torch.isfinite(out[0].float()))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_fused_step_random_cases_against_fp64_chain(seed):
+    """Seeded random combinations of head layout, block size, context lengths
+    (single key, block boundaries, long) and split plan: outputs against the
+    fp64 chain, the new tokens' cache rows (K within tolerance, V bit-exact)."""
+    rng = np.random.default_rng(9000 + seed)
+    hq, hkv = [(16, 8), (32, 4), (8, 8), (32, 8), (8, 1), (8, 4)][int(rng.integers(6))]
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    nseq = int(rng.integers(1, 13))
+    picks = [0, bs - 1, bs, bs + 1, 2 * bs - 1, int(rng.integers(1, 3000)), int(rng.integers(1, 400))]
+    lens = [int(picks[int(rng.integers(len(picks)))]) for _ in range(nseq)]
+    nblocks = sum(-(-(L + 1) // bs) for L in lens) + 4
+    spec = StepSpec(f"frand-{seed}", 9100 + seed, hq, hkv, nblocks, decode=tuple(Group(1, L, L) for L in lens),
+                    block_size=bs)
+    w = make_step(spec)
+    s = w.spec
+    mx = int(w.dec_ctx.max())
+    plan = None
+    if rng.integers(3):
+        gran = max(64, bs)
+        split = min(gran * int(rng.integers(1, 9)), 4096 // gran * gran)
+        plan = pg.DecodePlan(split, -(-mx // split), int(rng.choice([1, 2, 4, 8])), int(rng.integers(3)))
+    _note(f"[frand] seed {seed}: heads {hq}/{hkv} bs {bs} contexts {w.dec_ctx.tolist()} plan {plan}")
+    run = StepRun(w)
+    q_out = torch.empty_like(run.q)
+    out = pg.decode_step(run.pool, run.q, run.k, run.v, run.wq, run.wk, run.dec_ctx, run.dec_bt, mx, s.eps,
+                         s.rope_theta, SCALE, plan=plan, q_out=q_out)
+    assert run.pool.check_errors() == 0
+    bt_c = compact(w.block_tables, run.used)
+    pk, pv = w.prefix_k[run.used].copy(), w.prefix_v[run.used].copy()
+    q_ref, _ = O.fused_norm_rope_write(w.tok_q, w.tok_k, w.tok_v, w.wq, w.wk, w.tok_pos, w.tok_seq, bt_c, s.eps,
+                                       s.rope_theta, pk, pv)
+    compare(q_out, q_ref, f"seed {seed} q_out")
+    compare(out, O.decode_attention(O.bf16_round(q_ref), pk, pv, bt_c, w.dec_ctx, SCALE), f"seed {seed} out")
+    kk, vv = run.pool.read_logical(blocks=run.used)
+    blk, off = O.slot_of(w.tok_pos, w.tok_seq, bt_c, bs)
+    assert np.array_equal(vv.numpy().view(np.uint16)[blk, off], pv[blk, off])
+    compare(torch.from_numpy(kk.numpy()[blk, off]).view(torch.bfloat16), O.bf16_bits_to_f64(pk[blk, off]),
+            f"seed {seed} new K rows")
