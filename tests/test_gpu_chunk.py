@@ -227,3 +227,41 @@ def test_chunk_addressing_probe_one_hot_every_position(q_len):
                     for h in range(hq):
                         assert np.array_equal(out[i, h], vk[bt[0, jstar // bs], jstar % bs, h // 2]), (jstar, i, h)
 
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_chunk_random_mixed_steps(seed):
+    """Seeded random mixed steps: wide segments (more than 32 rows per kv head)
+    and short ones (verify rows, single tokens, empty) in one call, random
+    prefixes (block boundaries included), head layouts, block sizes and split
+    plans, against the fp64 reference."""
+    rng = np.random.default_rng(7300 + seed)
+    hq, hkv = [(16, 8), (32, 4), (8, 8), (32, 8), (8, 1), (16, 4)][int(rng.integers(6))]
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    segs = []
+    for _ in range(int(rng.integers(1, 9))):
+        kind = int(rng.integers(4))
+        q_len = [int(rng.integers(17, 160)), int(rng.integers(2, 9)), 1, 0][kind]
+        prefix = int(rng.choice([0, bs - 1, bs, int(rng.integers(1, 1500))]))
+        segs.append((prefix, q_len))
+    if all(q == 0 for _, q in segs):  # at least one query token in the call
+        segs[0] = (segs[0][0], 1)
+    nb = sum(-(-(L + q) // bs) for L, q in segs) + 4
+    spec = _chunk_spec(f"crand-{seed}", 7400 + seed, hq, hkv, bs, segs, nb)
+    w = make_step(spec)
+    plan = None
+    mc = int(w.chk_ctx.max())
+    if rng.integers(3):
+        wide = int(rng.choice([32, 64, 128, 256, 1024]))
+        short = int(rng.choice([0, 32, 64, 256]))
+        smallest = min(wide, short) if short else wide
+        plan = pg.ChunkPlan(wide, -(-mc // smallest), short, 0)
+    _note(f"[crand] seed {seed}: heads {hq}/{hkv} bs {bs} segments (prefix, q_len) {segs} plan {plan}")
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    qlens = np.diff(w.chk_qsl)
+    out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, int(qlens.max()), mc, SCALE,
+                                   plan=plan)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_chunk_on_gpu_inputs(q), f"seed {seed}")
