@@ -18,9 +18,9 @@
 // device metadata (see the work lists below):
 //   * wide (segments of more than 32 rows per kv head: prefill slices).  Item =
 //     (segment, g, group of 4 tiles, key split); 4 waves share every 32-key step,
-//     staged once in LDS by all 256 threads through a 3-deep LDS ring fed by a
-//     3-deep register ring of global loads.  Each wave issues the score MFMAs of
-//     step i+1 before the softmax of step i, so the matrix core works while the
+//     staged once in LDS by all 256 threads with direct global->LDS loads into a
+//     4-stage ring (three steps in flight).  Each wave computes the scores of
+//     step i+1 beside the softmax of step i, so the matrix core works while the
 //     VALU does the softmax.  MFMA-bound.
 //   * narrow (at most 32 rows per kv head: verify rows, decode-like rows).  Item =
 //     (segment, g, key split), one wave, many short splits.  V^T is loaded from
@@ -42,8 +42,9 @@
 //     time.
 //   * dims of the S product are split between the lane halves as
 //     (l/32)*64 + 8*kstep + j: a lane reads 128 contiguous bytes of its q row.
-//   * LDS rows are padded (K: 272 bytes, V^T: 80 bytes) so that the 16 lanes
-//     of each LDS read phase hit 16 different 4-bank groups.
+//   * LDS operand reads are conflict-free: the 16 lanes of each read phase hit
+//     16 different 4-bank groups (wide kernel: XOR-swizzled stages, which direct
+//     loads can fill; narrow kernel: K rows padded to 272 bytes).
 #include <math.h>
 
 #include "device_common.hpp"
@@ -57,11 +58,8 @@ constexpr int kRows = 32;                // query rows per tile (one wave)
 constexpr int kWideTiles = 4;            // row tiles (waves) of a wide item
 constexpr int kWideThreads = 64 * kWideTiles;
 constexpr int kStep = 32;                // keys per step
-constexpr int kKRow = 136;               // LDS K row stride in bf16 (128 + 8 padding)
-constexpr int kVRow = 40;                // LDS V^T row stride in bf16 (32 + 8 padding)
-constexpr int kKStage = kStep * kKRow;   // bf16 elements per stage
-constexpr int kVStage = kHeadDim * kVRow;
-constexpr int kRing = 3;                 // wide: LDS stages and register stages
+constexpr int kKRow = 136;               // narrow: LDS K row stride in bf16 (128 + 8 padding)
+constexpr int kKStage = kStep * kKRow;   // narrow: bf16 elements of the per-wave K tile
 constexpr int kMaxBlockIds = 4096 / 16 + 1;  // block ids one split can touch
 constexpr int kCombineRows = 8;          // rows per combine workgroup (32 lanes each)
 constexpr int kCombineParts = kRows / kCombineRows;
@@ -78,13 +76,19 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 }
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-// ok ? v : 0, selected by value (a select of two lvalues would select addresses
-// and force the operands to scratch memory).
-__device__ __forceinline__ uint4 keep_if(bool ok, uint4 v) {
-  const uint32_t m = ok ? 0xffffffffu : 0u;
-  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
-}
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// x of lane l combined with x of lane l ^ 32 (v_permlane32_swap: no LDS round
+// trip).  Each lane receives the pair {x_l, x_(l^32)}, so both halves compute
+// the same value.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
 
 // Segment metadata as read on the device; bad metadata makes the segment
 // "bad": its rows are zeroed and a sticky flag raised.
@@ -189,6 +193,24 @@ struct Located {
   SegInfo si;
 };
 
+// The same Located in scalar registers: every lane of a wave holds the same
+// values, and saying so lets the compiler do the per-step key and address
+// arithmetic on the scalar unit.
+__device__ __forceinline__ Located wave_uniform(const Located& l) {
+  auto u = [](int v) { return __builtin_amdgcn_readfirstlane(v); };
+  Located r;
+  r.item = make_int4(u(l.item.x), u(l.item.y), u(l.item.z), u(l.item.w));
+  r.si.q0 = u(l.si.q0);
+  r.si.qlen = u(l.si.qlen);
+  r.si.n = u(l.si.n);
+  r.si.rows = u(l.si.rows);
+  r.si.tiles = u(l.si.tiles);
+  r.si.claimed_tiles = u(l.si.claimed_tiles);
+  r.si.bad = u(int(l.si.bad)) != 0;
+  r.si.err = uint32_t(u(int(l.si.err)));
+  return r;
+}
+
 // Item idx of list K, computed by one whole wave (every lane gets the result).
 // Lane i counts segments [i*per, i*per + per); a second pass over the chosen
 // lane's segments finds the segment (num_segments <= 4096, so per <= 64).
@@ -281,7 +303,7 @@ __device__ __forceinline__ void softmax_max(RowState& st, const f32x16_t& sacc, 
   float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
   mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
                        fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = halves_max(mx);
   if (__builtin_amdgcn_ballot_w64(mx > st.m + tau_raw)) {
     const float mn = fmaxf(st.m, mx);
     const float corr = mn == -INFINITY ? 1.f : fast_exp2((st.m - mn) * c);
@@ -331,7 +353,7 @@ __device__ __forceinline__ void softmax_pv(RowState& st, const f32x16_t& sacc, b
 template <int R>
 __device__ __forceinline__ void write_rows(const ChunkArgs& a, const RowState& st, int half, bool row_ok,
                                            int64_t qrow, int g, int hh, int sp, int ns, float c) {
-  const float L = st.l + __shfl_xor(st.l, 32);
+  const float L = halves_sum(st.l);
   if (!row_ok) return;
   const int hq = a.num_q_heads;
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -376,15 +398,41 @@ __device__ __forceinline__ uint32_t keep2(int key, int klim) {
   return key + 1 < klim ? 0xffffffffu : key < klim ? 0x0000ffffu : 0u;
 }
 
-// Wide-kernel V staging: entry e (0 .. 511) of a 32-key step is 8 keys of one
-// V^T row: dim (e % 8) + 8 (e / 32), keys 8 ((e / 8) % 4) .. +7.
-__device__ __forceinline__ int v_dim(int e) { return (e & 7) + 8 * (e >> 5); }
-__device__ __forceinline__ int v_chunk(int e) { return (e >> 3) & 3; }
-
 // ---------------------------------------------------------------- wide kernel
+// LDS stage of one 32-key step (16 KB, filled by direct global->LDS loads, so
+// rows cannot be padded; an XOR swizzle keeps the operand reads free of bank
+// conflicts instead):
+//   K    bytes [0, 8192): key row kk (256 bytes) with its 16-byte chunk c at
+//        position c ^ (kk % 16);
+//   V^T  bytes 8192 + 4096 p: 16-key piece p as [dim][32 bytes], the 8-key half
+//        h of dim d at position h ^ ((d / 8) % 2).
+// Every 16-lane phase of a 16-byte operand read then touches 16 different
+// 16-byte bank groups.
+constexpr int kStageBytes = 16384;
+constexpr int kVBytes0 = 8192;
+constexpr int kWideRing = 4;  // stages: step i (V read), i+1 (K read), i+2 landing, i+3 issued
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte direct global->LDS load per lane: lane l writes LDS bytes
+// [dst + 16 l, dst + 16 l + 16); dst must be the same in every lane.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+constexpr int kWaitVm4 = 0x0F74;      // vmcnt(4)
+constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
+
+// A workgroup barrier that also orders the compiler's memory accesses, without
+// the release fence of __syncthreads (which would wait for every direct load
+// still in flight, prefetches included).
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int R>
 __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom pool, ChunkArgs a) {
-  const Located loc = locate<kWideList>(a, pool, blockIdx.x, R);
+  const Located loc = wave_uniform(locate<kWideList>(a, pool, blockIdx.x, R));
   if (loc.item.x < 0) return;
   const SegInfo& si = loc.si;
   const int s = loc.item.x, g = loc.item.y, grp = loc.item.z, sp = loc.item.w;
@@ -396,8 +444,13 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
     return;
   }
 
-  __shared__ __align__(16) uint16_t s_k[kRing][kKStage];
-  __shared__ __align__(16) uint16_t s_v[kRing][kVStage];
+  // Four separate arrays, not one indexed ring: the compiler then tells the
+  // stages apart and does not make a read of one stage wait for the direct
+  // loads still landing in another.
+  __shared__ __align__(1024) uint8_t s_st0[kStageBytes];
+  __shared__ __align__(1024) uint8_t s_st1[kStageBytes];
+  __shared__ __align__(1024) uint8_t s_st2[kStageBytes];
+  __shared__ __align__(1024) uint8_t s_st3[kStageBytes];
   __shared__ int32_t s_blk[kMaxBlockIds];
 
   const int prefix = si.n - si.qlen;
@@ -421,49 +474,69 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
   load_q(qv, a, row_ok, qrow, g * R + hh, half);
   __syncthreads();
 
-  // Staging roles per step: K key kkey, 16-byte chunks kch and kch + 8 (each
-  // wave instruction reads 8 whole half rows); V^T entries idx = tid + 256u for
-  // u = 0, 1: dim v_dim(idx), keys 8 v_chunk(idx) .. +7.  A wave instruction
-  // covers 16 dims x 32 keys (two 16-slot pieces: whole lines), and each group
-  // of 8 lanes stores 8 different dims of one 8-key chunk, which the 80-byte
-  // LDS row stride spreads over 8 different 16-byte bank groups (LDS stores are
-  // served 8 lanes at a time; two dims 128 bytes apart in one group would
-  // conflict).  A (block, head) tile holds bs << 8 bf16.
+  // Direct loads of a step (4 per lane, each wave instruction 1 KB of the stage):
+  //   K u = 0, 1:  key row kr = 4 (2 wave + u) + lane / 16, its chunk
+  //                (lane % 16) ^ (kr % 16), to stage bytes 1024 (2 wave + u) + 16 lane;
+  //   V u = 0, 1:  dim vd = 32 wave + lane / 2, the 8 keys of half
+  //                (lane % 2) ^ ((vd / 8) % 2) of piece u, to stage bytes
+  //                8192 + 4096 u + 1024 wave + 16 lane.
+  // Splits start at multiples of 32 keys, so each 16-key half of a step lies in
+  // one block: a step needs two tile addresses, the same in every lane, and each
+  // load adds a fixed per-lane offset.  A half past the split end re-reads the
+  // half that holds the split's last key; keys past the end inside a half read
+  // their own (unused) slots of the same block.  Their scores are masked and
+  // their V is zeroed by fix_tail.  A (block, head) tile holds bs << 8 bf16: K
+  // rows [bs][128], then V^T.
   const int tshift = lbs + 8;
-  const int kkey = tid >> 3, kch = tid & 7;
-  struct Stage {
-    uint4 k[2], v[2];
-  };
-  // Loads are unconditional: a key past the split end re-reads the split's last
-  // key (its score is masked, its V zeroed when stored), so the compiler counts
-  // outstanding loads exactly and the ring stays full.
-  auto fetch = [&](Stage& st, int step) {
-    const int key0 = k0 + step * kStep;
-    const int kk = min(key0 + kkey, k1 - 1);
-    const uint16_t* kp = pool.kv + (int64_t(s_blk[(kk >> lbs) - b0]) << tshift) + (kk & (bs - 1)) * kHeadDim + kch * 8;
-    st.k[0] = ld16(kp);
-    st.k[1] = ld16(kp + 64);
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int vd = 32 * wave + (lane >> 1);
+  const int vhalf = (lane & 1) ^ ((vd >> 3) & 1);
+  uint32_t koff[2];  // bytes from the K row of the half's first key
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + kWideThreads * u;
-      const int kv = min(key0 + 8 * v_chunk(idx), k1 - 1) & ~7;
-      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), v_dim(idx)));
+  for (int u = 0; u < 2; ++u) {
+    const int kr = 4 * (2 * wave + u) + (lane >> 4);
+    koff[u] = uint32_t(((kr & 15) * kHeadDim + ((lane & 15) ^ (kr & 15)) * 8) * 2);
+  }
+  const uint32_t voff = uint32_t((bs * kHeadDim + vd * kVSub + 8 * vhalf) * 2);  // V^T follows the K rows
+  const uint8_t* kv_bytes = reinterpret_cast<const uint8_t*>(pool.kv);
+  // The two half tiles of a step (read from s_blk one iteration before their
+  // loads are issued, so the LDS latency is hidden), then the step's 4 loads.
+  struct HalfBases {
+    const uint8_t* h[2];
+  };
+  auto half_bases = [&](int step) {
+    const int key0 = k0 + step * kStep;
+    HalfBases hb;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int hk = min(key0 + 16 * h, k1 - 1) & ~15;
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[(hk >> lbs) - b0]);
+      hb.h[h] = kv_bytes + ((int64_t(blk) << tshift) + (hk & (bs - 1)) * kHeadDim) * 2;
     }
+    return hb;
   };
-  auto store = [&](Stage& st, int step, int buf) {
+  auto dma_step = [&](uint8_t* st, const HalfBases& hb) {
+    const uint8_t* kb = (wv >> 1) ? hb.h[1] : hb.h[0];  // K rows of this wave: half wave / 2
+    dma16(reinterpret_cast<const uint16_t*>(kb + koff[0]), st + 1024 * (2 * wv));
+    dma16(reinterpret_cast<const uint16_t*>(kb + koff[1]), st + 1024 * (2 * wv + 1));
+    dma16(reinterpret_cast<const uint16_t*>(hb.h[0] + voff), st + kVBytes0 + 1024 * wv);
+    dma16(reinterpret_cast<const uint16_t*>(hb.h[1] + voff), st + kVBytes0 + 4096 + 1024 * wv);
+  };
+  // V of keys past the split end must be 0 (0 * NaN would poison O): each lane
+  // clears its own chunks of the split's last step once they have landed.
+  auto fix_tail = [&](uint8_t* st, int step) {
     const int key0 = k0 + step * kStep;
-    uint16_t* kd = &s_k[buf][kkey * kKRow + kch * 8];
-    *reinterpret_cast<uint4*>(kd) = st.k[0];
-    *reinterpret_cast<uint4*>(kd + 64) = st.k[1];
+    if (key0 + kStep <= k1) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int idx = tid + kWideThreads * u;
-      const int kv = key0 + 8 * v_chunk(idx);
-      if (kv + 8 > k1) {  // V of keys past the split end must be 0 (0 * NaN would poison O)
-        st.v[u].x &= keep2(kv + 0, k1); st.v[u].y &= keep2(kv + 2, k1);
-        st.v[u].z &= keep2(kv + 4, k1); st.v[u].w &= keep2(kv + 6, k1);
+      const int kv = key0 + 16 * u + 8 * vhalf;
+      if (kv + 8 > k1) {
+        uint4* p = reinterpret_cast<uint4*>(st + kVBytes0 + 4096 * u + 1024 * wave + 16 * lane);
+        uint4 v = *p;
+        v.x &= keep2(kv + 0, k1); v.y &= keep2(kv + 2, k1);
+        v.z &= keep2(kv + 4, k1); v.w &= keep2(kv + 6, k1);
+        *p = v;
       }
-      *reinterpret_cast<uint4*>(&s_v[buf][v_dim(idx) * kVRow + 8 * v_chunk(idx)]) = st.v[u];
     }
   };
 
@@ -476,62 +549,88 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
   const float tau_raw = kTau / c;
   const int qpos_first = prefix + (tile * kRows) / R;  // position of the tile's first token
   const int kperm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);  // pi(m): swap bits 2, 3
+  // Operand read offsets in a stage: K chunk half*8 + ks of row kperm is at
+  // k_off ^ (ks << 4); V^T of dim 32 dt + col, keys 16 s16 + 8 half at
+  // v_off + 1024 dt + 4096 s16.
+  const int k_off = kperm * 256 + ((half ^ ((kperm >> 3) & 1)) << 7) + ((kperm & 7) << 4);
+  const int v_off = kVBytes0 + col * 32 + ((half ^ ((col >> 3) & 1)) << 4);
 
-  auto qk = [&](int buf) -> f32x16_t {
-    const uint16_t* kr = &s_k[buf][kperm * kKRow + half * 64];
-    uint4 kop[8];
+  auto read_k = [&](const uint8_t* st, uint4 (&kop)[8]) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kop[ks] = ld16(kr + 8 * ks);
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = *reinterpret_cast<const uint4*>(st + (k_off ^ (ks << 4)));
+  };
+  auto qk = [&](const uint4 (&kop)[8]) -> f32x16_t {
     f32x16_t acc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(kop[ks], qv[ks], acc);
     return acc;
   };
 
-  // Pipeline (iteration i): scores of step i+1 are issued from LDS stage
-  // (i+1)%3, then the softmax and PV of step i (its scores came one iteration
-  // earlier), then registers of step i+2 go to LDS stage (i+2)%3 (last read in
-  // iteration i-1) and that register slot is refilled with step i+5.  One
-  // barrier per step.  Loads are clamped to the last step, never skipped.
-  Stage st0, st1, st2;
-  fetch(st0, 0);
-  fetch(st1, min(1, nsteps - 1));
-  fetch(st2, min(2, nsteps - 1));
-  store(st0, 0, 0);
-  fetch(st0, min(3, nsteps - 1));
-  store(st1, min(1, nsteps - 1), 1);
-  fetch(st1, min(4, nsteps - 1));
-  __syncthreads();
+  // Pipeline: iteration i issues the loads of step i+3 into the stage step i-1
+  // used and looks up the tiles of step i+4, computes step i (its scores came
+  // one iteration earlier) beside the scores of step i+1, then waits for its
+  // own loads of step i+2 and meets the others at the barrier, after which
+  // step i+2 is readable.  Loads are clamped to the last step, never skipped,
+  // so every lane has exactly 4 loads per step in flight and vmcnt(4) means
+  // "all but the latest step".
+  dma_step(s_st0, half_bases(0));
+  dma_step(s_st1, half_bases(min(1, nsteps - 1)));
+  dma_step(s_st2, half_bases(min(2, nsteps - 1)));
+  HalfBases next_hb = half_bases(min(3, nsteps - 1));
+  __builtin_amdgcn_s_waitcnt(kWaitVm4);
+  fix_tail(s_st0, 0);
+  if (nsteps > 1) fix_tail(s_st1, 1);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  stage_barrier();
   f32x16_t s_cur = f32x16_t{};
-  if (tile_ok) s_cur = qk(0);
-  // buf holds step i, nbuf step i+1 (stale past the last step: its scores go unused)
-  auto iter = [&](int i, int buf, int nbuf, int sbuf, Stage& sst) {
+  if (tile_ok) {
+    uint4 kop[8];
+    read_k(s_st0, kop);
+    s_cur = qk(kop);
+  }
+  // st: step i (V), nst: step i+1 (K), fst: step i+2 (landing), lst: step i+3 (issued now)
+  auto iter = [&](int i, const uint8_t* st, const uint8_t* nst, uint8_t* fst, uint8_t* lst) {
+    dma_step(lst, next_hb);
     if (tile_ok && i < nsteps) {
       const int key0 = k0 + i * kStep;
       const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= qpos_first;
+      uint4 kop[8];
+      read_k(nst, kop);
       float sv[16];
       softmax_max(rs, s_cur, full, key0, k1, qpos, half, c, tau_raw, sv);
-      // next step's scores, issued beside this step's exponentials (independent work in one block)
-      const f32x16_t s_next = qk(nbuf);
+      const f32x16_t s_next = qk(kop);
       uint4 pb[2];
       softmax_exp(rs, sv, c, pb);
 #pragma unroll
       for (int s16 = 0; s16 < 2; ++s16) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt)
-          rs.o[dt] = mfma32(ld16(&s_v[buf][(32 * dt + col) * kVRow + 16 * s16 + 8 * half]), pb[s16], rs.o[dt]);
+          rs.o[dt] = mfma32(*reinterpret_cast<const uint4*>(st + v_off + 1024 * dt + 4096 * s16), pb[s16], rs.o[dt]);
+      }
+      // Issue order of this block: one MFMA, then three VALU instructions, 16
+      // times.  The score MFMAs of step i+1 (a dependent chain) are ready first
+      // and fill the early MFMA slots, so their latency hides behind the
+      // exponentials instead of stalling the wave after them.
+#pragma unroll
+      for (int gidx = 0; gidx < 16; ++gidx) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
       }
       s_cur = s_next;
     }
-    store(sst, min(i + 2, nsteps - 1), sbuf);
-    fetch(sst, min(i + 5, nsteps - 1));
-    __syncthreads();
+    next_hb = half_bases(min(i + 4, nsteps - 1));
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    if (i + 2 < nsteps) fix_tail(fst, i + 2);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    stage_barrier();
   };
-  for (int base = 0; base < nsteps; base += kRing) {
-    iter(base, 0, 1, 2, st2);
-    iter(base + 1, 1, 2, 0, st0);
-    iter(base + 2, 2, 0, 1, st1);
+  for (int base = 0; base < nsteps; base += kWideRing) {
+    iter(base, s_st0, s_st1, s_st2, s_st3);
+    iter(base + 1, s_st1, s_st2, s_st3, s_st0);
+    iter(base + 2, s_st2, s_st3, s_st0, s_st1);
+    iter(base + 3, s_st3, s_st0, s_st1, s_st2);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no direct load outlives the workgroup's LDS
   if (!tile_ok) return;
   write_rows<R>(a, rs, half, row_ok, qrow, g, hh, sp, ns, c);
 }
