@@ -150,26 +150,30 @@ def test_chunk_block_permutation_bit_identical_and_deterministic():
     assert np.array_equal(a, call(pool2, dev_i32(bt2[w.num_decode:])))
 
 
-def test_chunk_ignores_garbage_past_the_context():
-    spec = _chunk_spec("cgarb", 724, 16, 8, 16, [(10, 7), (50, 30), (0, 3)], 40)
+@pytest.mark.parametrize("bs", [16, 32, 64, 256])
+def test_chunk_ignores_garbage_past_the_context(bs):
+    """Every cache slot outside the attended keys holds the sentinel (a NaN):
+    split ends inside a block, keys past a wide split's end and the unused
+    slots of the last block must not reach the output, at every block size."""
+    spec = _chunk_spec(f"cgarb-{bs}", 724, 16, 8, bs, [(10, 7), (50, 30), (0, 3)], 40)
     w = make_step(spec)
     run = StepRun(w, fill_prefix=False)
     s = w.spec
-    k = np.full((s.num_blocks, 16, 8, 128), SENTINEL, dtype=np.uint16)
+    k = np.full((s.num_blocks, bs, 8, 128), SENTINEL, dtype=np.uint16)
     v = k.copy()
     for row in range(w.num_chunks):
         L = int(w.chk_ctx[row]) - int(np.diff(w.chk_qsl)[row])
         for j in range(L):
-            blk, off = w.block_tables[row, j // 16], j % 16
+            blk, off = w.block_tables[row, j // bs], j % bs
             k[blk, off] = w.prefix_k[blk, off]
             v[blk, off] = w.prefix_v[blk, off]
     run.pool.fill_logical(k.view(np.int16), v.view(np.int16))
     run.write()
     q = run.chunk_q()
-    for split in (None, 64):
-        plan = None if split is None else pg.ChunkPlan(64, 2, 0, 0)
+    for split in (None, 32, 64):
+        plan = None if split is None else pg.ChunkPlan(max(split, bs), -(-80 // split), split, 0)
         out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 30, 80, SCALE, plan=plan)
-        compare(out, run.oracle_chunk_on_gpu_inputs(q), f"chunk garbage split={split}")
+        compare(out, run.oracle_chunk_on_gpu_inputs(q), f"chunk garbage bs={bs} split={split}")
 
 
 def test_chunk_bad_metadata_flags_and_zero_rows():
