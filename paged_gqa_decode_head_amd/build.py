@@ -28,6 +28,10 @@ COMMON = [
 ]
 # Packed fp32 VALU forms are kept out of the device code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-file device options.  chunk.hip: MFMA accumulators in VGPRs rather than
+# AGPRs (the narrow kernel otherwise copies them between the register files
+# around every softmax rescale).
+EXTRA = {"chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -40,7 +44,7 @@ def hipcc() -> str:
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     path = os.path.join(CSRC, src)
-    cmd = [hipcc(), *COMMON, *DEVICE, "-c", path, "-o", obj]
+    cmd = [hipcc(), *COMMON, *DEVICE, *EXTRA.get(src, []), "-c", path, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:

@@ -25,8 +25,8 @@
 //   * narrow (at most 32 rows per kv head: verify rows, decode-like rows).  Item =
 //     (segment, g, key split), one wave, many short splits.  V^T is loaded from
 //     the cache straight into the MFMA operand registers (whole 128-byte lines per
-//     load); K goes through a per-wave LDS tile to reach the operand layout.
-//     HBM-bound.
+//     load); K goes through a per-wave LDS ring (direct loads) to reach the operand
+//     layout.  HBM-bound.
 // Splits are merged by a log-sum-exp combine kernel when a row has several.
 //
 // Operand layouts (verified on the hardware): lane l supplies A[m][k] with
@@ -43,8 +43,8 @@
 //   * dims of the S product are split between the lane halves as
 //     (l/32)*64 + 8*kstep + j: a lane reads 128 contiguous bytes of its q row.
 //   * LDS operand reads are conflict-free: the 16 lanes of each read phase hit
-//     16 different 4-bank groups (wide kernel: XOR-swizzled stages, which direct
-//     loads can fill; narrow kernel: K rows padded to 272 bytes).
+//     16 different 4-bank groups of the XOR-swizzled stages, which direct
+//     global->LDS loads can fill.
 #include <math.h>
 
 #include "device_common.hpp"
@@ -58,8 +58,6 @@ constexpr int kRows = 32;                // query rows per tile (one wave)
 constexpr int kWideTiles = 4;            // row tiles (waves) of a wide item
 constexpr int kWideThreads = 64 * kWideTiles;
 constexpr int kStep = 32;                // keys per step
-constexpr int kKRow = 136;               // narrow: LDS K row stride in bf16 (128 + 8 padding)
-constexpr int kKStage = kStep * kKRow;   // narrow: bf16 elements of the per-wave K tile
 constexpr int kMaxBlockIds = 4096 / 16 + 1;  // block ids one split can touch
 constexpr int kCombineRows = 8;          // rows per combine workgroup (32 lanes each)
 constexpr int kCombineParts = kRows / kCombineRows;
@@ -422,6 +420,7 @@ __device__ __forceinline__ void dma16(const uint16_t* src, uint8_t* dst) {
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr int kWaitVm4 = 0x0F74;      // vmcnt(4)
+constexpr int kWaitVm16 = 0x4F70;     // vmcnt(16)
 constexpr int kWaitVm0 = 0x0F70;      // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;    // lgkmcnt(0)
 
@@ -637,12 +636,19 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
 
 // ---------------------------------------------------------------- narrow kernel
 // One wave per (segment, kv head, split) of a segment with at most 32 rows per
-// kv head.  Per 32-key step: K as 8 loads of 4 whole rows each (-> LDS ->
-// operand rows pi(m)), V^T as 8 loads straight into the PV operand registers;
-// two steps of loads in flight.
+// kv head.  Each 32-key step arrives by 16 direct global->LDS loads (K: 8 loads
+// of 4 whole rows; V^T: 8 loads of 32 dims of one 16-key piece) into a 2-stage
+// per-wave ring with the wide kernel's layout and swizzle, and is read back in
+// operand order.  Two steps of loads are in flight.  A workgroup is one wave, so
+// the wave's own waits are the only synchronisation.
+//
+// The 33 KB ring allows 4 such workgroups per CU (one wave per SIMD).  This file
+// is compiled with the MFMA VGPR form (build option), which keeps the
+// accumulators in ordinary VGPRs (178 in all), so the softmax rescale and the
+// epilogue touch them without copies between the two register files.
 template <int R>
 __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkArgs a) {
-  const Located loc = locate<kShortList>(a, pool, blockIdx.x, R);
+  const Located loc = wave_uniform(locate<kShortList>(a, pool, blockIdx.x, R));
   if (loc.item.x < 0) return;
   const SegInfo& si = loc.si;
   const int s = loc.item.x, g = loc.item.y, sp = loc.item.w;
@@ -653,7 +659,9 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
     return;
   }
 
-  __shared__ __align__(16) uint16_t s_k[kKStage];
+  // Two separate arrays so the compiler tells the stages apart (see the wide kernel).
+  __shared__ __align__(1024) uint8_t s_n0[kStageBytes];
+  __shared__ __align__(1024) uint8_t s_n1[kStageBytes];
   __shared__ int32_t s_blk[kMaxBlockIds];
 
   const int prefix = si.n - si.qlen;
@@ -674,26 +682,36 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
   load_q(qv, a, row_ok, qrow, g * R + hh, half);
   __syncthreads();
 
+  // Splits start at multiples of 32 keys: each 16-key half of a step lies in one
+  // block (see the wide kernel).  K load u (rows 4u + lane/16, stage bytes 1024 u)
+  // reads half u / 4; V load u (dims 32 (u % 4) + lane/2 of piece u / 4, stage
+  // bytes 8192 + 1024 u) reads half u / 4.
   const int tshift = lbs + 8;
-  struct Stage {
-    uint4 k[8], v[8];
-  };
-  // K load u: key 4u + lane/16 of the step, 16-byte chunk lane%16.
-  // V load 2dt + s16: dim 32dt + col, keys 16 s16 + 8 half .. +7.
-  auto fetch = [&](Stage& st, int step) {
+  uint32_t koff[4];  // bytes from the K row of the half's first key, for u % 4
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int kr = 4 * u + (lane >> 4);
+    koff[u] = uint32_t((kr * kHeadDim + ((lane & 15) ^ kr) * 8) * 2);
+  }
+  const int vdim = lane >> 1;                     // + 32 (u % 4)
+  const int vhalf = (lane & 1) ^ ((vdim >> 3) & 1);  // the lane's 8-key half of the piece
+  const uint32_t voff = uint32_t((bs * kHeadDim + vdim * kVSub + 8 * vhalf) * 2);
+  const uint8_t* kv_bytes = reinterpret_cast<const uint8_t*>(pool.kv);
+  auto fetch = [&](uint8_t* st, int step) {
     const int key0 = k0 + step * kStep;
+    const uint8_t* hb[2];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int kk = min(key0 + 4 * u + (lane >> 4), k1 - 1);
-      st.k[u] = ld16(pool.kv + (int64_t(s_blk[(kk >> lbs) - b0]) << tshift) + (kk & (bs - 1)) * kHeadDim +
-                     (lane & 15) * 8);
+    for (int h = 0; h < 2; ++h) {
+      const int hk = min(key0 + 16 * h, k1 - 1) & ~15;
+      const int blk = __builtin_amdgcn_readfirstlane(s_blk[(hk >> lbs) - b0]);
+      hb[h] = kv_bytes + ((int64_t(blk) << tshift) + (hk & (bs - 1)) * kHeadDim) * 2;
     }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this stage's operand reads are complete
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int dt = u >> 1, s16 = u & 1;
-      const int kv = min(key0 + 16 * s16 + 8 * half, k1 - 1) & ~7;
-      st.v[u] = ld16(pool.kv + (int64_t(s_blk[(kv >> lbs) - b0]) << tshift) + v_elem(bs, kv & (bs - 1), 32 * dt + col));
-    }
+    for (int u = 0; u < 8; ++u) dma16(reinterpret_cast<const uint16_t*>(hb[u >> 2] + koff[u & 3]), st + 1024 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      dma16(reinterpret_cast<const uint16_t*>(hb[u >> 2] + voff + 32 * kVSub * 2 * (u & 3)), st + kVBytes0 + 1024 * u);
   };
 
   RowState rs;
@@ -704,44 +722,50 @@ __global__ __launch_bounds__(64) void chunk_narrow_kernel(PoolGeom pool, ChunkAr
   const float c = a.qk_scale_log2;
   const float tau_raw = kTau / c;
   const int kperm = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  const int k_off = kperm * 256 + ((half ^ ((kperm >> 3) & 1)) << 7) + ((kperm & 7) << 4);
+  const int v_off = kVBytes0 + col * 32 + ((half ^ ((col >> 3) & 1)) << 4);
 
-  auto step = [&](Stage& st, int i) {
+  // Step i: wait for its loads (the 16 of step i+1 may stay in flight), scores,
+  // softmax and PV.  Loads are clamped to the last step.
+  auto step = [&](const uint8_t* st, int i) {
     const int key0 = k0 + i * kStep;
-    __syncthreads();  // the previous step's reads of s_k are done
+    __builtin_amdgcn_s_waitcnt(kWaitVm16);
+    if (key0 + kStep > k1) {
+      // V of keys past the split end must be 0 (0 * NaN would poison O): each
+      // lane clears its own chunks of the split's last step in the stage.
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<uint4*>(&s_k[(4 * u + (lane >> 4)) * kKRow + (lane & 15) * 8]) = st.k[u];
-    __syncthreads();
-    const uint16_t* kr = &s_k[kperm * kKRow + half * 64];
+      for (int u = 0; u < 8; ++u) {
+        const int kv = key0 + 16 * (u >> 2) + 8 * vhalf;
+        if (kv + 8 > k1) {
+          uint4* p = reinterpret_cast<uint4*>(const_cast<uint8_t*>(st) + kVBytes0 + 1024 * u + 16 * lane);
+          uint4 v = *p;
+          v.x &= keep2(kv + 0, k1); v.y &= keep2(kv + 2, k1);
+          v.z &= keep2(kv + 4, k1); v.w &= keep2(kv + 6, k1);
+          *p = v;
+        }
+      }
+    }
     uint4 kop[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kop[ks] = ld16(kr + 8 * ks);
+    for (int ks = 0; ks < 8; ++ks) kop[ks] = *reinterpret_cast<const uint4*>(st + (k_off ^ (ks << 4)));
     f32x16_t sacc = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) sacc = mfma32(kop[ks], qv[ks], sacc);
-    // V of keys past the split end must be 0: 0 * NaN would poison O.
-    if (key0 + kStep > k1) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int kv = key0 + 16 * (u & 1) + 8 * half;
-        st.v[u].x &= keep2(kv + 0, k1); st.v[u].y &= keep2(kv + 2, k1);
-        st.v[u].z &= keep2(kv + 4, k1); st.v[u].w &= keep2(kv + 6, k1);
-      }
-    }
     const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= prefix;
-    softmax_pv(rs, sacc, full, key0, k1, qpos, half, c, tau_raw,
-               [&](int dt, int s16) { return st.v[2 * dt + s16]; });
+    softmax_pv(rs, sacc, full, key0, k1, qpos, half, c, tau_raw, [&](int dt, int s16) {
+      return *reinterpret_cast<const uint4*>(st + v_off + 1024 * dt + 4096 * s16);
+    });
   };
 
-  Stage st0, st1;
-  fetch(st0, 0);
-  fetch(st1, min(1, nsteps - 1));
+  fetch(s_n0, 0);
+  fetch(s_n1, min(1, nsteps - 1));
   for (int base = 0; base < nsteps; base += 2) {
-    step(st0, base);
-    fetch(st0, min(base + 2, nsteps - 1));
-    if (base + 1 < nsteps) step(st1, base + 1);
-    fetch(st1, min(base + 3, nsteps - 1));
+    step(s_n0, base);
+    fetch(s_n0, min(base + 2, nsteps - 1));
+    if (base + 1 < nsteps) step(s_n1, base + 1);
+    fetch(s_n1, min(base + 3, nsteps - 1));
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no direct load outlives the workgroup's LDS
   write_rows<R>(a, rs, half, row_ok, qrow, g, hh, sp, ns, c);
 }
 
