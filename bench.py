@@ -137,7 +137,9 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
         rows["decode"][name] = {"batch": w.num_decode, "keys": int(w.dec_ctx.sum()), "us": round(med, 2),
                                 "alg_bytes": nb, "gbs": round(nb / med / 1e3, 1),
                                 "frac_hbm_peak": round(nb / med / 1e3 / HBM_PEAK_GBS, 4),
-                                "plan": [plan.split_tokens, plan.max_splits, plan.waves_per_split]}
+                                "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
+                                         "waves": plan.waves_per_split,
+                                         "kernel": "mfma" if plan.kernel == 2 else "dot"}}
         if name == "cfg5":
             qc = q_out[w.chk_tok0:].contiguous()
             res = {}
@@ -692,7 +694,8 @@ def main():
             "head_dim": 128, "block_size": s.block_size, "context_tokens": int(w.dec_ctx.sum()),
             "layers_cycled": args.layers,
             "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
-                     "waves_per_split": plan.waves_per_split},
+                     "waves_per_split": plan.waves_per_split,
+                     "kernel": "mfma" if plan.kernel == 2 else "dot"},
         },
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_decode / (ms_step * 1e-3), 1),

@@ -156,7 +156,11 @@ typedef struct {
   int32_t split_tokens;     /* keys per split: a multiple of max(block_size, 64), <= 1024 * waves_per_split */
   int32_t max_splits;       /* ceil(max_context_len / split_tokens) */
   int32_t waves_per_split;  /* 64-lane waves per workgroup: 1, 2, 4 or 8 */
-  int32_t load_hint;        /* K/V loads: 0 library default (streaming), 1 cached, 2 streaming (non-temporal) */
+  int32_t load_hint;        /* K/V loads: 0 library default (streaming in the dot-product kernel, cached in
+                               the matrix-core kernel), 1 cached, 2 streaming (non-temporal) */
+  int32_t kernel;           /* split kernel: 0 library default (matrix-core when 8 or more query heads share
+                               a kv head, else dot-product), 1 dot-product (VALU) kernel, 2 matrix-core
+                               (MFMA) kernel.  Both give the same results up to rounding. */
 } pgqa_decode_plan;
 
 /* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,

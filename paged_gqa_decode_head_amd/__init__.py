@@ -44,11 +44,11 @@ class PoolConfig(ctypes.Structure):
 
 class DecodePlan(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("waves_per_split", ctypes.c_int32), ("load_hint", ctypes.c_int32)]
+                ("waves_per_split", ctypes.c_int32), ("load_hint", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"DecodePlan(split_tokens={self.split_tokens}, max_splits={self.max_splits}, "
-                f"waves_per_split={self.waves_per_split}, load_hint={self.load_hint})")
+                f"waves_per_split={self.waves_per_split}, load_hint={self.load_hint}, kernel={self.kernel})")
 
 
 class ChunkPlan(ctypes.Structure):

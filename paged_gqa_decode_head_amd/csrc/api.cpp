@@ -107,12 +107,22 @@ pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t
     return fail(PGQA_ERR_INVALID_ARG, "plan.split_tokens=%d exceeds 1024 keys per wave (%d waves)", p.split_tokens,
                 p.waves_per_split);
   if (p.load_hint < 0 || p.load_hint > 2) return fail(PGQA_ERR_INVALID_ARG, "plan.load_hint=%d", p.load_hint);
+  if (p.kernel < 0 || p.kernel > 2) return fail(PGQA_ERR_INVALID_ARG, "plan.kernel=%d (0, 1 or 2)", p.kernel);
   const int64_t need = (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens;
   if (p.max_splits < need || p.max_splits > 65535)
     return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
                 max_context_len);
   return PGQA_OK;
 }
+
+// Split kernel of a decode plan with kernel = 0, by query heads per kv head.
+// The dot-product kernel's VALU work per key grows with r while its bytes per
+// key do not.  Measured on MI355X at r = 8 the matrix-core kernel is 24-32%
+// faster (Qwen3-30B-A3B batch-64 step 29.8 -> 22.9 us; batch 1 at 32k keys
+// 35.8 -> 24.4; batch 8 at up to 4k keys 20.9 -> 16.0); at r <= 4 the two are
+// within a few percent and the dot-product kernel is ahead on the large
+// batches, which stream at close to the memory system's rate.
+int32_t default_decode_kernel(int32_t r) { return r >= 8 ? 2 : 1; }
 
 // Rotary turn frequencies of rope_theta (host fp64), cached in the pool.
 void rope_table(pgqa_pool* pool, double rope_theta, double (&out)[64]) {
@@ -343,10 +353,12 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   //  * otherwise about one workgroup per CU, with splits of at least 1024 keys
   //    (1536 for contexts of 16k keys or more: the batch-1 32k-key step is
   //    fastest at 1536-key splits, 176 workgroups, 6% ahead of 2048);
-  //  * 8 waves per workgroup when 8 query heads share a kv head (more dot
-  //    products per byte), else 4.
+  //  * 4 waves per workgroup;
+  //  * the matrix-core kernel (8 query heads per kv head) was fastest with
+  //    512-key splits below 16k keys (its workgroups start up faster).
   const int32_t r = num_q_heads / num_kv_heads;
-  const int32_t waves = r >= 8 ? 8 : 4;
+  const int32_t kernel = default_decode_kernel(r);
+  const int32_t waves = 4;
   const int64_t gran = block_size > 64 ? block_size : 64;
   const int64_t units = int64_t(batch > 0 ? batch : 1) * num_kv_heads;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
@@ -357,7 +369,7 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   } else {
     const int64_t want = (num_cus + units - 1) / units;
     split = round_up((ctx + want - 1) / want, gran);
-    const int64_t floor_split = round_up(ctx >= 16384 ? 1536 : 1024, gran);
+    const int64_t floor_split = round_up(ctx >= 16384 ? 1536 : kernel == 2 ? 512 : 1024, gran);
     if (split < floor_split) split = floor_split;
     if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
   }
@@ -369,6 +381,7 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   out->max_splits = int32_t((ctx + split - 1) / split);
   out->waves_per_split = waves;
   out->load_hint = 0;
+  out->kernel = kernel;
   return PGQA_OK;
 }
 
@@ -439,7 +452,11 @@ pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, 
   a.split_tokens = p.split_tokens;
   a.max_splits = p.max_splits;
   a.waves = p.waves_per_split;
-  a.stream_loads = p.load_hint != 1;
+  a.mfma = (p.kernel == 0 ? default_decode_kernel(r) : p.kernel) == 2;
+  // load_hint 0: streaming loads in the dot-product kernel (whole lines, read
+  // once), cached loads in the matrix-core kernel (each K line is read by two
+  // load instructions; measured faster cached at every workload).
+  a.stream_loads = p.load_hint == 2 || (p.load_hint == 0 && !a.mfma);
   char* ws = wl.total > 0 ? static_cast<char*>(workspace) : nullptr;
   a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;

@@ -69,6 +69,67 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Merge the W waves' online-softmax states of one (sequence b, kv head g,
+// split sp), left in LDS by each wave (max m, weight sum l and unnormalised
+// accumulator per query head), and store the result: bf16 rows when the
+// sequence has one split, else the normalised partial and its lse (log2 units)
+// for the combine.  Thread i handles (head, dim) pairs i, i + 64 W, ...
+template <int R, int W>
+__device__ __forceinline__ void merge_waves(const float (&s_m)[W][R], const float (&s_l)[W][R],
+                                            const float (&s_acc)[W][R][kHeadDim], const DecodeArgs& a, int b, int g,
+                                            int sp, bool single, int hkv, uint16_t* out_bg) {
+  constexpr int kPairs = R * kHeadDim;
+  float* po = a.part_o + ((int64_t(b) * hkv + g) * a.max_splits + sp) * kPairs;
+  float* plse = a.part_lse + ((int64_t(b) * hkv + g) * a.max_splits + sp) * R;
+  for (int idx = threadIdx.x; idx < kPairs; idx += 64 * W) {
+    const int h = idx >> 7, d = idx & (kHeadDim - 1);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < W; ++w) {
+        const float e = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - M);
+        L += e * s_l[w][h];
+        A += e * s_acc[w][h][d];
+      }
+    }
+    const float o = L > 0.f ? A / L : 0.f;
+    if (single) {
+      out_bg[idx] = f32_to_bf16(o);
+    } else {
+      po[idx] = o;
+      if (d == 0) plse[h] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    }
+  }
+}
+
+// Fused step: the cache write of the new token of kv head g (position n - 1)
+// into block blk, from LDS rows holding its normed, rotated k and its raw v.
+// Called by lanes sub = 0..7 of one wave; lane sub stores dims 8 sub .. +7 and
+// 64 + 8 sub .. +7.  A block id outside the pool is flagged, nothing written.
+__device__ __forceinline__ void store_new_token(const PoolGeom& pool, int g, int32_t blk, int n, int sub,
+                                                const uint16_t* s_newk, const uint16_t* s_newv) {
+  if (unsigned(blk) < unsigned(pool.num_blocks)) {
+    const int bs = pool.block_size;
+    const int off = (n - 1) & (bs - 1);
+    uint16_t* tile = pool.kv + (int64_t(blk) * pool.num_kv_heads + g) * tile_elems(pool);
+    *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + sub * 8) =
+        *reinterpret_cast<const uint4*>(&s_newk[8 * sub]);
+    *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + 64 + sub * 8) =
+        *reinterpret_cast<const uint4*>(&s_newk[64 + 8 * sub]);
+    uint16_t* vt = tile + v_elem(bs, off, 0);  // V^T piece [dim][slot % 16]
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      vt[(8 * sub + e) * kVSub] = s_newv[8 * sub + e];
+      vt[(64 + 8 * sub + e) * kVSub] = s_newv[64 + 8 * sub + e];
+    }
+  } else if (sub == 0) {
+    raise_error(pool.err, kErrBlockId);
+  }
+}
+
 template <int R, int W, bool kStream, bool kFused>
 __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a, StepArgs st) {
   // grid (kv head, sequence, split): the split index varies slowest, so every
@@ -187,27 +248,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   // The slot write of the new token, from the LDS rows, after the tile loop.
   auto fused_epilogue = [&]() {
     if constexpr (kFused) {
-      if (writer) {
+      if (writer && lane < 8) {
         // block id of the token's slot: this wave's tile patch_tile / W
-        const int32_t blk = __builtin_amdgcn_readlane(lane_blk, patch_tile / W);
-        if (lane < 8) {
-          if (unsigned(blk) < unsigned(pool.num_blocks)) {
-            const int off = (n - 1) & (bs - 1);
-            uint16_t* tile = pool.kv + (int64_t(blk) * hkv + g) * tile_elems(pool);
-            *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + sub * 8) =
-                *reinterpret_cast<const uint4*>(&s_newk[8 * sub]);
-            *reinterpret_cast<uint4*>(tile + int64_t(off) * kHeadDim + 64 + sub * 8) =
-                *reinterpret_cast<const uint4*>(&s_newk[64 + 8 * sub]);
-            uint16_t* vt = tile + v_elem(bs, off, 0);  // V^T piece [dim][slot % 16]
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              vt[(8 * sub + e) * kVSub] = s_newv[8 * sub + e];
-              vt[(64 + 8 * sub + e) * kVSub] = s_newv[64 + 8 * sub + e];
-            }
-          } else if (sub == 0) {
-            raise_error(pool.err, kErrBlockId);
-          }
-        }
+        store_new_token(pool, g, __builtin_amdgcn_readlane(lane_blk, patch_tile / W), n, sub, s_newk, s_newv);
       }
     }
   };
@@ -419,34 +462,353 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     }
   }
   __syncthreads();
+  merge_waves<R, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, out_bg);
+}
 
-  // Merge the W waves: thread handles (head, dim) pairs.
-  constexpr int kPairs = R * kHeadDim;
-  const bool single = ns == 1;
-  float* po = a.part_o + ((int64_t(b) * hkv + g) * a.max_splits + sp) * kPairs;
-  float* plse = a.part_lse + ((int64_t(b) * hkv + g) * a.max_splits + sp) * R;
-  for (int idx = tid; idx < kPairs; idx += 64 * W) {
-    const int h = idx >> 7, d = idx & (kHeadDim - 1);
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) M = fmaxf(M, s_m[w][h]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < W; ++w) {
-        const float e = s_m[w][h] == -INFINITY ? 0.f : fast_exp2(s_m[w][h] - M);
-        L += e * s_l[w][h];
-        A += e * s_acc[w][h][d];
-      }
+// ---------------------------------------------------------------------------
+// Matrix-core split kernel.  When several query heads share a kv head, the
+// per-key dot products of the kernel above grow with the group size r while
+// the bytes per key stay fixed; here both products of a 32-key step run on
+// v_mfma_f32_16x16x32_bf16 instead, with the r query heads as MFMA columns
+// (columns r..15 hold zero q and are discarded).  Same work unit, split plan,
+// partial layout and combine as the kernel above.
+//
+// Operand layouts: lane l supplies A[m][k] with m = l%16, k = 8(l/16) + j and
+// B[k][n] with n = l%16; D[j] of lane l is row 4(l/16) + j, column l%16.
+// With c = l/16 and col = l%16:
+//   * S^T = K Q^T, two products per step (u = 0, 1), four 32-dim slices each
+//     (k of slice s is dim 32s + k).  Row m of product u is key
+//     8(m/4) + 4u + m%4 of the step, so D[j] of product u in lane l is key
+//     8c + 4u + j: the lane's 8 weights are keys 8c .. 8c+7 in order.
+//   * O^T += V^T P^T, eight products (dims 16t .. 16t+15), k = key of the step:
+//     the weights above are exactly the lane's B operand, and its A operand
+//     (dim 16t + col, keys 8c .. 8c+7) is 16 contiguous bytes of a 16-slot V^T
+//     piece.  Nothing is transposed or exchanged between lanes.
+// Each wave takes every W-th 32-key step of the split and keeps the next
+// step's 16 loads in flight while it computes the current one.  At most 256
+// registers per lane, so that two waves share each SIMD at every W.
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Component-wise select.  (A ternary on uint4 values can become a select
+// between their addresses, which keeps the operands out of registers.)
+__device__ __forceinline__ uint4 sel4(bool p, const uint4& x, const uint4& y) {
+  return make_uint4(p ? x.x : y.x, p ? x.y : y.y, p ? x.z : y.z, p ? x.w : y.w);
+}
+
+struct MStep {
+  uint4 k[2][4];  // score product u, dim slice s: key row of the lane, dims 32s + 8c .. +7
+  uint4 v[8];     // PV product t: dim 16t + col, keys 8c .. 8c+7
+  int ok;         // bit h: block id of the step's 16-key half h is valid
+};
+
+// kStream: K/V loads carry the non-temporal hint.  A K load instruction covers
+// 64 bytes of each of 16 key rows, so the other half of each 128-byte line
+// comes with the next instruction; with cached loads (the default for this
+// kernel) it hits in L2.
+template <int R, int W, bool kStream, bool kFused>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(PoolGeom pool,
+                                                                                                  DecodeArgs a,
+                                                                                                  StepArgs st) {
+  static_assert(R <= 16, "query heads per kv head exceed the MFMA columns");
+  const int g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, c = lane >> 4;
+  const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
+
+  __shared__ float s_m[W][R], s_l[W][R];
+  __shared__ __align__(16) float s_acc[W][R][kHeadDim];
+  // fused step: each wave's normed, rotated q rows, and the new token's k and v
+  __shared__ __align__(16) uint16_t s_q[kFused ? W : 1][kFused ? R : 1][kHeadDim];
+  __shared__ __align__(16) uint16_t s_newk[kFused ? kHeadDim : 1];
+  __shared__ __align__(16) uint16_t s_newv[kFused ? kHeadDim : 1];
+
+  // Context length, block ids and q issued together.  Lane i fetches the block
+  // id of half (i & 1) of the wave's step i / 2 (step wave + (i / 2) W of the
+  // split); the plan bounds a wave's steps by 32.
+  const int n = a.ctx[b];
+  const int k0 = sp * a.split_tokens;
+  int32_t lane_blk = -1;
+  {
+    const int off = (wave + (lane >> 1) * W) * 32 + (lane & 1) * 16;
+    const int64_t entry = (int64_t(k0) + off) / bs;
+    if (off < a.split_tokens && entry < a.bt_stride) lane_blk = a.bt[int64_t(b) * a.bt_stride + entry];
+  }
+  // Plain decode: q^T as the B operand of the score products, column col =
+  // head g R + col (zero past R), dims 32s + 8c .. +7.  Fused step: lanes
+  // 8h + sub (h < R) hold dims 8 sub .. and 64 + 8 sub .. of the raw q row of
+  // head g R + h (the layout of the shared norm + rotary code); lanes 0..7 also
+  // fetch the new token's raw k, v and the k norm weight.
+  uint4 qb[4];
+  uint4 qx, qy, nk0, nk1, nv0, nv1, nw0, nw1;
+  const int sub = lane & 7;
+  if constexpr (kFused) {
+    if (lane < 8 * R) {
+      const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + (lane >> 3)) * kHeadDim + 8 * sub;
+      qx = *reinterpret_cast<const uint4*>(qrow);
+      qy = *reinterpret_cast<const uint4*>(qrow + 64);
     }
-    const float o = L > 0.f ? A / L : 0.f;
-    if (single) {
-      out_bg[idx] = f32_to_bf16(o);
-    } else {
-      po[idx] = o;
-      if (d == 0) plse[h] = L > 0.f ? M + __log2f(L) : -INFINITY;
+    if (lane < 8) {
+      const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
+      const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
+      nk0 = *reinterpret_cast<const uint4*>(kr);
+      nk1 = *reinterpret_cast<const uint4*>(kr + 64);
+      nv0 = *reinterpret_cast<const uint4*>(vr);
+      nv1 = *reinterpret_cast<const uint4*>(vr + 64);
+      nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
+      nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
+    }
+  } else {
+    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + (col < R ? col : 0)) * kHeadDim + 8 * c;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      qb[s] = sel4(col < R, *reinterpret_cast<const uint4*>(qrow + 32 * s), make_uint4(0u, 0u, 0u, 0u));
     }
   }
+
+  const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;
+  uint16_t* out_bg = a.out + (int64_t(b) * hq + g * R) * kHeadDim;
+  if (bad_ctx || n == 0) {
+    if (sp == 0) {
+      if (bad_ctx && tid == 0) raise_error(pool.err, kErrContext);
+      for (int i = tid; i < R * kHeadDim; i += 64 * W) out_bg[i] = 0;
+    }
+    return;
+  }
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (sp >= ns) return;
+  const int k1 = min(n, k0 + a.split_tokens);
+
+  // Fused step: the new token sits at position n - 1, key o of step
+  // patch_step of the last split.  The wave that computes that step norms and
+  // rotates its k into LDS beside the raw v, substitutes both into the step's
+  // operands, and stores them into the cache slot after its step loop.
+  const int patch_step = kFused && sp == ns - 1 ? (n - 1 - k0) >> 5 : -1;
+  const int o = (n - 1 - k0) & 31;
+  const bool writer = kFused && patch_step >= 0 && wave == patch_step % W;
+  auto fused_prologue = [&]() {
+    if constexpr (kFused) {
+      if (lane < 8 * R) {
+        float cs[8], sn[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rope_angle(n - 1, st.rev_freq[8 * sub + j], cs[j], sn[j]);
+        const uint4 w0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
+        const uint4 w1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
+        const int h = lane >> 3;
+        uint4 o0, o1;
+        norm_rope_lane(qx, qy, w0, w1, cs, sn, st.eps, o0, o1);
+        *reinterpret_cast<uint4*>(&s_q[wave][h][8 * sub]) = o0;
+        *reinterpret_cast<uint4*>(&s_q[wave][h][64 + 8 * sub]) = o1;
+        if (st.q_out != nullptr && sp == 0 && wave == 0) {
+          uint16_t* dst = st.q_out + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 8;
+          *reinterpret_cast<uint4*>(dst) = o0;
+          *reinterpret_cast<uint4*>(dst + 64) = o1;
+        }
+        if (writer && lane < 8) {
+          norm_rope_lane(nk0, nk1, nw0, nw1, cs, sn, st.eps, o0, o1);
+          *reinterpret_cast<uint4*>(&s_newk[8 * sub]) = o0;
+          *reinterpret_cast<uint4*>(&s_newk[64 + 8 * sub]) = o1;
+          *reinterpret_cast<uint4*>(&s_newv[8 * sub]) = nv0;
+          *reinterpret_cast<uint4*>(&s_newv[64 + 8 * sub]) = nv1;
+        }
+      }
+      // the wave's own LDS rows are read back below
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&s_q[wave][col < R ? col : 0][32 * s + 8 * c]);
+        qb[s] = sel4(col < R, x, make_uint4(0u, 0u, 0u, 0u));
+      }
+    }
+  };
+
+  const int64_t tstride = tile_elems(pool);
+  const int64_t bstride = tstride * hkv;
+  const uint16_t* pool_g = pool.kv + int64_t(g) * tstride;
+  const int nsteps = (k1 - k0 + 31) >> 5;
+
+  // Lane offsets inside a 16-key half: K row of product 0 (product 1 is 4 rows
+  // on) in half col / 8; V^T keys 8(c & 1) .. of dim col in half c / 2.
+  const int khalf = col >> 3, vhalf = c >> 1;
+  const int k_off = (8 * ((col >> 2) & 1) + (col & 3)) * kHeadDim + 8 * c;
+  const int v_off = bs * kHeadDim + col * kVSub + 8 * (c & 1);
+
+  auto load = [&](MStep& ms, int i) {
+    const int key = k0 + (wave + i * W) * 32;
+    const int32_t r0 = __builtin_amdgcn_readlane(lane_blk, 2 * i);
+    const int32_t r1 = __builtin_amdgcn_readlane(lane_blk, 2 * i + 1);
+    const bool ok0 = unsigned(r0) < unsigned(pool.num_blocks), ok1 = unsigned(r1) < unsigned(pool.num_blocks);
+    ms.ok = (ok0 ? 1 : 0) | (ok1 ? 2 : 0);
+    const uint16_t* base0 = pool_g + int64_t(ok0 ? r0 : 0) * bstride + ((key & (bs - 1)) >> 4) * (16 * kHeadDim);
+    const uint16_t* base1 =
+        pool_g + int64_t(ok1 ? r1 : 0) * bstride + (((key + 16) & (bs - 1)) >> 4) * (16 * kHeadDim);
+    const uint16_t* kp = (khalf ? base1 : base0) + k_off;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ms.k[u][s] = ld16<kStream>(kp + 4 * u * kHeadDim + 32 * s);
+    }
+    const uint16_t* vp = (vhalf ? base1 : base0) + v_off;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ms.v[t] = ld16<kStream>(vp + 16 * t * kVSub);
+  };
+
+  // Fused step: key o of the step is the new token.  K: the lanes whose row of
+  // product u is key o take their four dim slices from LDS.  V: lanes of group
+  // c = o / 8 replace element o % 8 of their 8 keys in each product's operand
+  // (selects only: a runtime component index would put the step in scratch).
+  auto patch = [&](MStep& ms) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint4 x = *reinterpret_cast<const uint4*>(&s_newk[32 * s + 8 * c]);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // bit masks rather than selects: with selects the compiler kept both
+        // versions of the step's K operands and spilled them
+        const uint32_t nm = 8 * (col >> 2) + 4 * u + (col & 3) == o ? 0xffffffffu : 0u;
+        ms.k[u][s].x = (ms.k[u][s].x & ~nm) | (x.x & nm);
+        ms.k[u][s].y = (ms.k[u][s].y & ~nm) | (x.y & nm);
+        ms.k[u][s].z = (ms.k[u][s].z & ~nm) | (x.z & nm);
+        ms.k[u][s].w = (ms.k[u][s].w & ~nm) | (x.w & nm);
+      }
+    }
+    const bool mine = c == (o >> 3);
+    const int w = (o & 7) >> 1;
+    const uint32_t keep = (o & 1) ? 0x0000ffffu : 0xffff0000u;
+    const int shift = (o & 1) ? 16 : 0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t nv = uint32_t(s_newv[16 * t + col]) << shift;
+      ms.v[t].x = mine && w == 0 ? (ms.v[t].x & keep) | nv : ms.v[t].x;
+      ms.v[t].y = mine && w == 1 ? (ms.v[t].y & keep) | nv : ms.v[t].y;
+      ms.v[t].z = mine && w == 2 ? (ms.v[t].z & keep) | nv : ms.v[t].z;
+      ms.v[t].w = mine && w == 3 ? (ms.v[t].w & keep) | nv : ms.v[t].w;
+    }
+  };
+
+  f32x4_t acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY, l = 0.f;  // of column col; the four lane groups agree on m
+  bool bad_blk = false;
+
+  auto compute = [&](MStep& ms, int i) {
+    const int step = wave + i * W;
+    if constexpr (kFused) {
+      if (step == patch_step) {
+        // an opaque statement keeps this a branch, and its memory clobber keeps
+        // the patch's LDS reads inside it (hoisted out of the step loop they
+        // would hold ~24 registers for the whole loop)
+        asm volatile("" ::: "memory");
+        patch(ms);
+      }
+    }
+    const int key = k0 + step * 32;
+    // a half past the split end is never attended: its block id is not checked
+    bad_blk |= !(ms.ok & 1) || (key + 16 < k1 && !(ms.ok & 2));
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) s0 = mfma16(ms.k[0][s], qb[s], s0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) s1 = mfma16(ms.k[1][s], qb[s], s1);
+    // the lane's keys key + 8c .. +7: how many are attended
+    const bool okc = (ms.ok >> vhalf) & 1;
+    const int nv = okc ? min(max(k1 - (key + 8 * c), 0), 8) : 0;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = j < nv ? s0[j] * a.qk_scale_log2 : -INFINITY;
+      x[4 + j] = 4 + j < nv ? s1[j] * a.qk_scale_log2 : -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mx = fmaxf(mx, x[j]);
+    if (__ballot(mx > m + kTau)) {
+      float tm = fmaxf(mx, __shfl_xor(mx, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      if (tm > m) {
+        const float corr = fast_exp2(m - tm);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] *= corr;
+        l *= corr;
+        m = tm;
+      }
+    }
+    const float mh = m == -INFINITY ? 0.f : m;
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = fast_exp2(x[j] - mh);
+      l += p[j];
+    }
+    const uint4 pb = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                pack_bf16x2(p[6], p[7]));
+    // V of keys that are not attended is zeroed: their weight is 0, but the
+    // slots may hold any bits, and 0 * NaN would poison the accumulator.
+    if (key + 32 > k1 || ms.ok != 3) {
+      const uint32_t m0 = nv > 1 ? 0xffffffffu : nv > 0 ? 0x0000ffffu : 0u;
+      const uint32_t m1 = nv > 3 ? 0xffffffffu : nv > 2 ? 0x0000ffffu : 0u;
+      const uint32_t m2 = nv > 5 ? 0xffffffffu : nv > 4 ? 0x0000ffffu : 0u;
+      const uint32_t m3 = nv > 7 ? 0xffffffffu : nv > 6 ? 0x0000ffffu : 0u;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        ms.v[t].x &= m0;
+        ms.v[t].y &= m1;
+        ms.v[t].z &= m2;
+        ms.v[t].w &= m3;
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = mfma16(ms.v[t], pb, acc[t]);
+  };
+
+  const int my_steps = nsteps > wave ? (nsteps - wave + W - 1) / W : 0;
+  if (my_steps > 0) {
+    auto at = [&](int i) { return min(i, my_steps - 1); };
+    MStep ta, tb;
+    load(ta, 0);
+    fused_prologue();  // fused step: while the first step is in flight
+    for (int i = 0; i < my_steps; i += 2) {
+      load(tb, at(i + 1));
+      compute(ta, i);
+      load(ta, at(i + 2));
+      if (i + 1 < my_steps) compute(tb, i + 1);
+    }
+  }
+  // (wave 0 of split 0 and the writer wave always have steps: q_out and the
+  // new token's slot are written whenever the context is not empty)
+  if constexpr (kFused) {
+    if (writer && lane < 8) {
+      // block id of the token's slot: half o / 16 of this wave's step patch_step / W
+      store_new_token(pool, g, __builtin_amdgcn_readlane(lane_blk, 2 * (patch_step / W) + (o >> 4)), n, sub, s_newk,
+                      s_newv);
+    }
+  }
+  if (bad_blk && lane == 0) raise_error(pool.err, kErrBlockId);
+
+  // Column totals: each lane group summed the weights of its own keys.
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (col < R) {
+    if (c == 0) {
+      s_m[wave][col] = m;
+      s_l[wave][col] = l;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      *reinterpret_cast<float4*>(&s_acc[wave][col][16 * t + 4 * c]) =
+          make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
+  }
+  __syncthreads();
+  merge_waves<R, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, out_bg);
 }
 
 // Log-sum-exp combine of the split partials: one workgroup per (sequence,
@@ -514,24 +876,45 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
   a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(o);
 }
 
-template <int R, int W, bool kStream>
-hipError_t launch_rws(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
-  const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
-  if (st != nullptr) {
-    hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
-  } else {
-    hipLaunchKernelGGL((decode_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a, StepArgs{});
-  }
+// The combine launch that follows the split kernel when the plan has splits.
+hipError_t launch_combine_if_split(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL(combine_kernel, dim3(a.num_q_heads, a.batch), dim3(kHeadDim), 0, stream, pool, a);
   return hipGetLastError();
 }
 
+template <int R, int W, bool kStream>
+hipError_t launch_dot(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+  const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
+  if (st != nullptr) {
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a, StepArgs{});
+  }
+  return launch_combine_if_split(pool, a, stream);
+}
+
+template <int R, int W, bool kStream>
+hipError_t launch_mfma(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+  const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
+  if (st != nullptr) {
+    hipLaunchKernelGGL((decode_mfma_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a,
+                       StepArgs{});
+  }
+  return launch_combine_if_split(pool, a, stream);
+}
+
 template <int R, int W>
 hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
-  if (a.stream_loads) return launch_rws<R, W, true>(pool, a, st, stream);
-  return launch_rws<R, W, false>(pool, a, st, stream);
+  if (a.mfma) {
+    if (a.stream_loads) return launch_mfma<R, W, true>(pool, a, st, stream);
+    return launch_mfma<R, W, false>(pool, a, st, stream);
+  }
+  if (a.stream_loads) return launch_dot<R, W, true>(pool, a, st, stream);
+  return launch_dot<R, W, false>(pool, a, st, stream);
 }
 
 template <int R>

@@ -49,6 +49,7 @@ struct DecodeArgs {
   int32_t batch; int32_t num_q_heads; int32_t max_ctx;
   float qk_scale_log2;   // softmax scale * log2(e)
   int32_t split_tokens; int32_t max_splits; int32_t waves;
+  int32_t mfma;          // 1: matrix-core split kernel, 0: dot-product split kernel
   int32_t stream_loads;  // 1: K/V loads carry the non-temporal (streaming) hint
   float* part_o;         // [batch][Hkv][max_splits][r][128]
   float* part_lse;       // [batch][Hkv][max_splits][r]

@@ -140,3 +140,20 @@ class StepRun:
         pk, pv, bt_c = self.read_pool()
         q = f64_of(q_gpu)
         return O.chunk_attention(q, self.w.chk_qsl, pk, pv, bt_c[self.w.num_decode:], self.w.chk_ctx, SCALE)
+
+
+# Decode split kernels: 1 = dot-product (VALU) kernel, 2 = matrix-core (MFMA) kernel.
+KERNELS = [1, 2]
+
+
+def with_kernel(plan, kernel):
+    """A copy of a DecodePlan with its split kernel set."""
+    return pg.DecodePlan(plan.split_tokens, plan.max_splits, plan.waves_per_split, plan.load_hint, kernel)
+
+
+def default_plan(w, kernel):
+    """The library's plan for the decode rows of step w, with the split kernel set."""
+    s = w.spec
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    p = pg.plan_decode(cus, s.block_size, w.num_decode, s.num_kv_heads, s.num_q_heads, int(w.dec_ctx.max()))
+    return with_kernel(p, kernel)

@@ -11,7 +11,8 @@ import oracle as O
 import paged_gqa_decode_head_amd as pg
 from paged_gqa_decode_head_amd.workloads import SPECS, Group, StepSpec, make_step
 
-from harness import SCALE, SENTINEL, StepRun, bits_of, compare, dev_bf16, dev_i32, f64_of
+from harness import (KERNELS, SCALE, SENTINEL, StepRun, bits_of, compare, default_plan, dev_bf16, dev_i32,
+                     f64_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,14 +70,16 @@ def test_cache_write_parity_and_exact_slots(name):
 
 
 # ---------------------------------------------------------------- decode (a4-a5)
+@pytest.mark.parametrize("kernel", [0] + KERNELS)
 @pytest.mark.parametrize("name", ["cfg1", "cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5"])
-def test_decode_parity(name):
-    _note(f"[decode] {name}")
+def test_decode_parity(name, kernel):
+    """kernel 0: the library's default plan (plan = NULL)."""
+    _note(f"[decode] {name} kernel={kernel}")
     w = workload(name)
     run = StepRun(w)
     run.write()
     q = run.decode_q()
-    out = run.decode(q=q)
+    out = run.decode(q=q, plan=None if kernel == 0 else default_plan(w, kernel))
     assert run.pool.check_errors() == 0
     ref = run.oracle_decode_on_gpu_inputs(q)
     ma, mr = compare(out, ref, f"{name} decode")
@@ -104,7 +107,8 @@ def test_cfg1_end_to_end_chain():
 @pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 16), (32, 8, 32), (16, 8, 64),
                                        (16, 4, 256), (8, 1, 16), (2, 1, 128)])
 @pytest.mark.parametrize("plan", [None, (64, 1), (128, 2), (256, 4), (512, 8), (4096, 4)])
-def test_decode_small_shapes_and_plans(hq, hkv, bs, plan):
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_small_shapes_and_plans(hq, hkv, bs, plan, kernel):
     spec = StepSpec(f"small-{hq}-{hkv}-{bs}", 901 + hq + bs, hq, hkv, 256 if bs < 256 else 32,
                     decode=(Group(1, 0, 0), Group(1, 15, 15), Group(1, 16, 16), Group(4, 1, 700)),
                     block_size=bs)
@@ -112,22 +116,24 @@ def test_decode_small_shapes_and_plans(hq, hkv, bs, plan):
     run = StepRun(w)
     run.write()
     q = run.decode_q()
-    p = None
-    if plan is not None:
+    if plan is None:
+        p = default_plan(w, kernel)
+    else:
         split = max(plan[0], bs)
-        p = pg.DecodePlan(split, -(-int(w.dec_ctx.max()) // split), plan[1], 0)
+        p = pg.DecodePlan(split, -(-int(w.dec_ctx.max()) // split), plan[1], 0, kernel)
     out = run.decode(plan=p, q=q)
     assert run.pool.check_errors() == 0
-    compare(out, run.oracle_decode_on_gpu_inputs(q), f"{spec.name} plan={plan}")
+    compare(out, run.oracle_decode_on_gpu_inputs(q), f"{spec.name} plan={p}")
 
 
-def test_decode_deterministic_and_block_permutation_bit_identical():
-    _note("[perm] small")
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_deterministic_and_block_permutation_bit_identical(kernel):
+    _note(f"[perm] small kernel={kernel}")
     w = make_step(StepSpec("perm", 950, 16, 8, 640, decode=(Group(6, 100, 1500),)))
     run = StepRun(w)
     run.write()
     q = run.decode_q()
-    plan = pg.DecodePlan(256, 6, 4, 0)
+    plan = pg.DecodePlan(256, 6, 4, 0, kernel)
     a = bits_of(run.decode(plan=plan, q=q))
     b = bits_of(run.decode(plan=plan, q=q))
     assert np.array_equal(a, b)
@@ -143,11 +149,12 @@ def test_decode_deterministic_and_block_permutation_bit_identical():
     assert np.array_equal(a, bits_of(out2))
 
 
-def test_single_key_returns_v_exactly():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_single_key_returns_v_exactly(kernel):
     w = make_step(StepSpec("one", 960, 16, 8, 16, decode=(Group(3, 0, 0),)))
     run = StepRun(w)
     run.write()
-    out = bits_of(run.decode())
+    out = bits_of(run.decode(plan=default_plan(w, kernel)))
     for b in range(3):
         for h in range(16):
             assert np.array_equal(out[b, h], w.tok_v[b, h // 2])
@@ -181,7 +188,8 @@ def test_addressing_probe_one_hot_every_position():
             j = jstar % n
             kk[bt[s, j // bs], j % bs] = hot
         pool.fill_logical(kk.view(np.int16), vk.view(np.int16))
-        for plan in (pg.DecodePlan(64, 2, 1, 0), pg.DecodePlan(4096, 1, 4, 0)):
+        for plan in (pg.DecodePlan(64, 2, 1, 0, 1), pg.DecodePlan(4096, 1, 4, 0, 1),
+                     pg.DecodePlan(64, 2, 1, 0, 2), pg.DecodePlan(4096, 1, 4, 0, 2)):
             out = bits_of(pg.paged_decode_attention(pool, q, ctx, bt_d, max(lens), SCALE, plan=plan))
             for s, n in enumerate(lens):
                 j = jstar % n
@@ -189,34 +197,40 @@ def test_addressing_probe_one_hot_every_position():
                     assert np.array_equal(out[s, h], vk[bt[s, j // bs], j % bs, h // 2]), (jstar, s, h)
 
 
-def test_empty_batch_and_zero_context():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_empty_batch_and_zero_context(kernel):
     w = make_step(StepSpec("z", 970, 16, 8, 16, decode=(Group(2, 5, 5),)))
     run = StepRun(w)
     run.write()
     q = run.decode_q()
+    plan = default_plan(w, kernel)
     out = torch.full((2, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
-    pg.paged_decode_attention(run.pool, q[:0], run.dec_ctx[:0], run.dec_bt[:0], 6, SCALE, out=out[:0])
+    pg.paged_decode_attention(run.pool, q[:0], run.dec_ctx[:0], run.dec_bt[:0], 6, SCALE, out=out[:0], plan=plan)
     ctx0 = dev_i32(np.array([0, 6], dtype=np.int32))
-    pg.paged_decode_attention(run.pool, q, ctx0, run.dec_bt, 6, SCALE, out=out)
+    pg.paged_decode_attention(run.pool, q, ctx0, run.dec_bt, 6, SCALE, out=out, plan=plan)
     torch.cuda.synchronize()
     assert torch.all(out[0] == 0)
     assert run.pool.check_errors() == 0
 
 
-def test_bad_metadata_sets_flags_without_faulting():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_bad_metadata_sets_flags_without_faulting(kernel):
     w = make_step(StepSpec("bad", 980, 16, 8, 16, decode=(Group(2, 20, 20),)))
     run = StepRun(w)
     run.write()
     q = run.decode_q()
     # context longer than the table row: flagged, row zeroed
-    ctx = dev_i32(np.array([21, 16 * run.dec_bt.shape[1] + 1], dtype=np.int32))
-    out = pg.paged_decode_attention(run.pool, q, ctx, run.dec_bt, 16 * run.dec_bt.shape[1] + 1, SCALE)
+    mx = 16 * run.dec_bt.shape[1] + 1
+    ctx = dev_i32(np.array([21, mx], dtype=np.int32))
+    plan = pg.DecodePlan(64, -(-mx // 64), 4, 0, kernel)
+    out = pg.paged_decode_attention(run.pool, q, ctx, run.dec_bt, mx, SCALE, plan=plan)
     assert run.pool.check_errors() & pg.DEVERR_CONTEXT
     assert torch.all(out[1] == 0)
     # block id outside the pool: flagged, no fault
     bt = w.dec_block_tables.copy()
     bt[0, 0] = 10_000
-    out = pg.paged_decode_attention(run.pool, q, run.dec_ctx, dev_i32(bt), 21, SCALE)
+    out = pg.paged_decode_attention(run.pool, q, run.dec_ctx, dev_i32(bt), 21, SCALE,
+                                    plan=pg.DecodePlan(64, 1, 4, 0, kernel))
     assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
     # cache write with a position past the table and a bad seq id: skipped and flagged
     pos = dev_i32(np.array([10_000, 3], dtype=np.int32))
@@ -245,7 +259,8 @@ def test_host_pointer_rejected():
     assert st == 3 and b"context_lens" in L.pgqa_last_error()
 
 
-def test_decode_ignores_garbage_past_the_context():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_ignores_garbage_past_the_context(kernel):
     """Slots past each context hold NaN bit patterns: weights there are 0 and
     the result must not see them."""
     w = make_step(StepSpec("garbage", 975, 16, 8, 160, decode=(Group(6, 1, 300),)))
@@ -262,7 +277,7 @@ def test_decode_ignores_garbage_past_the_context():
     run.pool.fill_logical(k.view(np.int16), v.view(np.int16))
     run.write()
     q = run.decode_q()
-    for plan in (None, pg.DecodePlan(64, 5, 1, 0), pg.DecodePlan(4096, 1, 8, 0)):
+    for plan in (default_plan(w, kernel), pg.DecodePlan(64, 5, 1, 0, kernel), pg.DecodePlan(4096, 1, 8, 0, kernel)):
         out = run.decode(plan=plan, q=q)
         compare(out, run.oracle_decode_on_gpu_inputs(q), f"garbage plan={plan}")
 

@@ -10,7 +10,7 @@ import oracle as O
 import paged_gqa_decode_head_amd as pg
 from paged_gqa_decode_head_amd.workloads import SPECS, Group, StepSpec, make_step
 
-from harness import SCALE, StepRun, bits_of, compact, compare, dev_i32
+from harness import KERNELS, SCALE, StepRun, bits_of, compact, compare, default_plan, dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -38,13 +38,12 @@ def _bits_equal(a, b, w):
     return np.array_equal(ka.numpy(), kb.numpy()) and np.array_equal(va.numpy(), vb.numpy())
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("name", ["cfg2", "cfg3a", "cfg3b", "cfg4"])
-def test_fused_step_equals_write_then_decode(name):
-    _note(f"[step] {name}")
+def test_fused_step_equals_write_then_decode(name, kernel):
+    _note(f"[step] {name} kernel={kernel}")
     w = make_step(SPECS[name])
-    s = w.spec
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    plan = pg.plan_decode(cus, s.block_size, w.num_decode, s.num_kv_heads, s.num_q_heads, int(w.dec_ctx.max()))
+    plan = default_plan(w, kernel)
     a, b, out_a, out_b, qo_b = _pair(w, plan)
     assert a.pool.check_errors() == 0 and b.pool.check_errors() == 0
     assert np.array_equal(bits_of(qo_b), bits_of(a.q_out))
@@ -55,14 +54,18 @@ def test_fused_step_equals_write_then_decode(name):
 
 @pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 16), (32, 4, 16), (8, 8, 32), (8, 1, 64), (16, 4, 256)])
 @pytest.mark.parametrize("plan", [None, (64, 1), (256, 4), (4096, 8)])
-def test_fused_step_small_shapes_and_plans(hq, hkv, bs, plan):
+@pytest.mark.parametrize("kernel", [0] + KERNELS)
+def test_fused_step_small_shapes_and_plans(hq, hkv, bs, plan, kernel):
+    """kernel 0 with plan None: plan = NULL (the library's default plan)."""
     spec = StepSpec(f"fstep-{hq}-{hkv}-{bs}", 940 + hq + bs, hq, hkv, 256 if bs < 256 else 32,
                     decode=(Group(1, 0, 0), Group(1, 15, 15), Group(1, 16, 16), Group(4, 1, 700)), block_size=bs)
     w = make_step(spec)
     p = None
     if plan is not None:
         split = max(plan[0], bs)
-        p = pg.DecodePlan(split, -(-int(w.dec_ctx.max()) // split), plan[1], 0)
+        p = pg.DecodePlan(split, -(-int(w.dec_ctx.max()) // split), plan[1], 0, kernel)
+    elif kernel:
+        p = default_plan(w, kernel)
     a, b, out_a, out_b, qo_b = _pair(w, p)
     assert b.pool.check_errors() == 0
     assert np.array_equal(bits_of(out_b), bits_of(out_a))
@@ -70,7 +73,8 @@ def test_fused_step_small_shapes_and_plans(hq, hkv, bs, plan):
     assert _bits_equal(a, b, w)
 
 
-def test_fused_step_end_to_end_against_fp64_chain():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_fused_step_end_to_end_against_fp64_chain(kernel):
     """Row-strided q/k/v taken from one packed projection buffer; the output
     against the fp64 chain (norm, rotary, bf16 cache, attention) on raw inputs."""
     w = make_step(StepSpec("fchain", 961, 16, 8, 64, decode=(Group(3, 20, 200),)))
@@ -82,7 +86,7 @@ def test_fused_step_end_to_end_against_fp64_chain():
     k = packed[:, hq * 128:(hq + hkv) * 128].view(B, hkv, 128)
     v = packed[:, (hq + hkv) * 128:].view(B, hkv, 128)
     out = pg.decode_step(run.pool, q, k, v, run.wq, run.wk, run.dec_ctx, run.dec_bt, int(w.dec_ctx.max()), s.eps,
-                         s.rope_theta, SCALE)
+                         s.rope_theta, SCALE, plan=default_plan(w, kernel))
     assert run.pool.check_errors() == 0
     # fp64 chain: the new tokens written into a reference cache model (bf16 K/V),
     # q rounded to bf16 as the kernel holds it, then attention
@@ -94,7 +98,8 @@ def test_fused_step_end_to_end_against_fp64_chain():
     compare(out, ref, "fused step vs fp64 chain")
 
 
-def test_fused_step_zero_context_and_bad_block():
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_fused_step_zero_context_and_bad_block(kernel):
     w = make_step(StepSpec("fbad", 962, 16, 8, 16, decode=(Group(3, 30, 30),)))
     s = w.spec
     run = StepRun(w)
@@ -104,7 +109,7 @@ def test_fused_step_zero_context_and_bad_block():
     bt[2, (ctx[2] - 1) // 16] = s.num_blocks + 5  # the new token's block id is outside the pool
     out = torch.full((3, 16, 128), 7.0, dtype=torch.bfloat16, device="cuda")
     pg.decode_step(run.pool, run.q, run.k, run.v, run.wq, run.wk, dev_i32(ctx), dev_i32(bt), int(ctx.max()), s.eps,
-                   s.rope_theta, SCALE, out=out)
+                   s.rope_theta, SCALE, out=out, plan=default_plan(w, kernel))
     assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
     assert torch.all(out[1] == 0)
     assert torch.all(torch.isfinite(out[0].float()))
@@ -131,7 +136,8 @@ def test_fused_step_random_cases_against_fp64_chain(seed):
     if rng.integers(3):
         gran = max(64, bs)
         split = min(gran * int(rng.integers(1, 9)), 4096 // gran * gran)
-        plan = pg.DecodePlan(split, -(-mx // split), int(rng.choice([1, 2, 4, 8])), int(rng.integers(3)))
+        plan = pg.DecodePlan(split, -(-mx // split), int(rng.choice([1, 2, 4, 8])), int(rng.integers(3)),
+                             int(rng.integers(3)))
     _note(f"[frand] seed {seed}: heads {hq}/{hkv} bs {bs} contexts {w.dec_ctx.tolist()} plan {plan}")
     run = StepRun(w)
     q_out = torch.empty_like(run.q)
