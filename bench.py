@@ -146,10 +146,14 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
             cases = {"slice+verify": (qc, w.chk_qsl, w.chk_ctx, w.chk_block_tables),
                      "slice": (qc[:512].contiguous(), w.chk_qsl[:2], w.chk_ctx[:1], w.chk_block_tables[:1]),
                      "verify": (qc[512:].contiguous(), w.chk_qsl[1:] - 512, w.chk_ctx[1:], w.chk_block_tables[1:])}
+            # the verify rows once more on the chunk kernels (their planner split for such rows)
+            cases["verify_chunk_kernels"] = cases["verify"]
             for label, (qq, qs, cx, bb) in cases.items():
                 mq, mc = int(np.diff(qs).max()), int(cx.max())
                 o2 = torch.empty((qq.shape[0], s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
                 cp = pg.plan_chunk(cus, s.block_size, len(cx), qq.shape[0], s.num_kv_heads, s.num_q_heads, mq, mc)
+                if label == "verify_chunk_kernels":
+                    cp = pg.ChunkPlan(256, -(-mc // 256), 256, 1)
                 calls = [pg.bind_chunk(p, qq, to_i32(qs), to_i32(cx), to_i32(bb), mq, mc, scale, o2, plan=cp)
                          for p in pools]
                 med, _ = time_calls(calls, 30)
@@ -158,7 +162,8 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                               "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                               "kv_gbs": round(kv / med / 1e3, 1), "flops": flops, "kv_bytes": kv,
                               "plan": {"split_tokens": cp.split_tokens, "short_split_tokens": cp.short_split_tokens,
-                                       "max_splits": cp.max_splits}}
+                                       "max_splits": cp.max_splits,
+                                       "kernel": "columns" if cp.kernel == 2 else "chunk"}}
             rows["chunk_cfg5"] = res
         del pools
         torch.cuda.empty_cache()

@@ -248,7 +248,12 @@ typedef struct {
   int32_t split_tokens;        /* a multiple of 32, at most 4096 */
   int32_t max_splits;          /* >= ceil(max_context_len / min(split_tokens, short_split_tokens)) */
   int32_t short_split_tokens;  /* a multiple of 32, at most 4096; 0 = split_tokens */
-  int32_t reserved;            /* 0 */
+  int32_t kernel;              /* 0 or 1: the chunk kernels (wide / short items, combine);
+                                  2: the matrix-core decode kernel with the segment's (token, head) rows
+                                  as its 16 MFMA columns, for calls with max_q_len x group <= 16 (verify
+                                  rows, single tokens): split_tokens keys per split, a multiple of
+                                  max(block_size, 64), at most 4096; short_split_tokens unused.
+                                  pgqa_plan_chunk picks 2 whenever a call fits. */
 } pgqa_chunk_plan;
 
 /* Host-only: the plan pgqa_paged_chunk_attention uses when given plan = NULL. */

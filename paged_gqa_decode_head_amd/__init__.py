@@ -53,7 +53,7 @@ class DecodePlan(ctypes.Structure):
 
 class ChunkPlan(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("short_split_tokens", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("short_split_tokens", ctypes.c_int32), ("kernel", ctypes.c_int32)]
 
     def __repr__(self):
         return (f"ChunkPlan(split_tokens={self.split_tokens}, max_splits={self.max_splits}, "

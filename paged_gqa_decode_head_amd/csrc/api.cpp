@@ -124,6 +124,32 @@ pgqa_status validate_plan(const pgqa_decode_plan& p, int32_t block_size, int32_t
 // batches, which stream at close to the memory system's rate.
 int32_t default_decode_kernel(int32_t r) { return r >= 8 ? 2 : 1; }
 
+// Keys per split of the decode planner (see pgqa_plan_decode) for `units`
+// (sequence, kv head) pairs of at most ctx keys: one split when that gives at
+// least half a workgroup per CU, else about one workgroup per CU with a floor
+// on the split length (512 keys for the matrix-core kernel, 1024 otherwise,
+// 1536 from 16k keys); a multiple of max(block_size, 64), at most 1024 keys
+// per wave.
+int64_t decode_split(int32_t num_cus, int32_t block_size, int64_t units, int64_t ctx, bool mfma, int32_t waves) {
+  const int64_t gran = block_size > 64 ? block_size : 64;
+  const int64_t max_split = std::min<int64_t>(1024ll * waves, kMaxSplitTokens);
+  int64_t split;
+  if (2 * units >= num_cus) {
+    split = round_up(ctx, gran);
+  } else {
+    const int64_t want = (num_cus + units - 1) / units;
+    split = round_up((ctx + want - 1) / want, gran);
+    const int64_t floor_split = round_up(ctx >= 16384 ? 1536 : mfma ? 512 : 1024, gran);
+    if (split < floor_split) split = floor_split;
+    if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
+  }
+  if (split > max_split) {
+    const int64_t parts = (ctx + max_split - 1) / max_split;
+    split = std::min(round_up((ctx + parts - 1) / parts, gran), max_split / gran * gran);
+  }
+  return split;
+}
+
 // Rotary turn frequencies of rope_theta (host fp64), cached in the pool.
 void rope_table(pgqa_pool* pool, double rope_theta, double (&out)[64]) {
   std::lock_guard<std::mutex> lock(pool->rope_mu);
@@ -359,24 +385,9 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   const int32_t r = num_q_heads / num_kv_heads;
   const int32_t kernel = default_decode_kernel(r);
   const int32_t waves = 4;
-  const int64_t gran = block_size > 64 ? block_size : 64;
-  const int64_t units = int64_t(batch > 0 ? batch : 1) * num_kv_heads;
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  const int64_t max_split = std::min<int64_t>(1024ll * waves, kMaxSplitTokens);
-  int64_t split;
-  if (2 * units >= num_cus) {
-    split = round_up(ctx, gran);
-  } else {
-    const int64_t want = (num_cus + units - 1) / units;
-    split = round_up((ctx + want - 1) / want, gran);
-    const int64_t floor_split = round_up(ctx >= 16384 ? 1536 : kernel == 2 ? 512 : 1024, gran);
-    if (split < floor_split) split = floor_split;
-    if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
-  }
-  if (split > max_split) {
-    const int64_t parts = (ctx + max_split - 1) / max_split;
-    split = std::min(round_up((ctx + parts - 1) / parts, gran), max_split / gran * gran);
-  }
+  const int64_t split = decode_split(num_cus, block_size, int64_t(batch > 0 ? batch : 1) * num_kv_heads, ctx,
+                                     kernel == 2, waves);
   out->split_tokens = int32_t(split);
   out->max_splits = int32_t((ctx + split - 1) / split);
   out->waves_per_split = waves;
@@ -439,7 +450,7 @@ pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, 
                   workspace == nullptr ? size_t(0) : workspace_bytes);
     PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
   }
-  DecodeArgs a;
+  DecodeArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.q_stride = q_row_stride;
   a.ctx = context_lens;
@@ -537,6 +548,17 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
     split = std::max(split, floor_keys);
     return std::min(split, cap);
   };
+  if (int64_t(max_q_len) * r <= 16) {
+    // every segment fits the 16 columns of the matrix-core decode kernel
+    // (verify rows, single tokens): one workgroup per (kv head, segment,
+    // split), splits as the decode planner makes them for that kernel
+    const int64_t split = decode_split(num_cus, block_size, int64_t(std::max(num_segments, 1)) * num_kv_heads, ctx,
+                                       true, 4);
+    out->split_tokens = out->short_split_tokens = int32_t(split);
+    out->max_splits = int32_t((ctx + split - 1) / split);
+    out->kernel = 2;
+    return PGQA_OK;
+  }
   const ChunkLists lists = chunk_lists(num_segments, total_q, int32_t(r), max_q_len);
   const int64_t wide_groups = (int64_t(total_q) * r + 127) / 128;
   const int64_t wide = pick(std::max<int64_t>(wide_groups, 1) * num_kv_heads, 2, 256);
@@ -550,25 +572,45 @@ pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_seg
   out->split_tokens = int32_t(wide);
   out->short_split_tokens = int32_t(narrow);
   out->max_splits = int32_t((ctx + smallest - 1) / smallest);
-  out->reserved = 0;
+  out->kernel = 1;
   return PGQA_OK;
 }
 
 namespace {
 struct ChunkSizing {
+  bool columns;  // the call runs on the matrix-core decode kernel (plan kernel 2)
   int32_t split_wide, split_short, max_splits;
   ChunkGrids grids;
   ChunkWorkspace ws;
+  DecodeWorkspace cws;  // columns: split partials, 16 columns per (segment, kv head)
+  size_t total() const { return columns ? cws.total : ws.total; }
 };
 
-pgqa_status chunk_sizing(const pgqa_chunk_plan& p, int32_t num_segments, int32_t total_q, int32_t hkv, int32_t hq,
-                         int32_t max_q_len, int32_t max_context_len, ChunkSizing* out) {
+pgqa_status chunk_sizing(const pgqa_chunk_plan& p, int32_t block_size, int32_t num_segments, int32_t total_q,
+                         int32_t hkv, int32_t hq, int32_t max_q_len, int32_t max_context_len, ChunkSizing* out) {
+  if (p.kernel < 0 || p.kernel > 2) return fail(PGQA_ERR_INVALID_ARG, "chunk plan kernel=%d (0, 1 or 2)", p.kernel);
+  out->columns = p.kernel == 2;
+  if (out->columns) {
+    const int32_t gran = block_size > 64 ? block_size : 64;
+    if (int64_t(max_q_len) * (hq / hkv) > 16)
+      return fail(PGQA_ERR_INVALID_ARG, "chunk plan kernel=2 needs max_q_len x group <= 16 (%d x %d)", max_q_len,
+                  hq / hkv);
+    if (p.split_tokens <= 0 || p.split_tokens % gran != 0 || p.split_tokens > 4096)
+      return fail(PGQA_ERR_INVALID_ARG, "chunk plan kernel=2: split of %d keys must be a positive multiple of %d, "
+                  "at most 4096", p.split_tokens, gran);
+    if (p.max_splits < (int64_t(max_context_len) + p.split_tokens - 1) / p.split_tokens || p.max_splits > 65535)
+      return fail(PGQA_ERR_INVALID_ARG, "plan.max_splits=%d does not cover max_context_len=%d", p.max_splits,
+                  max_context_len);
+    out->split_wide = out->split_short = p.split_tokens;
+    out->max_splits = p.max_splits;
+    out->cws = decode_workspace_layout(num_segments, hkv, 16, p.max_splits);
+    return PGQA_OK;
+  }
   const int32_t short_split = p.short_split_tokens == 0 ? p.split_tokens : p.short_split_tokens;
   for (const int32_t sp : {p.split_tokens, short_split})
     if (sp <= 0 || sp % kChunkStep != 0 || sp > kMaxSplitTokens)
       return fail(PGQA_ERR_INVALID_ARG, "chunk plan split of %d keys must be a positive multiple of %d, at most %d",
                   sp, kChunkStep, kMaxSplitTokens);
-  if (p.reserved != 0) return fail(PGQA_ERR_INVALID_ARG, "chunk plan reserved field must be 0");
   const ChunkLists lists = chunk_lists(num_segments, total_q, hq / hkv, max_q_len);
   const int32_t smallest = !lists.narrow ? p.split_tokens : !lists.wide ? short_split
                                                                          : std::min(p.split_tokens, short_split);
@@ -600,10 +642,10 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
     return 0;
   }
   ChunkSizing z;
-  if (chunk_sizing(p, num_segments, total_q, pool->cfg.num_kv_heads, num_q_heads, max_q_len, max_context_len, &z) !=
-      PGQA_OK)
+  if (chunk_sizing(p, pool->cfg.block_size, num_segments, total_q, pool->cfg.num_kv_heads, num_q_heads, max_q_len,
+                   max_context_len, &z) != PGQA_OK)
     return 0;
-  return z.ws.total;
+  return z.total();
 }
 
 pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
@@ -635,18 +677,46 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
                              max_q_len, max_context_len, &p));
   }
   ChunkSizing z;
-  PGQA_TRY(chunk_sizing(p, num_segments, total_q, hkv, num_q_heads, max_q_len, max_context_len, &z));
+  PGQA_TRY(chunk_sizing(p, pool->cfg.block_size, num_segments, total_q, hkv, num_q_heads, max_q_len, max_context_len,
+                        &z));
   const int dev = pool->device;
   PGQA_TRY(check_device_ptr(q, dev, "q", 16));
   PGQA_TRY(check_device_ptr(query_start_loc, dev, "query_start_loc", 4));
   PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
   PGQA_TRY(check_device_ptr(out, dev, "out", 8));
-  if (z.ws.total > 0) {
-    if (workspace == nullptr || workspace_bytes < z.ws.total)
-      return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", z.ws.total,
+  if (z.total() > 0) {
+    if (workspace == nullptr || workspace_bytes < z.total())
+      return fail(PGQA_ERR_WORKSPACE, "chunk workspace of %zu bytes needed, %zu given", z.total(),
                   workspace == nullptr ? size_t(0) : workspace_bytes);
     PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  }
+  if (z.columns) {
+    DecodeArgs d{};
+    d.q = static_cast<const uint16_t*>(q);
+    d.q_stride = int64_t(num_q_heads) * 128;
+    d.ctx = context_lens;
+    d.bt = block_tables;
+    d.bt_stride = bt_stride;
+    d.batch = num_segments;
+    d.num_q_heads = num_q_heads;
+    d.max_ctx = max_context_len;
+    d.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
+    d.split_tokens = z.split_wide;
+    d.max_splits = z.max_splits;
+    d.waves = 4;
+    d.mfma = 1;
+    d.stream_loads = 0;
+    char* ws = static_cast<char*>(workspace);
+    d.part_o = z.cws.total > 0 ? reinterpret_cast<float*>(ws + z.cws.part_o_off) : nullptr;
+    d.part_lse = z.cws.total > 0 ? reinterpret_cast<float*>(ws + z.cws.part_lse_off) : nullptr;
+    d.out = static_cast<uint16_t*>(out);
+    d.qsl = query_start_loc;
+    d.total_q = total_q;
+    d.max_q_len = max_q_len;
+    hipError_t e = launch_decode_columns(pool->geom, d, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "chunk launch");
+    return PGQA_OK;
   }
   ChunkArgs a;
   a.q = static_cast<const uint16_t*>(q);

@@ -71,17 +71,20 @@ __device__ __forceinline__ uint4 ld16(const uint16_t* p) {
 
 // Merge the W waves' online-softmax states of one (sequence b, kv head g,
 // split sp), left in LDS by each wave (max m, weight sum l and unnormalised
-// accumulator per query head), and store the result: bf16 rows when the
-// sequence has one split, else the normalised partial and its lse (log2 units)
-// for the combine.  Thread i handles (head, dim) pairs i, i + 64 W, ...
-template <int R, int W>
-__device__ __forceinline__ void merge_waves(const float (&s_m)[W][R], const float (&s_l)[W][R],
-                                            const float (&s_acc)[W][R][kHeadDim], const DecodeArgs& a, int b, int g,
-                                            int sp, bool single, int hkv, uint16_t* out_bg) {
-  constexpr int kPairs = R * kHeadDim;
+// accumulator per column: query head, or (token, head) row of a chunk
+// segment), and store the result: bf16 rows (out_row(h): the output row of
+// column h) when the sequence has one split, else the
+// normalised partials and their lse (log2 units) for the combine.  Only the
+// first ncols columns are merged and stored.  Thread i handles (column, dim)
+// pairs i, i + 64 W, ...
+template <int C, int W, typename OutRow>
+__device__ __forceinline__ void merge_waves(const float (&s_m)[W][C], const float (&s_l)[W][C],
+                                            const float (&s_acc)[W][C][kHeadDim], const DecodeArgs& a, int b, int g,
+                                            int sp, bool single, int hkv, int ncols, OutRow out_row) {
+  constexpr int kPairs = C * kHeadDim;
   float* po = a.part_o + ((int64_t(b) * hkv + g) * a.max_splits + sp) * kPairs;
-  float* plse = a.part_lse + ((int64_t(b) * hkv + g) * a.max_splits + sp) * R;
-  for (int idx = threadIdx.x; idx < kPairs; idx += 64 * W) {
+  float* plse = a.part_lse + ((int64_t(b) * hkv + g) * a.max_splits + sp) * C;
+  for (int idx = threadIdx.x; idx < ncols * kHeadDim; idx += 64 * W) {
     const int h = idx >> 7, d = idx & (kHeadDim - 1);
     float M = -INFINITY;
 #pragma unroll
@@ -97,7 +100,7 @@ __device__ __forceinline__ void merge_waves(const float (&s_m)[W][R], const floa
     }
     const float o = L > 0.f ? A / L : 0.f;
     if (single) {
-      out_bg[idx] = f32_to_bf16(o);
+      out_row(h)[d] = f32_to_bf16(o);
     } else {
       po[idx] = o;
       if (d == 0) plse[h] = L > 0.f ? M + __log2f(L) : -INFINITY;
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     }
   }
   __syncthreads();
-  merge_waves<R, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, out_bg);
+  merge_waves<R, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, R, [&](int h) { return out_bg + h * kHeadDim; });
 }
 
 // ---------------------------------------------------------------------------
@@ -512,18 +515,27 @@ struct MStep {
 // 64 bytes of each of 16 key rows, so the other half of each 128-byte line
 // comes with the next instruction; with cached loads (the default for this
 // kernel) it hits in L2.
-template <int R, int W, bool kStream, bool kFused>
+//
+// kChunk: the same kernel over short causal chunk segments (speculative-verify
+// rows, single tokens) instead of one query token per sequence.  Unit b is
+// segment b of a chunk call: query tokens query_start_loc[b] .. +q_len - 1 at
+// positions n - q_len .. n - 1 of its n keys.  Column col is the (token
+// col / R, head col % R) row, so a segment fits when q_len R <= 16; each
+// column sees the keys up to its token's position (bottom-right causal).
+template <int R, int W, bool kStream, bool kFused, bool kChunk = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(PoolGeom pool,
                                                                                                   DecodeArgs a,
                                                                                                   StepArgs st) {
   static_assert(R <= 16, "query heads per kv head exceed the MFMA columns");
+  static_assert(!(kFused && kChunk), "the fused step has one query token per sequence");
+  constexpr int C = kChunk ? 16 : R;  // columns in use
   const int g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, c = lane >> 4;
   const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
 
-  __shared__ float s_m[W][R], s_l[W][R];
-  __shared__ __align__(16) float s_acc[W][R][kHeadDim];
+  __shared__ float s_m[W][C], s_l[W][C];
+  __shared__ __align__(16) float s_acc[W][C][kHeadDim];
   // fused step: each wave's normed, rotated q rows, and the new token's k and v
   __shared__ __align__(16) uint16_t s_q[kFused ? W : 1][kFused ? R : 1][kHeadDim];
   __shared__ __align__(16) uint16_t s_newk[kFused ? kHeadDim : 1];
@@ -540,8 +552,21 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int64_t entry = (int64_t(k0) + off) / bs;
     if (off < a.split_tokens && entry < a.bt_stride) lane_blk = a.bt[int64_t(b) * a.bt_stride + entry];
   }
+  // Chunk segment: its query rows and the checks of the chunk kernels.
+  int q0 = 0, qlen = 1;
+  bool rows_ok = true, q_ok = true;
+  if constexpr (kChunk) {
+    q0 = a.qsl[b];
+    const int q1 = a.qsl[b + 1];
+    qlen = q1 - q0;
+    rows_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q;
+    q_ok = rows_ok && qlen <= a.max_q_len && qlen * R <= 16 && n >= qlen;
+  }
+  const int tcol = col / R;  // chunk: the column's token in the segment
+  const bool cvalid = kChunk ? q_ok && tcol < qlen : col < R;
   // Plain decode: q^T as the B operand of the score products, column col =
-  // head g R + col (zero past R), dims 32s + 8c .. +7.  Fused step: lanes
+  // head g R + col (zero past R), dims 32s + 8c .. +7; chunk segments: head
+  // g R + col % R of query token q0 + col / R.  Fused step: lanes
   // 8h + sub (h < R) hold dims 8 sub .. and 64 + 8 sub .. of the raw q row of
   // head g R + h (the layout of the shared norm + rotary code); lanes 0..7 also
   // fetch the new token's raw k, v and the k norm weight.
@@ -565,16 +590,34 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
       nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
     }
   } else {
-    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + (col < R ? col : 0)) * kHeadDim + 8 * c;
+    const int64_t qr = kChunk ? (cvalid ? q0 + tcol : 0) : b;   // an invalid column reads row 0
+    const int qh = kChunk ? (cvalid ? g * R + col % R : 0) : g * R + (col < R ? col : 0);
+    const uint16_t* qrow = a.q + qr * a.q_stride + qh * kHeadDim + 8 * c;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      qb[s] = sel4(col < R, *reinterpret_cast<const uint4*>(qrow + 32 * s), make_uint4(0u, 0u, 0u, 0u));
+      qb[s] = sel4(cvalid, *reinterpret_cast<const uint4*>(qrow + 32 * s), make_uint4(0u, 0u, 0u, 0u));
     }
   }
 
   const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;
   uint16_t* out_bg = a.out + (int64_t(b) * hq + g * R) * kHeadDim;
-  if (bad_ctx || n == 0) {
+  if constexpr (kChunk) {
+    if (!q_ok || bad_ctx) {
+      // bad segment metadata: flagged, and its rows (when the offsets are
+      // usable) zeroed, as in the chunk kernels
+      if (sp == 0) {
+        if (tid == 0) raise_error(pool.err, !q_ok ? kErrQuery : kErrContext);
+        if (rows_ok) {
+          for (int i = tid; i < qlen * R * kHeadDim; i += 64 * W) {
+            const int row = i / (R * kHeadDim), e = i - row * (R * kHeadDim);
+            a.out[(int64_t(q0) + row) * a.q_stride + g * R * kHeadDim + e] = 0;
+          }
+        }
+      }
+      return;
+    }
+    if (qlen == 0) return;
+  } else if (bad_ctx || n == 0) {
     if (sp == 0) {
       if (bad_ctx && tid == 0) raise_error(pool.err, kErrContext);
       for (int i = tid; i < R * kHeadDim; i += 64 * W) out_bg[i] = 0;
@@ -584,6 +627,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (sp >= ns) return;
   const int k1 = min(n, k0 + a.split_tokens);
+  // keys the lane's column attends in this split: all of them in decode, up
+  // to its token's position in a chunk segment, none for an unused column
+  const int klim = kChunk ? (cvalid ? min(k1, n - qlen + tcol + 1) : k0) : k1;
 
   // Fused step: the new token sits at position n - 1, key o of step
   // patch_step of the last split.  The wave that computes that step norms and
@@ -719,14 +765,16 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     for (int s = 0; s < 4; ++s) s0 = mfma16(ms.k[0][s], qb[s], s0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) s1 = mfma16(ms.k[1][s], qb[s], s1);
-    // the lane's keys key + 8c .. +7: how many are attended
+    // the lane's keys key + 8c .. +7: how many hold data (nv) and how many its
+    // column attends (na)
     const bool okc = (ms.ok >> vhalf) & 1;
     const int nv = okc ? min(max(k1 - (key + 8 * c), 0), 8) : 0;
+    const int na = kChunk ? (okc ? min(max(klim - (key + 8 * c), 0), 8) : 0) : nv;
     float x[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      x[j] = j < nv ? s0[j] * a.qk_scale_log2 : -INFINITY;
-      x[4 + j] = 4 + j < nv ? s1[j] * a.qk_scale_log2 : -INFINITY;
+      x[j] = j < na ? s0[j] * a.qk_scale_log2 : -INFINITY;
+      x[4 + j] = 4 + j < na ? s1[j] * a.qk_scale_log2 : -INFINITY;
     }
     float mx = x[0];
 #pragma unroll
@@ -797,7 +845,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // Column totals: each lane group summed the weights of its own keys.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (col < R) {
+  if (col < C) {
     if (c == 0) {
       s_m[wave][col] = m;
       s_l[wave][col] = l;
@@ -808,7 +856,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
           make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
   }
   __syncthreads();
-  merge_waves<R, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, out_bg);
+  merge_waves<C, W>(s_m, s_l, s_acc, a, b, g, sp, ns == 1, hkv, kChunk ? qlen * R : R, [&](int h) -> uint16_t* {
+    if constexpr (kChunk) {
+      return a.out + (int64_t(q0) + h / R) * a.q_stride + (g * R + h % R) * kHeadDim;
+    } else {
+      return out_bg + h * kHeadDim;
+    }
+  });
 }
 
 // Log-sum-exp combine of the split partials: one workgroup per (sequence,
@@ -874,6 +928,65 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
     o /= L;
   }
   a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(o);
+}
+
+// Log-sum-exp combine of the query-column kernel's split partials: one
+// workgroup per (kv head, column, segment), one thread per dim, splits merged
+// in split order (rows of up to 32 splits: all loads issued at once).
+// Segments that the split kernel rejected, unused columns and rows with one
+// split (written directly) are skipped.
+__global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool, DecodeArgs a) {
+  const int g = blockIdx.x >> 4, col = blockIdx.x & 15, s = blockIdx.y, d = threadIdx.x;
+  const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
+  const int q0 = a.qsl[s], q1 = a.qsl[s + 1], n = a.ctx[s];
+  const int qlen = q1 - q0;
+  const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && qlen <= a.max_q_len && qlen * r <= 16 && n >= qlen &&
+                  n <= a.max_ctx && int64_t(n) <= int64_t(a.bt_stride) * pool.block_size;
+  if (!ok || col >= qlen * r) return;
+  const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  const int64_t unit = int64_t(s) * hkv + g;
+  const float* pl = a.part_lse + unit * a.max_splits * 16 + col;
+  const float* po = a.part_o + (unit * a.max_splits * 16 + col) * kHeadDim + d;
+  uint16_t* dst = a.out + (int64_t(q0) + col / r) * a.q_stride + (g * r + col % r) * kHeadDim + d;
+  if (ns <= kCombineFast) {
+    // every load at once: the partials of the row's splits and one lse per
+    // lane; the weights then go between lanes by shuffle
+    float v[kCombineFast];
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) v[k] = k < ns ? po[int64_t(k) * 16 * kHeadDim] : 0.f;
+    const int lane = d & 63;
+    const float lk = lane < ns ? pl[lane * 16] : -INFINITY;
+    float Mx = lk;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, o));
+    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - Mx);
+    float L = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) {
+      const float ek = __shfl(e, k);
+      if (k < ns) acc += ek * v[k];
+    }
+    *dst = f32_to_bf16(L > 0.f ? acc / L : 0.f);
+    return;
+  }
+  float M = -INFINITY;
+  for (int k = 0; k < ns; ++k) M = fmaxf(M, pl[k * 16]);
+  float o = 0.f;
+  if (M != -INFINITY) {
+    float L = 0.f;
+    for (int k = 0; k < ns; ++k) {
+      const float lk = pl[k * 16];
+      const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+      L += e;
+      o += e * po[int64_t(k) * 16 * kHeadDim];
+    }
+    o /= L;
+  }
+  *dst = f32_to_bf16(o);
 }
 
 // The combine launch that follows the split kernel when the plan has splits.
@@ -942,6 +1055,32 @@ DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int
   w.part_lse_off = w.part_o_off + up(units * max_splits * group * kHeadDim * sizeof(float));
   w.total = w.part_lse_off + up(units * max_splits * group * sizeof(float));
   return w;
+}
+
+// Chunk segments of at most 16 query rows per kv head on the matrix-core
+// kernel (4 waves, cached loads), then the column combine when split.
+template <int R>
+hipError_t launch_columns_r(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
+  hipLaunchKernelGGL((decode_mfma_kernel<R, 4, false, false, true>), grid, dim3(256), 0, stream, pool, a,
+                     StepArgs{});
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_splits == 1) return e;
+  hipLaunchKernelGGL(combine_columns_kernel, dim3(pool.num_kv_heads * 16, a.batch), dim3(kHeadDim), 0, stream, pool,
+                     a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_columns(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
+  if (a.batch == 0) return hipSuccess;
+  if (a.split_tokens > kMaxTilesPerWave * 16 * 4) return hipErrorInvalidValue;
+  switch (a.num_q_heads / pool.num_kv_heads) {
+    case 1: return launch_columns_r<1>(pool, a, stream);
+    case 2: return launch_columns_r<2>(pool, a, stream);
+    case 4: return launch_columns_r<4>(pool, a, stream);
+    case 8: return launch_columns_r<8>(pool, a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {

@@ -43,7 +43,7 @@ struct WriteArgs {
 hipError_t launch_cache_write(const PoolGeom& pool, const WriteArgs& a, hipStream_t stream);
 
 struct DecodeArgs {
-  const uint16_t* q; int64_t q_stride;  // q row stride per sequence, elements
+  const uint16_t* q; int64_t q_stride;  // q row stride per sequence (query token for chunk segments), elements
   const int32_t* ctx;
   const int32_t* bt; int32_t bt_stride;
   int32_t batch; int32_t num_q_heads; int32_t max_ctx;
@@ -51,9 +51,12 @@ struct DecodeArgs {
   int32_t split_tokens; int32_t max_splits; int32_t waves;
   int32_t mfma;          // 1: matrix-core split kernel, 0: dot-product split kernel
   int32_t stream_loads;  // 1: K/V loads carry the non-temporal (streaming) hint
-  float* part_o;         // [batch][Hkv][max_splits][r][128]
+  float* part_o;         // [batch][Hkv][max_splits][r][128] (chunk segments: 16 columns instead of r)
   float* part_lse;       // [batch][Hkv][max_splits][r]
-  uint16_t* out;
+  uint16_t* out;         // [batch][Hq][128] (chunk segments: [total_q][Hq][128], row stride q_stride)
+  // Chunk segments on the matrix-core kernel (launch_decode_columns): batch
+  // counts segments, whose query rows start at qsl[b]; nullptr otherwise.
+  const int32_t* qsl; int32_t total_q; int32_t max_q_len;
 };
 
 // The fused decode step (norm + rotary of the new token's q and k, its cache
@@ -70,6 +73,10 @@ struct StepArgs {
 
 // st == nullptr: plain decode attention over q as given.
 hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream);
+
+// Chunk segments of at most 16 query rows (q_len x group) per kv head on the
+// matrix-core decode kernel, one workgroup per (kv head, segment, split).
+hipError_t launch_decode_columns(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream);
 
 // Workspace carve-up shared by the host API and the launchers.
 struct DecodeWorkspace {

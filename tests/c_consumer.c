@@ -18,13 +18,17 @@ int main(void) {
 
   pgqa_decode_plan dp;
   if (pgqa_plan_decode(256, 16, 64, 8, 16, 2049, &dp) != PGQA_OK) return 1;
-  printf("decode_plan %d %d %d %d\n", dp.split_tokens, dp.max_splits, dp.waves_per_split, dp.load_hint);
+  printf("decode_plan %d %d %d %d %d\n", dp.split_tokens, dp.max_splits, dp.waves_per_split, dp.load_hint,
+         dp.kernel);
   if (pgqa_plan_decode(256, 16, 1, 8, 16, 32769, &dp) != PGQA_OK) return 1;
-  printf("decode_plan %d %d %d %d\n", dp.split_tokens, dp.max_splits, dp.waves_per_split, dp.load_hint);
+  printf("decode_plan %d %d %d %d %d\n", dp.split_tokens, dp.max_splits, dp.waves_per_split, dp.load_hint,
+         dp.kernel);
 
   pgqa_chunk_plan cp;
   if (pgqa_plan_chunk(256, 16, 9, 552, 8, 16, 512, 6656, &cp) != PGQA_OK) return 1;
-  printf("chunk_plan %d %d %d %d\n", cp.split_tokens, cp.max_splits, cp.short_split_tokens, cp.reserved);
+  printf("chunk_plan %d %d %d %d\n", cp.split_tokens, cp.max_splits, cp.short_split_tokens, cp.kernel);
+  if (pgqa_plan_chunk(256, 16, 8, 40, 8, 16, 5, 4096, &cp) != PGQA_OK) return 1;
+  printf("chunk_plan %d %d %d %d\n", cp.split_tokens, cp.max_splits, cp.short_split_tokens, cp.kernel);
 
   if (pgqa_plan_decode(0, 16, 1, 8, 16, 10, &dp) != PGQA_ERR_INVALID_ARG) return 2;
   printf("error %s | %s\n", pgqa_status_string(PGQA_ERR_INVALID_ARG), pgqa_last_error());

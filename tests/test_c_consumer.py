@@ -40,9 +40,13 @@ def test_version_pool_bytes_and_plans(output):
     plans = _line(output, "decode_plan")
     for line, args in zip(plans, [(64, 2049), (1, 32769)]):
         p = pg.plan_decode(256, 16, args[0], 8, 16, args[1])
-        assert line == f"decode_plan {p.split_tokens} {p.max_splits} {p.waves_per_split} {p.load_hint}"
-    c = pg.plan_chunk(256, 16, 9, 552, 8, 16, 512, 6656)
-    assert _line(output, "chunk_plan") == [f"chunk_plan {c.split_tokens} {c.max_splits} {c.short_split_tokens} 0"]
+        assert line == f"decode_plan {p.split_tokens} {p.max_splits} {p.waves_per_split} {p.load_hint} {p.kernel}"
+    want = []
+    for args in [(9, 552, 512, 6656), (8, 40, 5, 4096)]:  # a prefill slice with verify rows; verify rows only
+        c = pg.plan_chunk(256, 16, args[0], args[1], 8, 16, args[2], args[3])
+        want.append(f"chunk_plan {c.split_tokens} {c.max_splits} {c.short_split_tokens} {c.kernel}")
+    assert _line(output, "chunk_plan") == want
+    assert want[0].endswith(" 1") and want[1].endswith(" 2")
 
 
 def test_error_reporting(output):
