@@ -238,11 +238,13 @@ pgqa_status pgqa_decode_step(
 
 /*
  * Split plan of a chunk call.  Rows are (token, query head) pairs of one kv
- * head.  A segment with more than 32 rows per kv head (a prefill slice) is cut
- * into groups of 128 rows that read their keys in splits of split_tokens keys;
- * a segment with at most 32 rows per kv head (verify rows, single tokens) reads
- * its keys in splits of short_split_tokens keys.  Rows with several splits are
- * merged by a log-sum-exp combine.
+ * head.  On the chunk kernels (kernel 0 or 1), a segment with more than 32 rows
+ * per kv head (a prefill slice) is cut into groups of 128 rows that read their
+ * keys in splits of split_tokens keys; a segment with at most 32 rows per kv
+ * head (verify rows, single tokens) reads its keys in splits of
+ * short_split_tokens keys.  A call whose segments all have at most 16 rows per
+ * kv head can instead run on the matrix-core decode kernel (kernel 2).  Rows
+ * with several splits are merged by a log-sum-exp combine.
  */
 typedef struct {
   int32_t split_tokens;        /* a multiple of 32, at most 4096 */
@@ -290,9 +292,11 @@ size_t pgqa_chunk_workspace_bytes(const pgqa_pool* pool, int32_t num_segments, i
  * segment whose metadata is inconsistent gets zero output rows and sets
  * PGQA_DEVERR_QUERY or PGQA_DEVERR_CONTEXT.  A block id outside the pool sets
  * PGQA_DEVERR_BLOCK_ID; the rows that read it are then unspecified (the key is
- * read as zeros, never out of bounds).  The call enqueues the attention kernels
- * for long and short segments (each workgroup derives its own work item from
- * the device metadata) and, with more than one split, the combine.
+ * read as zeros, never out of bounds).  On the chunk kernels the call enqueues
+ * the attention kernels for long and short segments (each workgroup derives its
+ * own work item from the device metadata); with plan kernel 2, the matrix-core
+ * decode kernel over (kv head, segment, split).  With more than one split, the
+ * combine follows.
  */
 pgqa_status pgqa_paged_chunk_attention(
     pgqa_pool* pool,
