@@ -127,9 +127,11 @@ int32_t default_decode_kernel(int32_t r) { return r >= 8 ? 2 : 1; }
 // Keys per split of the decode planner (see pgqa_plan_decode) for `units`
 // (sequence, kv head) pairs of at most ctx keys: one split when that gives at
 // least half a workgroup per CU, else about one workgroup per CU with a floor
-// on the split length (512 keys for the matrix-core kernel, 1024 otherwise,
-// 1536 from 16k keys); a multiple of max(block_size, 64), at most 1024 keys
-// per wave.
+// on the split length (below 16k keys: 384, or 512 for the matrix-core
+// kernel; from 16k keys: 1536, or 768 for the matrix-core kernel); a multiple
+// of max(block_size, 64), at most 1024 keys per wave.  Measured on MI355X:
+// batch 1 at 8k keys (r = 2) 13.2 us at 384-key splits, 16 us and more at
+// 1024; batch 1 at 32k keys 27.0 us at 1536 (r = 2), 22.3 us at 768 (r = 8).
 int64_t decode_split(int32_t num_cus, int32_t block_size, int64_t units, int64_t ctx, bool mfma, int32_t waves) {
   const int64_t gran = block_size > 64 ? block_size : 64;
   const int64_t max_split = std::min<int64_t>(1024ll * waves, kMaxSplitTokens);
@@ -139,7 +141,7 @@ int64_t decode_split(int32_t num_cus, int32_t block_size, int64_t units, int64_t
   } else {
     const int64_t want = (num_cus + units - 1) / units;
     split = round_up((ctx + want - 1) / want, gran);
-    const int64_t floor_split = round_up(ctx >= 16384 ? 1536 : mfma ? 512 : 1024, gran);
+    const int64_t floor_split = round_up(ctx >= 16384 ? (mfma ? 768 : 1536) : (mfma ? 512 : 384), gran);
     if (split < floor_split) split = floor_split;
     if (split > round_up(ctx, gran)) split = round_up(ctx, gran);
   }
@@ -376,12 +378,13 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   // first K/V tile arrives, so long splits win over many short ones.
   //  * one split per (sequence, kv head) when that already gives at least half
   //    a workgroup per CU (no partials, no combine launch);
-  //  * otherwise about one workgroup per CU, with splits of at least 1024 keys
-  //    (1536 for contexts of 16k keys or more: the batch-1 32k-key step is
-  //    fastest at 1536-key splits, 176 workgroups, 6% ahead of 2048);
+  //  * otherwise about one workgroup per CU, with a floor on the split
+  //    length (decode_split: 384 keys, 1536 from 16k keys; the batch-1
+  //    32k-key step is fastest at 1536-key splits, 176 workgroups, 6% ahead
+  //    of 2048);
   //  * 4 waves per workgroup;
   //  * the matrix-core kernel (8 query heads per kv head) was fastest with
-  //    512-key splits below 16k keys (its workgroups start up faster).
+  //    512-key splits below 16k keys and 768 from 16k keys.
   const int32_t r = num_q_heads / num_kv_heads;
   const int32_t kernel = default_decode_kernel(r);
   const int32_t waves = 4;

@@ -865,10 +865,49 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   });
 }
 
+// Log-sum-exp merge of ns split partials of one output element, in split
+// order, for any ns: kCombineFast splits at a time, each group's loads issued
+// at once (one lse per lane, weights exchanged by shuffle), groups merged with
+// a running maximum and sum.  pl / po point at split 0's lse and partial;
+// consecutive splits are lse_stride / o_stride floats apart.  Called by whole
+// waves.
+__device__ __forceinline__ float merge_splits(const float* pl, int64_t lse_stride, const float* po, int64_t o_stride,
+                                              int ns) {
+  const int lane = threadIdx.x & 63;
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int k0 = 0; k0 < ns; k0 += kCombineFast) {
+    float v[kCombineFast];
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) v[k] = k0 + k < ns ? po[(k0 + k) * o_stride] : 0.f;
+    const float lk = lane < kCombineFast && k0 + lane < ns ? pl[(k0 + lane) * lse_stride] : -INFINITY;
+    float mg = lk;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mg = fmaxf(mg, __shfl_xor(mg, o));
+    const float mn = fmaxf(M, mg);
+    if (mn == -INFINITY) continue;  // wave-uniform: no weight yet
+    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - mn);
+    float lg = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lg += __shfl_xor(lg, o);
+    float ag = 0.f;
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) {
+      const float ek = __shfl(e, k);
+      if (k0 + k < ns) ag += ek * v[k];
+    }
+    const float corr = M == -INFINITY ? 0.f : fast_exp2(M - mn);
+    L = L * corr + lg;
+    acc = acc * corr + ag;
+    M = mn;
+  }
+  return L > 0.f ? acc / L : 0.f;
+}
+
 // Log-sum-exp combine of the split partials: one workgroup per (sequence,
 // query head), one thread per dim.  Partials are merged in split order, so
 // the result does not depend on the order in which split workgroups ran.
-// Plans of up to 32 splits issue every load at once (one round trip).
+// Plans of up to 32 splits issue every load at once, before the context
+// length is known (one round trip); longer plans merge 32 splits at a time.
 // A separate launch: the kernel boundary makes the partials visible without
 // per-workgroup cache write-back fences.
 __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, DecodeArgs a) {
@@ -914,25 +953,12 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
   if (n <= 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * pool.block_size) return;
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (ns <= 1) return;  // written directly by the split kernel
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, pl[k * r]);
-  float o = 0.f;
-  if (M != -INFINITY) {
-    float L = 0.f;
-    for (int k = 0; k < ns; ++k) {
-      const float lk = pl[k * r];
-      const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
-      L += e;
-      o += e * po[int64_t(k) * r * kHeadDim];
-    }
-    o /= L;
-  }
-  a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(o);
+  a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(merge_splits(pl, r, po, int64_t(r) * kHeadDim, ns));
 }
 
 // Log-sum-exp combine of the query-column kernel's split partials: one
 // workgroup per (kv head, column, segment), one thread per dim, splits merged
-// in split order (rows of up to 32 splits: all loads issued at once).
+// in split order (merge_splits).
 // Segments that the split kernel rejected, unused columns and rows with one
 // split (written directly) are skipped.
 __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool, DecodeArgs a) {
@@ -948,45 +974,8 @@ __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool
   const int64_t unit = int64_t(s) * hkv + g;
   const float* pl = a.part_lse + unit * a.max_splits * 16 + col;
   const float* po = a.part_o + (unit * a.max_splits * 16 + col) * kHeadDim + d;
-  uint16_t* dst = a.out + (int64_t(q0) + col / r) * a.q_stride + (g * r + col % r) * kHeadDim + d;
-  if (ns <= kCombineFast) {
-    // every load at once: the partials of the row's splits and one lse per
-    // lane; the weights then go between lanes by shuffle
-    float v[kCombineFast];
-#pragma unroll
-    for (int k = 0; k < kCombineFast; ++k) v[k] = k < ns ? po[int64_t(k) * 16 * kHeadDim] : 0.f;
-    const int lane = d & 63;
-    const float lk = lane < ns ? pl[lane * 16] : -INFINITY;
-    float Mx = lk;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) Mx = fmaxf(Mx, __shfl_xor(Mx, o));
-    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - Mx);
-    float L = e;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < kCombineFast; ++k) {
-      const float ek = __shfl(e, k);
-      if (k < ns) acc += ek * v[k];
-    }
-    *dst = f32_to_bf16(L > 0.f ? acc / L : 0.f);
-    return;
-  }
-  float M = -INFINITY;
-  for (int k = 0; k < ns; ++k) M = fmaxf(M, pl[k * 16]);
-  float o = 0.f;
-  if (M != -INFINITY) {
-    float L = 0.f;
-    for (int k = 0; k < ns; ++k) {
-      const float lk = pl[k * 16];
-      const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
-      L += e;
-      o += e * po[int64_t(k) * 16 * kHeadDim];
-    }
-    o /= L;
-  }
-  *dst = f32_to_bf16(o);
+  a.out[(int64_t(q0) + col / r) * a.q_stride + (g * r + col % r) * kHeadDim + d] =
+      f32_to_bf16(merge_splits(pl, 16, po, 16 * kHeadDim, ns));
 }
 
 // The combine launch that follows the split kernel when the plan has splits.

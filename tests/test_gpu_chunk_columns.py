@@ -279,3 +279,17 @@ def test_columns_random_steps(seed):
     out = _call(run, q, plan)
     assert run.pool.check_errors() == 0
     compare(out, run.oracle_chunk_on_gpu_inputs(q), f"seed {seed}")
+
+
+def test_columns_many_splits():
+    """Query-column calls with more than 32 splits (merged 32 at a time)."""
+    spec = _spec("colmany", 1727, 16, 8, 16, [(3000, 5), (4990, 8), (64, 1), (2047, 3)], 1024)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    plan = _columns_plan(64, int(w.chk_ctx.max()))
+    assert plan.max_splits > 64
+    out = _call(run, q, plan)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_chunk_on_gpu_inputs(q), "columns, many splits")

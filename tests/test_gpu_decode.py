@@ -297,3 +297,20 @@ def test_unsupported_group_size_is_rejected():
             pg.paged_chunk_attention(run.pool, q, dev_i32(np.array([0, 1, 2], dtype=np.int32)), run.dec_ctx,
                                      run.dec_bt, 1, 8, SCALE)
 
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_decode_many_splits(kernel):
+    """Plans of more than 32 splits (merged 32 at a time): 64-key splits over
+    contexts up to 5000 keys (79 splits), block boundaries included."""
+    w = make_step(StepSpec("many", 985, 16, 8, 1536, decode=(Group(1, 0, 0), Group(1, 63, 63), Group(1, 2047, 2047),
+                                                              Group(1, 2048, 2048), Group(3, 3000, 4999))))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    mx = int(w.dec_ctx.max())
+    plan = pg.DecodePlan(64, -(-mx // 64), 4, 0, kernel)
+    assert plan.max_splits > 64
+    out = run.decode(plan=plan, q=q)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_decode_on_gpu_inputs(q), f"many splits kernel={kernel}")
