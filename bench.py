@@ -552,8 +552,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-row measurements of the other workloads")
-    ap.add_argument("--only", choices=["chunk"], default=None,
-                    help="profiling aid: run only the mixed workload's rows (chunk attention) and print them")
+    ap.add_argument("--only", choices=["chunk", "cfg4"], default=None,
+                    help="profiling aid: run only one workload's rows and print them (chunk: the mixed "
+                         "workload, chunk attention included; cfg4: the Qwen3-30B-A3B decode step)")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 256 MiB plain copy (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -570,9 +571,11 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
-    if args.only == "chunk":
-        # profiling aid: only the mixed workload's rows (its decode, write and chunk calls)
-        print(json.dumps({"rows": measure_rows(args, dev, ("cfg5",))}), flush=True)
+    if args.only is not None:
+        # profiling aid: only one workload's rows (its write, decode and, for the
+        # mixed workload, chunk calls)
+        print(json.dumps({"rows": measure_rows(args, dev, ("cfg5",) if args.only == "chunk" else (args.only,))}),
+              flush=True)
         return
     w = make_step(SPECS[args.workload])
     s = w.spec
