@@ -486,7 +486,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
 //   * O^T += V^T P^T, eight products (dims 16t .. 16t+15), k = key of the step:
 //     the weights above are exactly the lane's B operand, and its A operand
 //     (dim 16t + col, keys 8c .. 8c+7) is 16 contiguous bytes of a 16-slot V^T
-//     piece.  Nothing is transposed or exchanged between lanes.
+//     piece.  No operand is transposed or moved between lanes; the only
+//     cross-lane work is the row maximum (when it must rise) and the sums.
 // Each wave takes every W-th 32-key step of the split and keeps the next
 // step's 16 loads in flight while it computes the current one.  At most 256
 // registers per lane, so that two waves share each SIMD at every W.
