@@ -96,3 +96,26 @@ def test_plan_rejects_bad_input():
         pg.plan_decode(0, 16, 1, 8, 16, 100)
     with pytest.raises(pg.PgqaError):
         pg.plan_decode(256, 24, 1, 8, 16, 100)
+
+
+@pytest.mark.parametrize("cus", [256, 80])
+@pytest.mark.parametrize("bs", [16, 64, 256])
+@pytest.mark.parametrize("segs,total_q,max_q,ctx", [(8, 40, 5, 4101), (9, 552, 512, 6656), (64, 64, 1, 2049),
+                                                     (1, 16, 16, 32784), (3, 9, 3, 700), (1, 1, 1, 1)])
+def test_chunk_plan_properties(cus, bs, segs, total_q, max_q, ctx):
+    """The chunk planner takes the query-column route (kernel 2) exactly when
+    every segment fits 16 MFMA columns (max_q_len x group <= 16); its splits
+    then follow the decode kernels' rules, else the chunk kernels' (multiples
+    of 32)."""
+    for hkv, r in ((8, 1), (8, 2), (4, 4), (4, 8)):
+        p = pg.plan_chunk(cus, bs, segs, total_q, hkv, r * hkv, max_q, ctx)
+        if max_q * r <= 16:
+            assert p.kernel == 2
+            assert p.split_tokens % max(bs, 64) == 0 and 0 < p.split_tokens <= 4096
+            assert p.max_splits == -(-ctx // p.split_tokens)
+        else:
+            assert p.kernel == 1
+            short = p.short_split_tokens or p.split_tokens
+            for sp in (p.split_tokens, short):
+                assert sp % 32 == 0 and 0 < sp <= 4096
+            assert p.max_splits >= -(-ctx // min(p.split_tokens, short))
