@@ -15,7 +15,7 @@ from harness import SCALE, bits_of, compare, dev_bf16, dev_i32
 
 pytestmark = pytest.mark.gpu
 
-NB, BS, HKV, HQ, MAXB, MBS = 64, 16, 8, 16, 4, 8   # pool blocks, block size, heads, max batch, blocks/seq
+NB, BS, MAXB, MBS = 64, 16, 4, 8   # pool blocks, block size, max batch, blocks/seq
 EPS, THETA = 1e-6, 1e6
 
 
@@ -23,35 +23,36 @@ def _bf16(rng, shape):
     return torch.from_numpy(rng.standard_normal(shape)).to(torch.bfloat16).to("cuda")
 
 
-def _pools(rng, n):
-    k = torch.from_numpy(rng.standard_normal((NB, BS, HKV, 128))).to(torch.bfloat16)
-    v = torch.from_numpy(rng.standard_normal((NB, BS, HKV, 128))).to(torch.bfloat16)
+def _pools(rng, n, hkv):
+    k = torch.from_numpy(rng.standard_normal((NB, BS, hkv, 128))).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((NB, BS, hkv, 128))).to(torch.bfloat16)
     out = []
     for _ in range(n):
-        p = pg.Pool(NB, BS, HKV)
+        p = pg.Pool(NB, BS, hkv)
         p.fill_logical(k.view(torch.int16).numpy(), v.view(torch.int16).numpy())
         out.append(p)
     return out
 
 
 @pytest.mark.parametrize("fused", [True, False])
-def test_decode_graph_replays_match_eager_calls(fused):
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])  # the dot-product and the matrix-core split kernel
+def test_decode_graph_replays_match_eager_calls(fused, hq, hkv):
     """Graphs of the fused step (one launch per layer) or of the two calls,
     against the two eager calls: the fused step is bit-identical to them."""
     rng = np.random.default_rng(31)
     L = 2
     state = rng.bit_generator.state
-    pools_g = _pools(rng, L)
+    pools_g = _pools(rng, L, hkv)
     rng.bit_generator.state = state
-    pools_e = _pools(rng, L)
+    pools_e = _pools(rng, L, hkv)
     wq = torch.from_numpy(1 + 0.1 * rng.standard_normal(128)).to(torch.bfloat16).cuda()
     wk = torch.from_numpy(1 + 0.1 * rng.standard_normal(128)).to(torch.bfloat16).cuda()
     pad = NB - 1
-    graphs = DecodeGraphs(pools_g, HQ, MBS, pad, wq, wk, EPS, THETA, SCALE, MAXB, buckets=[1, 2, 4], fused=fused)
+    graphs = DecodeGraphs(pools_g, hq, MBS, pad, wq, wk, EPS, THETA, SCALE, MAXB, buckets=[1, 2, 4], fused=fused)
     assert graphs.bucket_for(3) == 4 and graphs.bucket_for(5) is None
     perm = rng.permutation(NB - 1)  # block ids for the sequences; the pad block is never dealt
     for step, B in enumerate([3, 4, 1, 3, 2]):
-        print(f"[graph] fused={fused} step {step} batch {B}", flush=True)
+        print(f"[graph] fused={fused} heads {hq}/{hkv} step {step} batch {B}", flush=True)
         bucket = graphs.bucket_for(B)
         ctx = rng.integers(1, MBS * BS + 1, size=B).astype(np.int32)
         bt = np.full((B, MBS), -1, dtype=np.int32)
@@ -59,7 +60,7 @@ def test_decode_graph_replays_match_eager_calls(fused):
             nblk = -(-int(ctx[i]) // BS)
             bt[i, :nblk] = perm[i * MBS: i * MBS + nblk]
         pos = ctx - 1
-        q, k, v = _bf16(rng, (L, B, HQ, 128)), _bf16(rng, (L, B, HKV, 128)), _bf16(rng, (L, B, HKV, 128))
+        q, k, v = _bf16(rng, (L, B, hq, 128)), _bf16(rng, (L, B, hkv, 128)), _bf16(rng, (L, B, hkv, 128))
         ctx_d, bt_d, pos_d = dev_i32(ctx), dev_i32(bt), dev_i32(pos)
         seq_d = dev_i32(np.arange(B))
         # eager calls with the bucket's plan
