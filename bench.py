@@ -491,8 +491,10 @@ def stream_read_ceiling(dev, nbytes: int, copies: int = 4):
             "frac_hbm_peak": round(nbytes / pct["median"] / 1e3 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(w, seconds: float):
-    """The fp64 reference decode, timed on the host on a bounded sample of sequences."""
+def cpu_baseline(w, seconds: float, sample=None):
+    """The fp64 reference decode, timed on the host on a bounded sample of sequences.
+    With `sample` (one fused step's q_out, output and cache read back from the
+    GPU), the same reference also checks three of that step's output rows."""
     import numpy as np
     import oracle as O
 
@@ -531,12 +533,21 @@ def cpu_baseline(w, seconds: float):
                   "sample": f"{d1} sequences, BLAS limited to 1 thread, {e1:.1f} s wall"}
     except Exception:
         pass
+    parity = None
+    if sample is not None:
+        rows = sample["rows"]
+        ref = O.decode_attention(O.bf16_bits_to_f64(sample["q_bits"])[rows], sample["k_bits"], sample["v_bits"],
+                                 sample["block_tables"][rows], w.dec_ctx[rows], sample["scale"])
+        got = O.bf16_bits_to_f64(sample["out_bits"])[rows]
+        d = np.abs(got - ref)
+        parity = {"rows": rows, "max_abs": float(d.max()), "mean_rel": float(d.sum() / np.abs(ref).sum())}
     return {
         "value": nbytes / el / 1e9, "unit": "GB/s", "seqs_per_s": done / el, "cores": int(threads),
         "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
         "sample": f"{done} sequences of this step's decode batch (cycled), fp64 numpy reference, "
                   f"{el:.1f} s wall",
         "single_thread": single,
+        "parity_sample": parity,
     }
 
 
@@ -661,24 +672,23 @@ def main():
     launch_gbs = step_bytes / (step_ms * 1e-3) / 1e9
     two_bytes = dec_bytes + wr_bytes
 
-    # sampled parity of one fused step (q_out requested so the reference sees the q the kernel used)
-    import oracle as O
-
-    fused_pool = pools[0]
-    pg.decode_step(fused_pool, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, plan=plan,
-                   workspace=ws, out=out, q_out=q_out)
-    torch.cuda.synchronize()
-    rows = [0, w.num_decode // 2, w.num_decode - 1]
-    k_all, v_all = fused_pool.read_logical(blocks=w.used_blocks)
-    inv = np.full(s.num_blocks, -1, dtype=np.int64)
-    inv[w.used_blocks] = np.arange(len(w.used_blocks))
-    bt_c = np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1)
-    q_gpu = O.bf16_bits_to_f64(q_out.view(torch.int16).cpu().numpy().view(np.uint16))
-    ref = O.decode_attention(q_gpu[rows], k_all.numpy().view(np.uint16), v_all.numpy().view(np.uint16),
-                             bt_c[rows], w.dec_ctx[rows], scale)
-    got = O.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))[rows]
-    d = np.abs(got - ref)
-    parity = {"rows": rows, "max_abs": float(d.max()), "mean_rel": float(d.sum() / np.abs(ref).sum())}
+    # One fused step's outputs for the sampled parity check of the cpu_baseline
+    # leg (q_out requested so the reference sees the q the kernel used).
+    sample = None
+    if not args.no_cpu_baseline:
+        fused_pool = pools[0]
+        pg.decode_step(fused_pool, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, plan=plan,
+                       workspace=ws, out=out, q_out=q_out)
+        torch.cuda.synchronize()
+        k_all, v_all = fused_pool.read_logical(blocks=w.used_blocks)
+        inv = np.full(s.num_blocks, -1, dtype=np.int64)
+        inv[w.used_blocks] = np.arange(len(w.used_blocks))
+        sample = {"rows": [0, w.num_decode // 2, w.num_decode - 1],
+                  "q_bits": q_out.view(torch.int16).cpu().numpy().view(np.uint16),
+                  "out_bits": out.view(torch.int16).cpu().numpy().view(np.uint16),
+                  "k_bits": k_all.numpy().view(np.uint16), "v_bits": v_all.numpy().view(np.uint16),
+                  "block_tables": np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1),
+                  "scale": scale}
 
     launch_dist = percentiles(per_launch_us(lambda i: fused[i % args.layers](), args.steps, args.layers))
     ceiling = stream_read_ceiling(dev, step_bytes) if not args.main_only else None
@@ -727,7 +737,6 @@ def main():
             "write_us": round(write_ms * 1e3, 3), "decode_us": round(decode_ms * 1e3, 3),
             "decode_gbs": round(dec_bytes / (decode_ms * 1e-3) / 1e9, 2),
         },
-        "parity_sample": parity,
     }
     if args.calibrate_copy:
         result["copy_calibration"] = copy_calibration(dev)
@@ -739,7 +748,7 @@ def main():
         result["rows"]["block_size"] = measure_block_sizes(dev)
         result["rows"]["serving_decode_stall"] = measure_serving(dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)
     print(json.dumps(result), flush=True)
 
 
