@@ -314,3 +314,48 @@ def test_decode_many_splits(kernel):
     out = run.decode(plan=plan, q=q)
     assert run.pool.check_errors() == 0
     compare(out, run.oracle_decode_on_gpu_inputs(q), f"many splits kernel={kernel}")
+
+
+@pytest.mark.parametrize("bs", [16, 64])
+def test_cache_write_runs_of_consecutive_positions(bs):
+    """Token lists as prefill chunks and mixed steps produce them: runs of
+    consecutive positions of one sequence that fill a 16-slot V^T piece or not,
+    unaligned, interrupted by another sequence, reversed, at the ends of the
+    list.  The cache must hold exactly the oracle's bits for V (K within
+    tolerance), and no other slot may change."""
+    hq, hkv, nb = 16, 8, 64
+    rng = np.random.default_rng(77 + bs)
+    nblk = 8
+    perm = rng.permutation(nb)
+    bt = perm[: 4 * nblk].reshape(4, nblk).astype(np.int32)
+    toks = []                                                   # (seq, pos) in list order
+    toks += [(0, p) for p in range(0, 16)]                      # complete run, list start
+    toks += [(1, p) for p in range(3, 19)]                      # 16 positions, not aligned
+    toks += [(2, p) for p in range(32, 48)][:7] + [(3, 5)] + [(2, p) for p in range(39, 48)]  # interrupted
+    toks += [(3, p) for p in range(47, 31, -1)]                 # a full run, reversed
+    toks += [(0, p) for p in range(16, 31)]                     # 15 of a run
+    toks += [(2, p) for p in range(64, 80)]                     # complete run
+    toks += [(1, p) for p in range(96, 112)]                    # complete run at the end of the list
+    seq = np.array([s for s, _ in toks], dtype=np.int32)
+    pos = np.array([p for _, p in toks], dtype=np.int32)
+    T = len(toks)
+    q = O.f64_to_bf16_bits(rng.standard_normal((T, hq, 128)))
+    k = O.f64_to_bf16_bits(rng.standard_normal((T, hkv, 128)))
+    v = O.f64_to_bf16_bits(rng.standard_normal((T, hkv, 128)))
+    wq = O.f64_to_bf16_bits(1 + 0.1 * rng.standard_normal(128))
+    wk = O.f64_to_bf16_bits(1 + 0.1 * rng.standard_normal(128))
+    pool = pg.Pool(nb, bs, hkv)
+    sent = np.full((nb, bs, hkv, 128), SENTINEL, dtype=np.uint16)
+    pool.fill_logical(sent.view(np.int16), sent.view(np.int16))
+    pg.rms_norm_rope_cache_write(pool, dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_bf16(wq), dev_bf16(wk),
+                                 dev_i32(pos), dev_i32(seq), dev_i32(bt), 1e-6, 1e6)
+    assert pool.check_errors() == 0
+    pk, pv = sent.copy(), sent.copy()
+    _, k_ref = O.fused_norm_rope_write(q, k, v, wq, wk, pos, seq, bt, 1e-6, 1e6, pk, pv)
+    kk, vv = pool.read_logical()
+    assert np.array_equal(vv.numpy().view(np.uint16), pv)      # V: every slot bit-exact
+    kg = kk.numpy().view(np.uint16)
+    written = np.any(pk != SENTINEL, axis=(2, 3))
+    assert np.array_equal(np.any(kg != SENTINEL, axis=(2, 3)), written)
+    blk, off = O.slot_of(pos, seq, bt, bs)
+    compare(torch.from_numpy(kg[blk, off].view(np.int16)).view(torch.bfloat16), k_ref, f"run write K bs={bs}")
