@@ -107,7 +107,7 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
     to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     scale = 1.0 / math.sqrt(128)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    rows = {"decode": {}, "cache_write": {}}
+    rows = {"decode": {}, "decode_step": {}, "cache_write": {}}
     for name in names:
         w = make_step(SPECS[name])
         s = w.spec
@@ -140,6 +140,18 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                                 "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
                                          "waves": plan.waves_per_split,
                                          "kernel": "mfma" if plan.kernel == 2 else "dot"}}
+        # the same decode rows as one fused pgqa_decode_step launch (norm + rotary
+        # + cache write + decode) on the raw q, k, v of their new tokens
+        dsel = torch.from_numpy(w.dec_tok.astype(np.int64)).to(dev)
+        qr, kr, vr = q[dsel].contiguous(), k[dsel].contiguous(), v[dsel].contiguous()
+        fcalls = [pg.bind_decode_step(p, qr, kr, vr, to_bf16(w.wq), to_bf16(w.wk), ctx, bt, mx, s.eps, s.rope_theta,
+                                      scale, out, plan=plan) for p in pools]
+        fmed, _ = time_calls(fcalls, 40)
+        nbf = step_alg_bytes(w)
+        rows["decode_step"][name] = {"batch": w.num_decode, "us": round(fmed, 2), "alg_bytes": nbf,
+                                     "gbs": round(nbf / fmed / 1e3, 1),
+                                     "frac_hbm_peak": round(nbf / fmed / 1e3 / HBM_PEAK_GBS, 4),
+                                     "kernel": "mfma" if plan.kernel == 2 else "dot"}
         if name == "cfg5":
             qc = q_out[w.chk_tok0:].contiguous()
             res = {}
