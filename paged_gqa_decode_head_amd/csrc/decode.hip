@@ -846,7 +846,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // Column totals: each lane group summed the weights of its own keys.
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (col < C) {
+  if (col < (kChunk ? qlen * R : R)) {  // the columns the merge reads
     if (c == 0) {
       s_m[wave][col] = m;
       s_l[wave][col] = l;
@@ -957,14 +957,21 @@ __global__ __launch_bounds__(kHeadDim) void combine_kernel(PoolGeom pool, Decode
   a.out[(int64_t(b) * a.num_q_heads + h) * kHeadDim + d] = f32_to_bf16(merge_splits(pl, r, po, int64_t(r) * kHeadDim, ns));
 }
 
+// Columns a query-column call can use: max_q_len x group, between 1 and 16.
+__host__ __device__ inline int columns_of(const DecodeArgs& a, int r) {
+  const int64_t c = int64_t(a.max_q_len) * r;
+  return c < 1 ? 1 : c < 16 ? int(c) : 16;
+}
+
 // Log-sum-exp combine of the query-column kernel's split partials: one
 // workgroup per (kv head, column, segment), one thread per dim, splits merged
 // in split order (merge_splits).
 // Segments that the split kernel rejected, unused columns and rows with one
 // split (written directly) are skipped.
 __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool, DecodeArgs a) {
-  const int g = blockIdx.x >> 4, col = blockIdx.x & 15, s = blockIdx.y, d = threadIdx.x;
   const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
+  const int cols = columns_of(a, r);
+  const int g = blockIdx.x / cols, col = blockIdx.x - g * cols, s = blockIdx.y, d = threadIdx.x;
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1], n = a.ctx[s];
   const int qlen = q1 - q0;
   const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && qlen <= a.max_q_len && qlen * r <= 16 && n >= qlen &&
@@ -1056,8 +1063,8 @@ hipError_t launch_columns_r(const PoolGeom& pool, const DecodeArgs& a, hipStream
                      StepArgs{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
-  hipLaunchKernelGGL(combine_columns_kernel, dim3(pool.num_kv_heads * 16, a.batch), dim3(kHeadDim), 0, stream, pool,
-                     a);
+  hipLaunchKernelGGL(combine_columns_kernel, dim3(pool.num_kv_heads * columns_of(a, R), a.batch), dim3(kHeadDim), 0,
+                     stream, pool, a);
   return hipGetLastError();
 }
 
