@@ -687,8 +687,8 @@ def main():
     # One fused step's outputs for the sampled parity check of the cpu_baseline
     # leg (q_out requested so the reference sees the q the kernel used).
     sample = None
+    fused_pool = pools[0]
     if not args.no_cpu_baseline:
-        fused_pool = pools[0]
         pg.decode_step(fused_pool, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, plan=plan,
                        workspace=ws, out=out, q_out=q_out)
         torch.cuda.synchronize()
