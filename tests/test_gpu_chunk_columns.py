@@ -250,7 +250,7 @@ def test_columns_plan_rejected_when_segments_do_not_fit():
         assert e.value.status == pg.PGQA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(24))
 def test_columns_random_steps(seed):
     """Seeded random verify-like calls: head layouts, block sizes, prefixes at
     block boundaries, q_len up to the 16-column limit (empty and single-token

@@ -359,3 +359,39 @@ def test_cache_write_runs_of_consecutive_positions(bs):
     assert np.array_equal(np.any(kg != SENTINEL, axis=(2, 3)), written)
     blk, off = O.slot_of(pos, seq, bt, bs)
     compare(torch.from_numpy(kg[blk, off].view(np.int16)).view(torch.bfloat16), k_ref, f"run write K bs={bs}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_cases_both_kernels(seed):
+    """Seeded random decode batches (head layouts, block sizes, contexts at
+    block boundaries and up to 5000 keys, random split plans, waves and load
+    hints) on both split kernels, against the fp64 reference; the two kernels
+    agree within the same tolerance."""
+    rng = np.random.default_rng(9500 + seed)
+    hq, hkv = [(16, 8), (32, 4), (8, 8), (32, 8), (8, 1), (16, 4)][int(rng.integers(6))]
+    bs = int(rng.choice([16, 32, 64, 128, 256]))
+    nseq = int(rng.integers(1, 17))
+    picks = [0, bs - 1, bs, bs + 1, 2 * bs - 1, int(rng.integers(1, 5000)), int(rng.integers(1, 600))]
+    lens = [int(picks[int(rng.integers(len(picks)))]) for _ in range(nseq)]
+    nblocks = sum(-(-(L + 1) // bs) for L in lens) + 4
+    w = make_step(StepSpec(f"drand-{seed}", 9600 + seed, hq, hkv, nblocks,
+                           decode=tuple(Group(1, L, L) for L in lens), block_size=bs))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    mx = int(w.dec_ctx.max())
+    gran = max(64, bs)
+    split = min(gran * int(rng.integers(1, 17)), 4096 // gran * gran)
+    waves = int(rng.choice([1, 2, 4, 8]))
+    split = min(split, 1024 * waves // gran * gran)
+    hint = int(rng.integers(3))
+    ref = run.oracle_decode_on_gpu_inputs(q)
+    outs = []
+    for kernel in KERNELS:
+        plan = pg.DecodePlan(split, -(-mx // split), waves, hint, kernel)
+        _note(f"[drand] seed {seed}: heads {hq}/{hkv} bs {bs} contexts {w.dec_ctx.tolist()} plan {plan}")
+        out = run.decode(plan=plan, q=q)
+        assert run.pool.check_errors() == 0
+        compare(out, ref, f"seed {seed} kernel {kernel}")
+        outs.append(f64_of(out))
+    assert np.abs(outs[0] - outs[1]).max() <= 2e-2
