@@ -412,3 +412,127 @@ def test_empty_context_gives_zero_row():
     pk = np.zeros((2, 16, 1, 128), dtype=np.uint16)
     o = O.decode_attention(np.ones((1, 2, 128)), pk, pk, np.array([[0]]), [0], 0.1)
     assert np.all(o == 0)
+
+
+# ---------------------------------------------------------------- a1+a2+a3 composed
+def _fused_case_rows(case, key):
+    D = case["head_dim"]
+    row = np.zeros(D)
+    for i, v in case[key].items():
+        row[int(i)] = v
+    return row
+
+
+def test_fused_write_closed_forms():
+    """Norm before rotary, each row with its own weight: hand-derived values."""
+    for case in _golden()["fused_write"]:
+        D = case["head_dim"]
+        x = _fused_case_rows(case, "x_nonzero")
+        wq = np.ones(D)
+        wk = np.ones(D)
+        for i, v in case["w_nonzero"].items():
+            wq[int(i)] = v
+        for i, v in case["k_w_nonzero"].items():
+            wk[int(i)] = v
+        bits = O.f64_to_bf16_bits
+        assert np.array_equal(O.bf16_bits_to_f64(bits(x)), x)      # exactly representable
+        pk = np.zeros((2, 16, 1, D), dtype=np.uint16)
+        pv = pk.copy()
+        q_out, k_out = O.fused_norm_rope_write(
+            bits(x)[None, None], bits(x)[None, None], bits(x)[None, None], bits(wq), bits(wk),
+            np.array([case["position"]]), np.array([0]), np.array([[1]]), case["eps"], case["theta"],
+            pk, pv)
+        for name, got in (("q_out_nonzero", q_out[0, 0]), ("k_out_nonzero", k_out[0, 0])):
+            want = _fused_case_rows(case, name)
+            # dims outside pair 0 stay exactly 0; pair 0 matches the closed form
+            assert np.allclose(got, want, rtol=1e-14, atol=1e-14), name
+        assert np.array_equal(pk[1, 1, 0], bits(k_out[0, 0]))
+
+
+def _qwen3_attention(hq, hkv, D, wq, wk):
+    """A Qwen3 attention layer whose projections select slices of the hidden row.
+
+    hidden = [q | k | v] (hq*D + 2*hkv*D values), so the layer's q, k and v are
+    exactly the given rows, and o_proj returns the attention output unchanged in
+    the first hq*D dims.  Everything else is the model's own code path: its
+    q_norm/k_norm modules, then its rotary helper, then its cache update and
+    eager attention.
+    """
+    from transformers import Qwen3Config
+    from transformers.models.qwen3.modeling_qwen3 import Qwen3Attention
+
+    hidden = hq * D + 2 * hkv * D
+    cfg = Qwen3Config(hidden_size=hidden, num_attention_heads=hq, num_key_value_heads=hkv,
+                      head_dim=D, rms_norm_eps=1e-6, attention_bias=False, attention_dropout=0.0)
+    cfg._attn_implementation = "eager"
+    layer = Qwen3Attention(cfg, layer_idx=0).double().eval()
+    eye = torch.eye(hidden, dtype=torch.float64)
+    with torch.no_grad():
+        layer.q_proj.weight.copy_(eye[: hq * D])
+        layer.k_proj.weight.copy_(eye[hq * D: (hq + hkv) * D])
+        layer.v_proj.weight.copy_(eye[(hq + hkv) * D:])
+        layer.o_proj.weight.copy_(eye[:, : hq * D])
+        layer.q_norm.weight.copy_(torch.from_numpy(wq))
+        layer.k_norm.weight.copy_(torch.from_numpy(wk))
+    return layer
+
+
+@pytest.mark.parametrize("hq,hkv,start", [(16, 8, 0), (32, 4, 1500)])
+def test_fused_write_matches_qwen3_attention_layer(hq, hkv, start):
+    """q_out/k_out and the attention built on them against the model's own layer.
+
+    The layer's cache holds its k after norm and rotary; its output depends on
+    q after norm and rotary.  Different q and k weights catch a swapped weight;
+    weights far from 1 in both halves of each rotary pair catch a weight
+    applied after the rotation.
+    """
+    from transformers.cache_utils import DynamicCache
+
+    rng = np.random.default_rng(17 + hq)
+    D, T, eps, theta = 128, 12, 1e-6, 1e6
+    bits = O.f64_to_bf16_bits
+    q = bits(rng.standard_normal((T, hq, D)))
+    k = bits(rng.standard_normal((T, hkv, D)))
+    v = bits(rng.standard_normal((T, hkv, D)))
+    wq = bits(1 + 0.3 * rng.standard_normal(D))
+    wk = bits(1 + 0.3 * rng.standard_normal(D))
+    pos = np.arange(start, start + T)
+    # the oracle: one fused write of the T tokens into a small shuffled pool
+    bs = 16
+    nb = -(-(start + T) // bs) + 2
+    bt = rng.permutation(nb)[None, : -(-(start + T) // bs)]
+    pk = np.zeros((nb, bs, hkv, D), dtype=np.uint16)
+    pv = pk.copy()
+    q_out, k_out = O.fused_norm_rope_write(q, k, v, wq, wk, pos, np.zeros(T, dtype=np.int64), bt,
+                                           eps, theta, pk, pv)
+    # the model: fp64 rotary tables from fp64 angles (the frequency itself is
+    # pinned against the model's in test_rope_matches_qwen3_rotary)
+    f64 = O.bf16_bits_to_f64
+    layer = _qwen3_attention(hq, hkv, D, f64(wq), f64(wk))
+    ang = pos[:, None].astype(np.float64) * O.rope_inv_freq(D, theta)[None, :]
+    emb = np.concatenate([ang, ang], axis=-1)
+    cos, sin = torch.from_numpy(np.cos(emb))[None], torch.from_numpy(np.sin(emb))[None]
+    x = np.concatenate([f64(q).reshape(T, -1), f64(k).reshape(T, -1), f64(v).reshape(T, -1)], axis=1)
+    mask = torch.full((T, T), -math.inf, dtype=torch.float64).triu(1)[None, None]
+    cache = DynamicCache()
+    with torch.no_grad():
+        out, _ = layer(torch.from_numpy(x)[None], (cos, sin), mask, past_key_values=cache)
+    model_k = cache.layers[0].keys[0].permute(1, 0, 2).numpy()        # [T, hkv, D]
+    # Qwen3RMSNorm normalises in fp32, hence the 1e-5 bound
+    assert np.allclose(k_out, model_k, rtol=0, atol=2e-5)
+    # the attention of every token over the tokens up to itself, from the oracle's
+    # unrounded q_out / k_out (the model's cache keeps k unrounded too)
+    r = hq // hkv
+    ref = np.zeros((T, hq, D))
+    for t in range(T):
+        for h in range(hq):
+            ref[t, h] = O.attend(q_out[t, h], k_out[: t + 1, h // r], f64(v)[: t + 1, h // r],
+                                 1 / math.sqrt(D))
+    got = out[0, :, : hq * D].reshape(T, hq, D).numpy()
+    assert np.allclose(got, ref, rtol=0, atol=2e-5)
+    # and q_out itself from the model's q_norm module and rotary helper
+    from transformers.models.qwen3.modeling_qwen3 import apply_rotary_pos_emb
+    with torch.no_grad():
+        qn = layer.q_norm(torch.from_numpy(f64(q))).permute(1, 0, 2)[None]
+        qr, _ = apply_rotary_pos_emb(qn, qn, cos, sin, unsqueeze_dim=1)
+    assert np.allclose(q_out, qr[0].permute(1, 0, 2).numpy(), rtol=0, atol=2e-5)
