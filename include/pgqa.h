@@ -237,6 +237,40 @@ pgqa_status pgqa_decode_step(
     void* q_out, void* out, void* stream);
 
 /*
+ * The fused decode step above for callers that cannot allocate device memory
+ * or own a workspace: code recorded under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments, results and errors are
+ * those of pgqa_decode_step (same kernels, bit-identical outputs for the same
+ * plan), without the workspace arguments.
+ *
+ * The split partials go to a fixed device array of PGQA_NOALLOC_SCRATCH_BYTES
+ * that is part of the library's code object: every GPU that loads the library
+ * holds one copy until the process ends.  The call allocates and frees
+ * nothing; on its first call on a device it looks up that device's copy once.
+ * The partials need no initial contents, so nothing is cleared.
+ *
+ * A plan whose partials (pgqa_decode_workspace_bytes) exceed the array returns
+ * PGQA_ERR_WORKSPACE before anything is enqueued.  The library's default plans
+ * stay far below it (a batch-1 call at 32768 keys needs about 0.2 MiB).
+ * All calls on one GPU share its array: two calls whose kernels may overlap on
+ * one GPU (different streams, or graphs replayed concurrently) race on it and
+ * give undefined results; order them on one stream.
+ */
+#define PGQA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+pgqa_status pgqa_decode_step_noalloc(
+    pgqa_pool* pool,
+    const void* q, int64_t q_row_stride,
+    const void* k, int64_t k_row_stride,
+    const void* v, int64_t v_row_stride,
+    const void* q_norm_weight, const void* k_norm_weight,
+    float eps, double rope_theta,
+    const int32_t* context_lens, const int32_t* block_tables, int32_t bt_stride,
+    int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+    float scale, const pgqa_decode_plan* plan,
+    void* q_out, void* out, void* stream);
+
+/*
  * Split plan of a chunk call.  Rows are (token, query head) pairs of one kv
  * head.  On the chunk kernels (kernel 0 or 1), a segment with more than 32 rows
  * per kv head (a prefill slice) is cut into groups of 128 rows that read their

@@ -91,6 +91,8 @@ _SIGNATURES = {
                                      _P, _SZ, _P, _P], ctypes.c_int),
     "pgqa_decode_step": ([_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _F32, _F64, _P, _P, _I32, _I32, _I32, _I32,
                           _F32, ctypes.POINTER(DecodePlan), _P, _SZ, _P, _P, _P], ctypes.c_int),
+    "pgqa_decode_step_noalloc": ([_P, _P, _I64, _P, _I64, _P, _I64, _P, _P, _F32, _F64, _P, _P, _I32, _I32, _I32,
+                                  _I32, _F32, ctypes.POINTER(DecodePlan), _P, _P, _P], ctypes.c_int),
     "pgqa_plan_chunk": ([_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)],
                         ctypes.c_int),
     "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)], _SZ),
@@ -365,6 +367,31 @@ def decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens,
         block_tables.shape[1], B, hq, int(max_context_len), float(scale), pp, _ptr(workspace),
         workspace.numel() * workspace.element_size(), None if q_out is None else _ptr(q_out), _ptr(out),
         _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # PGQA_NOALLOC_SCRATCH_BYTES
+
+
+def decode_step_noalloc(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens, block_tables,
+                        max_context_len: int, eps: float, rope_theta: float, scale: float, out,
+                        plan: DecodePlan = None, q_out=None, stream=None):
+    """pgqa_decode_step_noalloc: the fused decode step with its split partials in
+    the library's fixed per-GPU scratch; ``out`` (and ``q_out``) are the caller's,
+    nothing is allocated.  Calls that overlap on one GPU race on the scratch."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
+        if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != 128):
+            raise ValueError(f"{name}: heads must be contiguous 128-element rows")
+    _require(out, "out", torch.bfloat16, pool.device)
+    pp = None if plan is None else ctypes.byref(plan)
+    _check(lib().pgqa_decode_step_noalloc(
+        pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
+        _ptr(k_norm_weight), float(eps), float(rope_theta), _ptr(context_lens), _ptr(block_tables),
+        block_tables.shape[1], q.shape[0], q.shape[1], int(max_context_len), float(scale), pp,
+        None if q_out is None else _ptr(q_out), _ptr(out), _stream(stream)))
     return out
 
 

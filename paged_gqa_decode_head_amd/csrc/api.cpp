@@ -24,6 +24,8 @@
 
 using namespace pgqa;
 
+static_assert(kNoAllocScratchBytes == PGQA_NOALLOC_SCRATCH_BYTES, "fixed decode scratch size");
+
 struct pgqa_pool {
   pgqa_pool_config cfg;
   PoolGeom geom;
@@ -419,7 +421,8 @@ namespace {
 pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, const int32_t* context_lens,
                           const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
                           int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
-                          size_t workspace_bytes, void* out, void* stream, const StepArgs* st) {
+                          size_t workspace_bytes, void* out, void* stream, const StepArgs* st,
+                          bool static_scratch = false) {
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   if (batch < 0 || batch > 65535) return fail(PGQA_ERR_INVALID_ARG, "batch=%d", batch);
@@ -447,7 +450,13 @@ pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, 
   PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
   PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
   PGQA_TRY(check_device_ptr(out, dev, "out"));
-  if (wl.total > 0) {
+  if (static_scratch) {
+    if (wl.total > workspace_bytes)
+      return fail(PGQA_ERR_WORKSPACE,
+                  "the split partials of this plan need %zu bytes, more than the %zu-byte fixed scratch of the "
+                  "allocation-free decode step (use a plan with fewer splits or pgqa_decode_step with a workspace)",
+                  wl.total, workspace_bytes);
+  } else if (wl.total > 0) {
     if (workspace == nullptr || workspace_bytes < wl.total)
       return fail(PGQA_ERR_WORKSPACE, "decode workspace of %zu bytes needed, %zu given", wl.total,
                   workspace == nullptr ? size_t(0) : workspace_bytes);
@@ -493,13 +502,14 @@ pgqa_status pgqa_paged_decode_attention(pgqa_pool* pool, const void* q, const in
                        num_q_heads, max_context_len, scale, plan, workspace, workspace_bytes, out, stream, nullptr);
 }
 
-pgqa_status pgqa_decode_step(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
-                             int64_t k_row_stride, const void* v, int64_t v_row_stride, const void* q_norm_weight,
-                             const void* k_norm_weight, float eps, double rope_theta, const int32_t* context_lens,
-                             const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
-                             int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
-                             size_t workspace_bytes, void* q_out, void* out, void* stream) {
-  clear_error();
+namespace {
+
+pgqa_status decode_step_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
+                               int64_t k_row_stride, const void* v, int64_t v_row_stride, const void* q_norm_weight,
+                               const void* k_norm_weight, float eps, double rope_theta, const int32_t* context_lens,
+                               const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
+                               int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
+                               size_t workspace_bytes, void* q_out, void* out, void* stream, bool static_scratch) {
   PGQA_TRY(check_pool(pool));
   PGQA_TRY(check_group(pool, num_q_heads));
   const int64_t hkv = pool->cfg.num_kv_heads;
@@ -528,7 +538,39 @@ pgqa_status pgqa_decode_step(pgqa_pool* pool, const void* q, int64_t q_row_strid
   st.q_out = static_cast<uint16_t*>(q_out);
   rope_table(pool, rope_theta, st.rev_freq);
   return decode_common(pool, q, q_row_stride, context_lens, block_tables, bt_stride, batch, num_q_heads,
-                       max_context_len, scale, plan, workspace, workspace_bytes, out, stream, &st);
+                       max_context_len, scale, plan, workspace, workspace_bytes, out, stream, &st, static_scratch);
+}
+
+}  // namespace
+
+pgqa_status pgqa_decode_step(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
+                             int64_t k_row_stride, const void* v, int64_t v_row_stride, const void* q_norm_weight,
+                             const void* k_norm_weight, float eps, double rope_theta, const int32_t* context_lens,
+                             const int32_t* block_tables, int32_t bt_stride, int32_t batch, int32_t num_q_heads,
+                             int32_t max_context_len, float scale, const pgqa_decode_plan* plan, void* workspace,
+                             size_t workspace_bytes, void* q_out, void* out, void* stream) {
+  clear_error();
+  return decode_step_common(pool, q, q_row_stride, k, k_row_stride, v, v_row_stride, q_norm_weight, k_norm_weight,
+                            eps, rope_theta, context_lens, block_tables, bt_stride, batch, num_q_heads,
+                            max_context_len, scale, plan, workspace, workspace_bytes, q_out, out, stream, false);
+}
+
+pgqa_status pgqa_decode_step_noalloc(pgqa_pool* pool, const void* q, int64_t q_row_stride, const void* k,
+                                     int64_t k_row_stride, const void* v, int64_t v_row_stride,
+                                     const void* q_norm_weight, const void* k_norm_weight, float eps,
+                                     double rope_theta, const int32_t* context_lens, const int32_t* block_tables,
+                                     int32_t bt_stride, int32_t batch, int32_t num_q_heads, int32_t max_context_len,
+                                     float scale, const pgqa_decode_plan* plan, void* q_out, void* out,
+                                     void* stream) {
+  clear_error();
+  PGQA_TRY(check_pool(pool));
+  // The fixed scratch of this device (its address is looked up once per device).
+  void* scratch = nullptr;
+  const hipError_t e = noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "address of the fixed decode scratch");
+  return decode_step_common(pool, q, q_row_stride, k, k_row_stride, v, v_row_stride, q_norm_weight, k_norm_weight,
+                            eps, rope_theta, context_lens, block_tables, bt_stride, batch, num_q_heads,
+                            max_context_len, scale, plan, scratch, kNoAllocScratchBytes, q_out, out, stream, true);
 }
 
 pgqa_status pgqa_plan_chunk(int32_t num_cus, int32_t block_size, int32_t num_segments, int32_t total_q,

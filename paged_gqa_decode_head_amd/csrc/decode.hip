@@ -42,6 +42,8 @@
 // far more than the extra launch.)
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 #include "norm_rope.hpp"
@@ -1078,6 +1080,33 @@ hipError_t launch_decode_columns(const PoolGeom& pool, const DecodeArgs& a, hipS
     case 8: return launch_columns_r<8>(pool, a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Split partials of the allocation-free decode step (pgqa_decode_step_noalloc):
+// a fixed array in the code object, so each GPU that loads the library holds
+// one copy until the process ends.  Host code never passes the array's name to
+// a kernel (on the host it is only a stand-in for the symbol); it passes the
+// device address that hipGetSymbolAddress reports for the current device.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {

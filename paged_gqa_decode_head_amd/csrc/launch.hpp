@@ -78,6 +78,12 @@ hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepAr
 // matrix-core decode kernel, one workgroup per (kv head, segment, split).
 hipError_t launch_decode_columns(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream);
 
+// The allocation-free decode step keeps its split partials in a fixed device
+// array of kNoAllocScratchBytes per GPU.  noalloc_scratch returns that array's
+// address on the current device (looked up once per device, thread-safe).
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Workspace carve-up shared by the host API and the launchers.
 struct DecodeWorkspace {
   size_t part_o_off, part_lse_off, total;  // total = 0 when max_splits == 1
