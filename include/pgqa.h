@@ -53,7 +53,8 @@ typedef enum {
 #define PGQA_DEVERR_POSITION 0x2u  /* a position < 0 or past the end of its block-table row */
 #define PGQA_DEVERR_BLOCK_ID 0x4u  /* a block-table entry outside [0, num_blocks) where it is read */
 #define PGQA_DEVERR_CONTEXT  0x8u  /* a context length < 0, past its table row, or above max_context_len */
-#define PGQA_DEVERR_QUERY    0x10u /* query_start_loc not ascending, or a chunk longer than its context or max_q_len */
+#define PGQA_DEVERR_QUERY    0x10u /* query_start_loc not ascending or not ending at total_q, or a chunk longer than
+                                      its context or max_q_len */
 
 /*
  * Paged KV pool configuration.  [P3] Summary and file list: the cache is

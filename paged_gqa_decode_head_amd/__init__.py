@@ -158,6 +158,86 @@ def _require(t, name, dtype=None, device=None, contiguous=True):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _shape(t, name, *dims):
+    """t has shape dims (None = any extent); ValueError otherwise."""
+    if t.dim() != len(dims) or any(d is not None and t.shape[i] != d for i, d in enumerate(dims)):
+        want = "[" + ", ".join("*" if d is None else str(d) for d in dims) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+
+
+def _check_decode_inputs(pool, q, context_lens, block_tables, out, fused=None):
+    """Shapes and dtypes of a decode call (or, with fused = (k, v, wq, wk, q_out),
+    a fused decode step) before anything reaches the library."""
+    import torch
+
+    _require(context_lens, "context_lens", torch.int32, pool.device)
+    _require(block_tables, "block_tables", torch.int32, pool.device)
+    B, hq = q.shape[0], q.shape[1]
+    if q.dim() != 3 or q.shape[2] != 128:
+        raise ValueError(f"q has shape {list(q.shape)}, expected [batch, num_q_heads, 128]")
+    _shape(context_lens, "context_lens", B)
+    if block_tables.dim() != 2 or block_tables.shape[0] < B or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables has shape {list(block_tables.shape)}, expected [>= {B}, >= 1]")
+    if out is not None:
+        _require(out, "out", torch.bfloat16, pool.device)
+        _shape(out, "out", B, hq, 128)
+    if fused is not None:
+        k, v, wq, wk, q_out = fused
+        hkv = pool.num_kv_heads
+        for name, t in (("k", k), ("v", v)):
+            if t.shape[0] < B or (t.dim() == 3 and tuple(t.shape[1:]) != (hkv, 128)) or \
+                    (t.dim() == 2 and t.shape[1] < hkv * 128) or t.dim() not in (2, 3):
+                raise ValueError(f"{name} has shape {list(t.shape)}, expected [{B}, {hkv}, 128] rows")
+        for name, t in (("q_norm_weight", wq), ("k_norm_weight", wk)):
+            _require(t, name, torch.bfloat16, pool.device)
+            _shape(t, name, 128)
+        if q_out is not None:
+            _require(q_out, "q_out", torch.bfloat16, pool.device)
+            _shape(q_out, "q_out", B, hq, 128)
+
+
+def _check_write_inputs(pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables, q_out):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
+        if t.dim() != 3 or t.shape[2] != 128 or t.stride(2) != 1 or t.stride(1) != 128:
+            raise ValueError(f"{name} must be [T, heads, 128] with dense heads and dims")
+    T = q.shape[0]
+    for name, t in (("k", k), ("v", v)):
+        _shape(t, name, T, pool.num_kv_heads, 128)
+    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        _require(t, name, torch.bfloat16, pool.device)
+        _shape(t, name, 128)
+    for name, t in (("positions", positions), ("seq_ids", seq_ids), ("block_tables", block_tables)):
+        _require(t, name, torch.int32, pool.device)
+    _shape(positions, "positions", T)
+    _shape(seq_ids, "seq_ids", T)
+    if block_tables.dim() != 2 or block_tables.shape[0] < 1 or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables has shape {list(block_tables.shape)}, expected [num_seqs, width]")
+    _require(q_out, "q_out", torch.bfloat16, pool.device)
+    _shape(q_out, "q_out", T, q.shape[1], 128)
+
+
+def _check_chunk_inputs(pool, q, query_start_loc, context_lens, block_tables, out):
+    import torch
+
+    for name, t in (("query_start_loc", query_start_loc), ("context_lens", context_lens),
+                    ("block_tables", block_tables)):
+        _require(t, name, torch.int32, pool.device)
+    if q.dim() != 3 or q.shape[2] != 128:
+        raise ValueError(f"q has shape {list(q.shape)}, expected [total_q, num_q_heads, 128]")
+    N = context_lens.shape[0] if context_lens.dim() == 1 else -1
+    if N < 0:
+        raise ValueError(f"context_lens has shape {list(context_lens.shape)}, expected [num_segments]")
+    _shape(query_start_loc, "query_start_loc", N + 1)
+    if block_tables.dim() != 2 or block_tables.shape[0] < N or block_tables.shape[1] < 1:
+        raise ValueError(f"block_tables has shape {list(block_tables.shape)}, expected [>= {N}, >= 1]")
+    if out is not None:
+        _require(out, "out", torch.bfloat16, pool.device)
+        _shape(out, "out", q.shape[0], q.shape[1], 128)
+
+
 def version() -> str:
     return lib().pgqa_version().decode()
 
@@ -280,17 +360,9 @@ def rms_norm_rope_cache_write(pool: Pool, q, k, v, q_norm_weight, k_norm_weight,
     import torch
 
     T, hq = q.shape[0], q.shape[1]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
-        if t.dim() != 3 or t.shape[2] != 128 or t.stride(2) != 1 or t.stride(1) != 128:
-            raise ValueError(f"{name} must be [T, heads, 128] with dense heads and dims")
-    for name, t in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
-        _require(t, name, torch.bfloat16, pool.device)
-    for name, t in (("positions", positions), ("seq_ids", seq_ids), ("block_tables", block_tables)):
-        _require(t, name, torch.int32, pool.device)
     if q_out is None:
         q_out = torch.empty((T, hq, 128), dtype=torch.bfloat16, device=pool.device)
-    _require(q_out, "q_out", torch.bfloat16, pool.device)
+    _check_write_inputs(pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables, q_out)
     _check(lib().pgqa_rms_norm_rope_cache_write(
         pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0),
         _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), _ptr(seq_ids), _ptr(block_tables),
@@ -322,12 +394,10 @@ def paged_decode_attention(pool: Pool, q, context_lens, block_tables, max_contex
     import torch
 
     _require(q, "q", torch.bfloat16, pool.device)
-    _require(context_lens, "context_lens", torch.int32, pool.device)
-    _require(block_tables, "block_tables", torch.int32, pool.device)
+    _check_decode_inputs(pool, q, context_lens, block_tables, out)
     B, hq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device=pool.device)
-    _require(out, "out", torch.bfloat16, pool.device)
     pp = None if plan is None else ctypes.byref(plan)
     need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
     if workspace is None:
@@ -351,12 +421,10 @@ def decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens,
         _require(t, name, torch.bfloat16, pool.device, contiguous=False)
         if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != 128):
             raise ValueError(f"{name}: heads must be contiguous 128-element rows")
-    _require(context_lens, "context_lens", torch.int32, pool.device)
-    _require(block_tables, "block_tables", torch.int32, pool.device)
+    _check_decode_inputs(pool, q, context_lens, block_tables, out, (k, v, q_norm_weight, k_norm_weight, q_out))
     B, hq = q.shape[0], q.shape[1]
     if out is None:
         out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device=pool.device)
-    _require(out, "out", torch.bfloat16, pool.device)
     pp = None if plan is None else ctypes.byref(plan)
     need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
     if workspace is None:
@@ -385,7 +453,7 @@ def decode_step_noalloc(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, conte
         _require(t, name, torch.bfloat16, pool.device, contiguous=False)
         if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != 128):
             raise ValueError(f"{name}: heads must be contiguous 128-element rows")
-    _require(out, "out", torch.bfloat16, pool.device)
+    _check_decode_inputs(pool, q, context_lens, block_tables, out, (k, v, q_norm_weight, k_norm_weight, q_out))
     pp = None if plan is None else ctypes.byref(plan)
     _check(lib().pgqa_decode_step_noalloc(
         pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
@@ -420,14 +488,11 @@ def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_ta
     import torch
 
     _require(q, "q", torch.bfloat16, pool.device)
-    for name, t in (("query_start_loc", query_start_loc), ("context_lens", context_lens),
-                    ("block_tables", block_tables)):
-        _require(t, name, torch.int32, pool.device)
+    _check_chunk_inputs(pool, q, query_start_loc, context_lens, block_tables, out)
     Tq, hq = q.shape[0], q.shape[1]
     N = context_lens.shape[0]
     if out is None:
         out = torch.empty((Tq, hq, 128), dtype=torch.bfloat16, device=pool.device)
-    _require(out, "out", torch.bfloat16, pool.device)
     pp = None if plan is None else ctypes.byref(plan)
     need = int(lib().pgqa_chunk_workspace_bytes(pool.handle, N, Tq, hq, int(max_q_len), int(max_context_len), pp))
     if workspace is None:
@@ -462,6 +527,7 @@ class BoundCall:
 
 def bind_cache_write(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables,
                      eps: float, rope_theta: float, q_out, stream=None) -> BoundCall:
+    _check_write_inputs(pool, q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables, q_out)
     keep = (q, k, v, q_norm_weight, k_norm_weight, positions, seq_ids, block_tables, q_out)
     args = (pool.handle, _ptr(q), q.stride(0), _ptr(k), k.stride(0), _ptr(v), v.stride(0), _ptr(q_norm_weight),
             _ptr(k_norm_weight), _ptr(positions), _ptr(seq_ids), _ptr(block_tables), block_tables.shape[1],
@@ -472,6 +538,10 @@ def bind_cache_write(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, position
 
 def bind_decode(pool: Pool, q, context_lens, block_tables, max_context_len: int, scale: float, out,
                 plan: DecodePlan = None, workspace=None, stream=None) -> BoundCall:
+    import torch
+
+    _require(q, "q", torch.bfloat16, pool.device)
+    _check_decode_inputs(pool, q, context_lens, block_tables, out)
     B, hq = q.shape[0], q.shape[1]
     pp = None if plan is None else ctypes.byref(plan)
     need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
@@ -487,6 +557,13 @@ def bind_decode(pool: Pool, q, context_lens, block_tables, max_context_len: int,
 def bind_decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_lens, block_tables,
                      max_context_len: int, eps: float, rope_theta: float, scale: float, out, plan: DecodePlan = None,
                      workspace=None, q_out=None, stream=None) -> BoundCall:
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _require(t, name, torch.bfloat16, pool.device, contiguous=False)
+        if t.stride(-1) != 1 or (t.dim() == 3 and t.stride(1) != 128):
+            raise ValueError(f"{name}: heads must be contiguous 128-element rows")
+    _check_decode_inputs(pool, q, context_lens, block_tables, out, (k, v, q_norm_weight, k_norm_weight, q_out))
     B, hq = q.shape[0], q.shape[1]
     pp = None if plan is None else ctypes.byref(plan)
     need = int(lib().pgqa_decode_workspace_bytes(pool.handle, B, hq, max_context_len, pp))
@@ -503,6 +580,10 @@ def bind_decode_step(pool: Pool, q, k, v, q_norm_weight, k_norm_weight, context_
 
 def bind_chunk(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int, max_context_len: int,
                scale: float, out, plan: ChunkPlan = None, workspace=None, stream=None) -> BoundCall:
+    import torch
+
+    _require(q, "q", torch.bfloat16, pool.device)
+    _check_chunk_inputs(pool, q, query_start_loc, context_lens, block_tables, out)
     Tq, hq = q.shape[0], q.shape[1]
     N = context_lens.shape[0]
     pp = None if plan is None else ctypes.byref(plan)

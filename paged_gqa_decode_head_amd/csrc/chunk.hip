@@ -104,7 +104,9 @@ __device__ __forceinline__ SegInfo seg_info(const ChunkArgs& a, int s, int r, in
   si.n = a.ctx[s];
   si.qlen = q1 - si.q0;
   const bool rows_ok = si.q0 >= 0 && q1 >= si.q0 && q1 <= a.total_q;
-  const bool q_ok = rows_ok && si.qlen <= a.max_q_len && si.n >= si.qlen;
+  // the last segment must end at total_q: the host sized the call's work lists from total_q
+  const bool end_ok = s + 1 < a.num_segments || q1 == a.total_q;
+  const bool q_ok = rows_ok && end_ok && si.qlen <= a.max_q_len && si.n >= si.qlen;
   const bool c_ok = si.n <= a.max_ctx && int64_t(si.n) <= int64_t(a.bt_stride) * bs;
   si.bad = !(q_ok && c_ok);
   si.err = !q_ok ? kErrQuery : !c_ok ? kErrContext : 0u;
@@ -139,16 +141,23 @@ __device__ __forceinline__ int wide_kend(const SegInfo& si, int grp, int r) {
 // K/V stream.
 enum ListKind { kWideList, kShortList, kCombineList };
 
+// Whether the host launched the short-item kernel: not for a call whose lone
+// segment is wide by its host-side size (chunk_lists).  A bad segment whose
+// claimed rows fit one tile is then zeroed by a wide-list item instead.
+__device__ __forceinline__ bool short_launched(const ChunkArgs& a, int r) {
+  return !(a.num_segments == 1 && int64_t(a.total_q) * r > kRows);
+}
+
 template <ListKind K>
 __device__ __forceinline__ int list_count(const ChunkArgs& a, const SegInfo& si, int r, int hkv) {
   if (K == kWideList) {
-    if (si.bad) return si.claimed_tiles > 1 ? hkv : 0;
+    if (si.bad) return si.claimed_tiles > 1 || !short_launched(a, r) ? hkv : 0;
     if (si.tiles <= 1) return 0;
     int cnt = 0;
     for (int grp = 0; grp < wide_groups(si); ++grp) cnt += cdiv(wide_kend(si, grp, r), a.split_wide);
     return cnt * hkv;
   } else if (K == kShortList) {
-    if (si.bad) return si.claimed_tiles == 1 ? hkv : 0;
+    if (si.bad) return si.claimed_tiles == 1 && short_launched(a, r) ? hkv : 0;
     return si.tiles == 1 ? hkv * cdiv(si.n, a.split_short) : 0;
   } else {
     if (si.tiles == 0) return 0;

@@ -563,7 +563,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     const int q1 = a.qsl[b + 1];
     qlen = q1 - q0;
     rows_ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q;
-    q_ok = rows_ok && qlen <= a.max_q_len && qlen * R <= 16 && n >= qlen;
+    q_ok = rows_ok && (b + 1 < a.batch || q1 == a.total_q) && qlen <= a.max_q_len && qlen * R <= 16 && n >= qlen;
   }
   const int tcol = col / R;  // chunk: the column's token in the segment
   const bool cvalid = kChunk ? q_ok && tcol < qlen : col < R;
@@ -976,7 +976,8 @@ __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool
   const int g = blockIdx.x / cols, col = blockIdx.x - g * cols, s = blockIdx.y, d = threadIdx.x;
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1], n = a.ctx[s];
   const int qlen = q1 - q0;
-  const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && qlen <= a.max_q_len && qlen * r <= 16 && n >= qlen &&
+  const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && (s + 1 < a.batch || q1 == a.total_q) &&
+                  qlen <= a.max_q_len && qlen * r <= 16 && n >= qlen &&
                   n <= a.max_ctx && int64_t(n) <= int64_t(a.bt_stride) * pool.block_size;
   if (!ok || col >= qlen * r) return;
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;

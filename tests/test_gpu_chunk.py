@@ -199,6 +199,39 @@ def test_chunk_bad_metadata_flags_and_zero_rows():
     assert run.pool.check_errors() == 0
 
 
+def test_chunk_last_offset_must_equal_total_q():
+    """A lone segment whose offsets end before total_q: the host sized the call
+    as one wide segment (40 tokens, 80 rows per kv head), the device offsets
+    claim 10 tokens (20 rows, one tile).  The segment is flagged and its
+    claimed rows zeroed; nothing reads stale partials."""
+    spec = _chunk_spec("cend", 726, 16, 8, 16, [(30, 40)], 16)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    out = torch.full((40, 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    qsl = dev_i32(np.array([0, 10], dtype=np.int32))
+    _note("[chunk] lone segment ending before total_q")
+    pg.paged_chunk_attention(run.pool, q, qsl, run.chk_ctx, run.chk_bt, 40, 70, SCALE, out=out)
+    assert run.pool.check_errors() & pg.DEVERR_QUERY
+    assert torch.all(out[:10] == 0)
+    assert torch.all(out[10:] == 3.0)
+    # the same on the query-column route (two short segments, the last ending early)
+    spec = _chunk_spec("cend2", 727, 16, 8, 16, [(30, 5), (12, 5)], 16)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    out = torch.full((10, 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    qsl = dev_i32(np.array([0, 5, 8], dtype=np.int32))
+    pg.paged_chunk_attention(run.pool, q, qsl, run.chk_ctx, run.chk_bt, 5, 35, SCALE, out=out,
+                             plan=pg.ChunkPlan(64, 1, 0, 2))
+    assert run.pool.check_errors() & pg.DEVERR_QUERY
+    assert torch.all(out[5:8] == 0)
+    good = run.oracle_chunk_on_gpu_inputs(q)
+    compare(out[:5], good[:5], "good segment before the bad one")
+
+
 @pytest.mark.parametrize("q_len", [5, 40])  # a short (verify-sized) and a wide segment
 def test_chunk_addressing_probe_one_hot_every_position(q_len):
     """Only key j* matches every query strongly: each query that sees j* must
