@@ -77,15 +77,40 @@ def chunk_alg(w, qsl, ctx):
     return 4 * 128 * s.num_q_heads * pairs, kv
 
 
-def time_calls(calls, iters, warmup=3):
-    """Median and mean microseconds of each call (HIP events on the current stream)."""
+FLUSH_BYTES = 1 << 30   # 4x the 256 MB Infinity Cache
+
+
+class CacheFlush:
+    """A read of FLUSH_BYTES (torch's sum over a buffer of ones, ordinary cached
+    loads) before a timed launch, so that launch finds neither its K/V in the
+    Infinity Cache nor its metadata in L2: every row is then an HBM figure, as
+    in a model step where the other layers' K/V passes between two uses of one
+    layer's cache."""
+
+    def __init__(self, dev):
+        import torch
+
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        import torch
+
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def time_calls_cold(calls, iters, flush, warmup=3):
+    """Median and mean microseconds of each call, each launch preceded by the
+    cache flush (HIP events around the launch only, on the current stream)."""
     import torch
 
     for i in range(warmup):
+        flush()
         calls[i % len(calls)]()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i in range(iters):
+        flush()
         ev[i][0].record()
         calls[i % len(calls)]()
         ev[i][1].record()
@@ -96,7 +121,8 @@ def time_calls(calls, iters, warmup=3):
 
 def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
     """Every hot-path row on its own synthetic workload: decode on each decode
-    workload, chunk attention (slice, verify rows, both) on the mixed step."""
+    workload, chunk attention (slice, verify rows, both) on the mixed step.
+    Every timed launch follows a 1 GiB cache flush (cold Infinity Cache and L2)."""
     import numpy as np
     import torch
 
@@ -107,12 +133,15 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
     to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     scale = 1.0 / math.sqrt(128)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    rows = {"decode": {}, "decode_step": {}, "cache_write": {}}
+    rows = {"decode": {}, "decode_step": {}, "cache_write": {}, "timing": "median of per-launch HIP events, each "
+            "launch after a 1 GiB read that evicts the 256 MB Infinity Cache and L2 (cold caches)"}
+    flush = CacheFlush(dev)
+    time_calls = lambda calls, iters: time_calls_cold(calls, iters, flush)  # noqa: E731
     for name in names:
         w = make_step(SPECS[name])
         s = w.spec
         pools = []
-        for _ in range(2):
+        for _ in range(1):
             p = pg.Pool(s.num_blocks, s.block_size, s.num_kv_heads, device=dev)
             p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
                            blocks=w.used_blocks)
@@ -179,6 +208,8 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
             rows["chunk_cfg5"] = res
         del pools
         torch.cuda.empty_cache()
+    del flush
+    torch.cuda.empty_cache()
     return rows
 
 
@@ -277,7 +308,9 @@ def measure_block_sizes(dev, sizes=(16, 32, 64, 128, 256)):
     to_bf16 = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     scale = 1.0 / math.sqrt(128)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    res = {}
+    res = {"timing": "median of per-launch HIP events, each launch after a 1 GiB cache flush"}
+    flush = CacheFlush(dev)
+    time_calls = lambda calls, iters: time_calls_cold(calls, iters, flush)  # noqa: E731
     for bs in sizes:
         row = {}
         for name in ("cfg3b", "cfg5"):
@@ -285,7 +318,7 @@ def measure_block_sizes(dev, sizes=(16, 32, 64, 128, 256)):
             spec = dataclasses.replace(base, block_size=bs, num_blocks=base.num_blocks * base.block_size // bs)
             w = make_step(spec)
             pools = []
-            for _ in range(2):
+            for _ in range(1):
                 p = pg.Pool(spec.num_blocks, bs, spec.num_kv_heads, device=dev)
                 p.fill_logical(w.prefix_k[w.used_blocks].view(np.int16), w.prefix_v[w.used_blocks].view(np.int16),
                                blocks=w.used_blocks)
@@ -323,6 +356,8 @@ def measure_block_sizes(dev, sizes=(16, 32, 64, 128, 256)):
             del pools
             torch.cuda.empty_cache()
         res[str(bs)] = row
+    del flush
+    torch.cuda.empty_cache()
     return res
 
 
@@ -503,62 +538,197 @@ def stream_read_ceiling(dev, nbytes: int, copies: int = 4):
             "frac_hbm_peak": round(nbytes / pct["median"] / 1e3 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(w, seconds: float, sample=None):
-    """The fp64 reference decode, timed on the host on a bounded sample of sequences.
-    With `sample` (one fused step's q_out, output and cache read back from the
-    GPU), the same reference also checks three of that step's output rows."""
+# ---------------------------------------------------------------- cpu baseline
+# The fp64 oracle timed on the host on the same synthetic steps: one process
+# with BLAS at one thread, and a pool of spawned worker processes (created
+# before the first GPU call; they import only numpy and the oracle and never
+# touch the GPU) over (sequence, kv head) and (segment, kv head, query block)
+# units.  The step's arrays reach the workers through shared memory.
+CPU_ROWS = ("cfg2", "cfg3a", "cfg3b", "cfg4", "cfg5_decode", "cfg5_slice", "cfg5_verify")
+_SHM = {}
+
+
+def _cpu_worker_init():
+    """Worker start-up: one BLAS/OpenMP thread per worker process (the pool is
+    the parallelism), set before the worker first imports numpy."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        os.environ[var] = "1"
+
+
+def _cpu_attach(name, shape, dtype):
+    """A numpy view of a shared-memory array (attached once per worker)."""
+    import numpy as np
+    from multiprocessing import shared_memory
+
+    if name not in _SHM:
+        _SHM[name] = shared_memory.SharedMemory(name=name)
+    return np.ndarray(shape, dtype=dtype, buffer=_SHM[name].buf)
+
+
+def _cpu_unit(task):
+    """One unit of the oracle's work on the shared arrays: decode attention of
+    sequence b over kv head g, or chunk attention of query rows [i0, i1) of
+    segment s over kv head g (the rows as a sub-segment that ends at position
+    n - q_len + i1, which is how the chunk rule aligns them)."""
     import numpy as np
     import oracle as O
 
-    try:
-        from threadpoolctl import threadpool_info
+    kind, arrs, scale, r, unit = task
+    q = _cpu_attach(*arrs["q"])
+    pk = _cpu_attach(*arrs["pk"])
+    pv = _cpu_attach(*arrs["pv"])
+    bt = _cpu_attach(*arrs["bt"])
+    ctx = _cpu_attach(*arrs["ctx"])
+    if kind == "decode":
+        b, g = unit
+        o = O.decode_attention(O.bf16_bits_to_f64(q[b:b + 1, g * r:(g + 1) * r]), pk[:, :, g:g + 1],
+                               pv[:, :, g:g + 1], bt[b:b + 1], ctx[b:b + 1], scale)
+    else:
+        qsl = _cpu_attach(*arrs["qsl"])
+        seg, g, i0, i1 = unit
+        q0, qlen, n = int(qsl[seg]), int(qsl[seg + 1] - qsl[seg]), int(ctx[seg])
+        o = O.chunk_attention(O.bf16_bits_to_f64(q[q0 + i0:q0 + i1, g * r:(g + 1) * r]), np.array([0, i1 - i0]),
+                              pk[:, :, g:g + 1], pv[:, :, g:g + 1], bt[seg:seg + 1],
+                              np.array([n - qlen + i1]), scale)
+    return float(np.abs(o).sum())
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+
+def _cpu_step(w, row):
+    """(kind, q bits, compact pool K/V, compact block tables, contexts, qsl,
+    units, algorithmic bytes, sequences or query tokens) of one row's step."""
+    import numpy as np
+
     s = w.spec
-    scale = 1.0 / math.sqrt(128)
-    q = O.bf16_bits_to_f64(w.tok_q[w.dec_tok])
+    inv = np.full(s.num_blocks, -1, dtype=np.int64)
+    inv[w.used_blocks] = np.arange(len(w.used_blocks))
+    bt_c = np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1)
+    pk, pv = w.prefix_k[w.used_blocks], w.prefix_v[w.used_blocks]
+    hkv = s.num_kv_heads
+    if not row.startswith("cfg5") or row == "cfg5_decode":
+        q = w.tok_q[w.dec_tok]
+        ctx = w.dec_ctx
+        units = [(b, g) for b in range(w.num_decode) for g in range(hkv)]
+        work = [int(ctx[b]) for b, _ in units]
+        return ("decode", q, pk, pv, bt_c[: w.num_decode], ctx, None, units, decode_alg_bytes(w), w.num_decode,
+                None, work)
+    qc = w.tok_q[w.chk_tok0:]
+    qsl, ctx, bt = w.chk_qsl, w.chk_ctx, bt_c[w.num_decode:]
+    segs = [0] if row == "cfg5_slice" else list(range(1, len(ctx)))
+    units, work = [], []
+    for seg in segs:
+        ql, n = int(qsl[seg + 1] - qsl[seg]), int(ctx[seg])
+        for g in range(hkv):
+            for i0 in range(0, ql, 32):
+                i1 = min(ql, i0 + 32)
+                units.append((seg, g, i0, i1))
+                work.append(sum(n - ql + i + 1 for i in range(i0, i1)))   # visible (query, key) pairs
+    sel = np.array(segs)
+    flops, kv = chunk_alg(w, np.concatenate([[0], np.cumsum(np.diff(qsl)[sel])]), ctx[sel])
+    tokens = int(np.diff(qsl)[sel].sum())
+    return ("chunk", qc, pk, pv, bt, ctx, qsl, units, kv, tokens, flops, work)
 
-    def run(limit):
-        done, t0 = 0, time.perf_counter()
-        nbytes = 0
-        while True:
-            b = done % w.num_decode
-            O.decode_attention(q[b:b + 1], w.prefix_k, w.prefix_v, w.dec_block_tables[b:b + 1],
-                               w.dec_ctx[b:b + 1], scale)
-            n = int(w.dec_ctx[b])
-            nbytes += n * s.num_kv_heads * 128 * 4 + 2 * s.num_q_heads * 128 * 2 + 4 * (-(-n // s.block_size)) + 4
-            done += 1
-            el = time.perf_counter() - t0
-            if el >= limit:
-                return done, nbytes, el
 
-    done, nbytes, el = run(seconds)
-    single = None
+def cpu_baseline(pool, pool_size, seconds_per_row: float, sample=None):
+    """The oracle on every row's step, one process (BLAS at one thread) and the
+    worker pool; rates from the same algorithmic bytes as the GPU rows."""
+    import numpy as np
+    from multiprocessing import shared_memory
+
+    import oracle as O
+    from paged_gqa_decode_head_amd.workloads import SPECS, make_step
+
     try:
         from threadpoolctl import threadpool_limits
-
-        with threadpool_limits(limits=1):
-            d1, b1, e1 = run(seconds / 2)
-        single = {"value": b1 / e1 / 1e9, "seqs_per_s": d1 / e1, "cores": 1,
-                  "sample": f"{d1} sequences, BLAS limited to 1 thread, {e1:.1f} s wall"}
-    except Exception:
-        pass
+    except ImportError:
+        threadpool_limits = None
+    scale = 1.0 / math.sqrt(128)
+    out = {}
+    for row in CPU_ROWS:
+        w = make_step(SPECS[row.split("_")[0]])
+        st = _cpu_step(w, row)
+        kind, q, pk, pv, bt, ctx, qsl, units, nbytes, count = st[:10]
+        shms, arrs = [], {}
+        for key, a in (("q", q), ("pk", pk), ("pv", pv), ("bt", bt.astype(np.int64)), ("ctx", ctx.astype(np.int64)),
+                       ("qsl", None if qsl is None else qsl.astype(np.int64))):
+            if a is None:
+                continue
+            a = np.ascontiguousarray(a)
+            m = shared_memory.SharedMemory(create=True, size=max(a.nbytes, 1))
+            np.ndarray(a.shape, dtype=a.dtype, buffer=m.buf)[...] = a
+            shms.append(m)
+            arrs[key] = (m.name, a.shape, a.dtype.str)
+        work = st[11]
+        r = w.spec.num_q_heads // w.spec.num_kv_heads
+        tasks = [(kind, arrs, scale, r, u) for u in units]
+        res = {"units": len(units), "alg_bytes": int(nbytes)}
+        if kind == "chunk":
+            res["flops"] = int(st[10])
+        for mode in ("single_thread", "pool"):
+            ctxm = threadpool_limits(limits=1) if threadpool_limits is not None else None
+            if ctxm is not None:
+                ctxm.__enter__()
+            try:
+                if mode == "pool":
+                    # whole steps: one timed, repeated while that took under the row's budget
+                    run = lambda: pool.map(_cpu_unit, tasks, chunksize=max(1, len(tasks) // (4 * pool_size)))
+                    t0 = time.perf_counter()
+                    run()
+                    el, reps = time.perf_counter() - t0, 1
+                    more = min(50, int(seconds_per_row / max(el, 1e-3)))
+                    if more > 0:
+                        t0 = time.perf_counter()
+                        for _ in range(more):
+                            run()
+                        el, reps = (time.perf_counter() - t0) / more, more
+                    sampled = 1.0
+                else:
+                    # units in a strided order until the budget is spent; the
+                    # step's time is extrapolated by the share of its (query,
+                    # key) pairs done (units of one step differ only in length)
+                    order = [i for k in range(7) for i in range(k, len(tasks), 7)]
+                    done_work, reps, t0 = 0, 0, time.perf_counter()
+                    for i in order:
+                        _cpu_unit(tasks[i])
+                        done_work += work[i]
+                        reps += 1
+                        if time.perf_counter() - t0 >= seconds_per_row:
+                            break
+                    sampled = done_work / sum(work)
+                    el = (time.perf_counter() - t0) / sampled
+            finally:
+                if ctxm is not None:
+                    ctxm.__exit__(None, None, None)
+            d = {"s_per_step": round(el, 5), "gbs": round(nbytes / el / 1e9, 3),
+                 "cores": 1 if mode == "single_thread" else pool_size,
+                 "steps_timed" if mode == "pool" else "units_timed": reps,
+                 "share_of_step_timed": round(min(sampled, 1.0) if mode != "pool" else float(reps), 4)}
+            if kind == "decode":
+                d["seqs_per_s"] = round(count / el, 1)
+            else:
+                d["tokens_per_s"] = round(count / el, 1)
+                d["gflops"] = round(st[10] / el / 1e9, 2)
+            res[mode] = d
+        for m in shms:
+            m.close()
+            m.unlink()
+        out[row] = res
     parity = None
     if sample is not None:
         rows = sample["rows"]
         ref = O.decode_attention(O.bf16_bits_to_f64(sample["q_bits"])[rows], sample["k_bits"], sample["v_bits"],
-                                 sample["block_tables"][rows], w.dec_ctx[rows], sample["scale"])
+                                 sample["block_tables"][rows], sample["ctx"][rows], sample["scale"])
         got = O.bf16_bits_to_f64(sample["out_bits"])[rows]
         d = np.abs(got - ref)
         parity = {"rows": rows, "max_abs": float(d.max()), "mean_rel": float(d.sum() / np.abs(ref).sum())}
+    head = out["cfg3b"]["pool"]
     return {
-        "value": nbytes / el / 1e9, "unit": "GB/s", "seqs_per_s": done / el, "cores": int(threads),
+        "value": head["gbs"], "unit": "GB/s", "seqs_per_s": head["seqs_per_s"], "cores": pool_size,
         "host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-        "sample": f"{done} sequences of this step's decode batch (cycled), fp64 numpy reference, "
-                  f"{el:.1f} s wall",
-        "single_thread": single,
+        "sample": "the whole batch-64 Qwen3-1.7B decode step (64 sequences x 8 kv heads), repeated, fp64 numpy "
+                  f"oracle in a pool of {pool_size} spawned processes over (sequence, kv head) units; every other "
+                  "row's step in 'rows' the same way, and in one process with BLAS at one thread on a strided "
+                  "sample of the step's units (share_of_step_timed), extrapolated by (query, key) pairs",
+        "rows": out,
         "parity_sample": parity,
     }
 
@@ -572,12 +742,12 @@ def main():
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--split-tokens", type=int, default=0, help="override the planner's split length")
     ap.add_argument("--waves", type=int, default=0, help="override the planner's waves per split")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=2.0, help="host time budget per cpu_baseline row and mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--main-only", action="store_true", help="skip the per-row measurements of the other workloads")
-    ap.add_argument("--only", choices=["chunk", "cfg4"], default=None,
-                    help="profiling aid: run only one workload's rows and print them (chunk: the mixed "
-                         "workload, chunk attention included; cfg4: the Qwen3-30B-A3B decode step)")
+    ap.add_argument("--only", choices=["cfg2", "cfg3a", "cfg4", "cfg5", "chunk"], default=None,
+                    help="profiling aid: run only one workload's rows and print them (cfg5 or chunk: the mixed "
+                         "workload, chunk attention included)")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 256 MiB plain copy (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -585,6 +755,14 @@ def main():
               "shards by sequence or kv head with no exchange, which this benchmark does not exercise",
               file=sys.stderr)
         sys.exit(2)
+
+    # The oracle's worker processes are spawned before anything touches the GPU.
+    cpu_pool, cpu_pool_size = None, 0
+    if not args.no_cpu_baseline and args.only is None:
+        import multiprocessing as mp
+
+        cpu_pool_size = max(1, min(16, len(os.sched_getaffinity(0))))
+        cpu_pool = mp.get_context("spawn").Pool(cpu_pool_size, initializer=_cpu_worker_init)
 
     import numpy as np
     import torch
@@ -599,6 +777,8 @@ def main():
         # mixed workload, chunk calls)
         print(json.dumps({"rows": measure_rows(args, dev, ("cfg5",) if args.only == "chunk" else (args.only,))}),
               flush=True)
+        if args.calibrate_copy:
+            copy_calibration(dev)
         return
     w = make_step(SPECS[args.workload])
     s = w.spec
@@ -700,7 +880,7 @@ def main():
                   "out_bits": out.view(torch.int16).cpu().numpy().view(np.uint16),
                   "k_bits": k_all.numpy().view(np.uint16), "v_bits": v_all.numpy().view(np.uint16),
                   "block_tables": np.where(w.block_tables >= 0, inv[np.maximum(w.block_tables, 0)], -1),
-                  "scale": scale}
+                  "ctx": w.dec_ctx, "scale": scale}
 
     launch_dist = percentiles(per_launch_us(lambda i: fused[i % args.layers](), args.steps, args.layers))
     ceiling = stream_read_ceiling(dev, step_bytes) if not args.main_only else None
@@ -759,8 +939,10 @@ def main():
         result["rows"]["decode_graph"] = measure_graphs(dev)
         result["rows"]["block_size"] = measure_block_sizes(dev)
         result["rows"]["serving_decode_stall"] = measure_serving(dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sample)
+    if cpu_pool is not None:
+        result["cpu_baseline"] = cpu_baseline(cpu_pool, cpu_pool_size, args.cpu_seconds, sample)
+        cpu_pool.close()
+        cpu_pool.join()
     print(json.dumps(result), flush=True)
 
 
