@@ -344,6 +344,74 @@ pgqa_status pgqa_paged_chunk_attention(
     void* out, void* stream);
 
 /*
+ * One attention launch for a whole mixed serving step: decode rows, chunked-
+ * prefill slices and b x (k+1) speculative-verify rows of one call, from a work
+ * list built on the host.  [P1] Summary items 1 (decode and prefill routed on
+ * the host over one paged cache), 3 (routing decided on the host, no device
+ * synchronisation) and 4 (chunked prefill and the fixed b x (k+1) verify shape
+ * in one forward).
+ *
+ * Semantics are those of pgqa_paged_chunk_attention: segment s owns query rows
+ * query_start_loc[s] .. query_start_loc[s+1]-1 and context_lens[s] keys (its
+ * own tokens included, already in the cache); query i sits at position
+ * n_s - q_len_s + i and attends to keys 0 .. that position.  A decode row is a
+ * segment of one token.
+ *
+ * pgqa_plan_mixed (host only) reads HOST copies of query_start_loc
+ * [num_segments + 1] and context_lens [num_segments] (the step planner has
+ * them) and writes the work list to `items` (host, PGQA_MIXED_ITEM_INTS int32
+ * per item, plan->num_items attention items then plan->num_combine combine
+ * items; item_capacity counts items).  With items = NULL it only fills *out,
+ * so a caller can size its buffer.  Segments with more than 16 query rows per
+ * kv head (q_len x group > 16) become wide items (128 rows over one key split of
+ * split_wide keys, matrix cores), the others query-column items (the segment's
+ * rows as MFMA columns over one split of split_columns keys).  0 for a split
+ * lets the planner choose.  Returns PGQA_ERR_INVALID_ARG for inconsistent host
+ * metadata or a buffer that is too small.
+ *
+ * The caller copies the items to device memory (with its other per-step
+ * metadata) and passes them and the plan to pgqa_paged_mixed_attention, which
+ * enqueues one attention kernel (plan->num_items workgroups) and, when some row
+ * has several splits, one combine kernel.  The workspace (device, caller-owned)
+ * holds >= pgqa_mixed_workspace_bytes bytes of split partials (no initial
+ * contents needed; 0 bytes when plan->max_splits is 1).
+ *
+ * Every item carries the host's offset, length and key count of its segment;
+ * the kernels compare them with the device metadata.  A mismatch, or metadata
+ * that fails the chunk call's checks, sets PGQA_DEVERR_QUERY (or
+ * PGQA_DEVERR_CONTEXT) and zeroes that item's output rows.  Items must come from
+ * pgqa_plan_mixed for the same metadata: rows that no item covers are not
+ * written.
+ */
+#define PGQA_MIXED_ITEM_INTS 8
+
+typedef struct {
+  int32_t split_wide;     /* keys per split of wide items: a multiple of 32, at most 4096 */
+  int32_t split_columns;  /* keys per split of query-column items: a multiple of max(64, block_size), <= 4096 */
+  int32_t max_splits;     /* partial slots per query row (1: no partials, no combine) */
+  int32_t num_items;      /* attention work items: workgroups of the attention launch */
+  int32_t num_combine;    /* combine items that follow them in the list */
+} pgqa_mixed_plan;
+
+pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_heads, int32_t num_q_heads,
+                            int32_t num_segments, const int32_t* query_start_loc, const int32_t* context_lens,
+                            int32_t split_wide, int32_t split_columns, int32_t* items, int64_t item_capacity,
+                            pgqa_mixed_plan* out);
+
+/* Device workspace bytes of a mixed call with this plan. */
+size_t pgqa_mixed_workspace_bytes(const pgqa_mixed_plan* plan, int32_t total_q, int32_t num_q_heads);
+
+pgqa_status pgqa_paged_mixed_attention(
+    pgqa_pool* pool,
+    const void* q, const int32_t* query_start_loc, const int32_t* context_lens,
+    const int32_t* block_tables, int32_t bt_stride,
+    int32_t num_segments, int32_t total_q, int32_t num_q_heads,
+    int32_t max_q_len, int32_t max_context_len,
+    float scale, const pgqa_mixed_plan* plan, const int32_t* items,
+    void* workspace, size_t workspace_bytes,
+    void* out, void* stream);
+
+/*
  * Measurement helper, not part of the attention path: a plain streaming read of
  * `bytes` bytes at src (device, 16-byte aligned, bytes a multiple of 16) with
  * 16-byte non-temporal loads in a grid-stride loop, two per thread in flight.

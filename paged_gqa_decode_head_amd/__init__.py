@@ -60,6 +60,18 @@ class ChunkPlan(ctypes.Structure):
                 f"short_split_tokens={self.short_split_tokens})")
 
 
+class MixedPlan(ctypes.Structure):
+    _fields_ = [("split_wide", ctypes.c_int32), ("split_columns", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("num_items", ctypes.c_int32), ("num_combine", ctypes.c_int32)]
+
+    def __repr__(self):
+        return (f"MixedPlan(split_wide={self.split_wide}, split_columns={self.split_columns}, "
+                f"max_splits={self.max_splits}, num_items={self.num_items}, num_combine={self.num_combine})")
+
+
+MIXED_ITEM_INTS = 8   # PGQA_MIXED_ITEM_INTS
+
+
 class SchedConfig(ctypes.Structure):
     _fields_ = [("token_budget", ctypes.c_int32), ("max_segments", ctypes.c_int32),
                 ("chunked_prefill", ctypes.c_int32), ("block_size", ctypes.c_int32),
@@ -98,6 +110,11 @@ _SIGNATURES = {
     "pgqa_chunk_workspace_bytes": ([_P, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(ChunkPlan)], _SZ),
     "pgqa_paged_chunk_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32,
                                     ctypes.POINTER(ChunkPlan), _P, _SZ, _P, _P], ctypes.c_int),
+    "pgqa_plan_mixed": ([_I32, _I32, _I32, _I32, _I32, _P, _P, _I32, _I32, _P, _I64, ctypes.POINTER(MixedPlan)],
+                        ctypes.c_int),
+    "pgqa_mixed_workspace_bytes": ([ctypes.POINTER(MixedPlan), _I32, _I32], _SZ),
+    "pgqa_paged_mixed_attention": ([_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _I32, _F32,
+                                    ctypes.POINTER(MixedPlan), _P, _P, _SZ, _P, _P], ctypes.c_int),
     # host producers (include/pgqa_sched.h)
     "pgqa_prompt_lookup": ([_P, _I32, _I32, _I32, _I32, _P], _I32),
     "pgqa_accept_greedy": ([_P, _I32, _P, _P], _I32),
@@ -502,6 +519,76 @@ def paged_chunk_attention(pool: Pool, q, query_start_loc, context_lens, block_ta
         N, Tq, hq, int(max_q_len), int(max_context_len), float(scale), pp, _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
     return out
+
+def plan_mixed(num_cus, block_size, num_kv_heads, num_q_heads, query_start_loc, context_lens, split_wide=0,
+               split_columns=0):
+    """pgqa_plan_mixed on host copies of the step's metadata: (MixedPlan, int32
+    numpy array [num_items + num_combine, MIXED_ITEM_INTS])."""
+    import numpy as np
+
+    qsl = np.ascontiguousarray(query_start_loc, dtype=np.int32)
+    ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+    if qsl.ndim != 1 or ctx.ndim != 1 or qsl.size != ctx.size + 1:
+        raise ValueError("query_start_loc must hold len(context_lens) + 1 entries")
+    plan = MixedPlan()
+    _check(lib().pgqa_plan_mixed(num_cus, block_size, num_kv_heads, num_q_heads, ctx.size, _np_ptr(qsl),
+                                 _np_ptr(ctx), split_wide, split_columns, None, 0, ctypes.byref(plan)))
+    items = np.zeros((plan.num_items + plan.num_combine, MIXED_ITEM_INTS), dtype=np.int32)
+    if items.size:
+        _check(lib().pgqa_plan_mixed(num_cus, block_size, num_kv_heads, num_q_heads, ctx.size, _np_ptr(qsl),
+                                     _np_ptr(ctx), split_wide, split_columns, _np_ptr(items), items.shape[0],
+                                     ctypes.byref(plan)))
+    return plan, items
+
+
+def mixed_workspace_bytes(plan: MixedPlan, total_q: int, num_q_heads: int) -> int:
+    return int(lib().pgqa_mixed_workspace_bytes(ctypes.byref(plan), total_q, num_q_heads))
+
+
+def _mixed_args(pool, q, query_start_loc, context_lens, block_tables, max_q_len, max_context_len, scale, plan,
+                items, workspace, out, stream):
+    import torch
+
+    _require(q, "q", torch.bfloat16, pool.device)
+    _check_chunk_inputs(pool, q, query_start_loc, context_lens, block_tables, out)
+    _require(items, "items", torch.int32, pool.device)
+    if items.dim() != 2 or items.shape[1] != MIXED_ITEM_INTS or items.shape[0] < plan.num_items + plan.num_combine:
+        raise ValueError(f"items has shape {list(items.shape)}, the plan needs "
+                         f"[{plan.num_items + plan.num_combine}, {MIXED_ITEM_INTS}]")
+    Tq, hq = q.shape[0], q.shape[1]
+    need = mixed_workspace_bytes(plan, Tq, hq)
+    if workspace is None:
+        workspace = pool.workspace(need, "mixed")
+    args = (pool.handle, _ptr(q), _ptr(query_start_loc), _ptr(context_lens), _ptr(block_tables),
+            block_tables.shape[1], context_lens.shape[0], Tq, hq, int(max_q_len), int(max_context_len), float(scale),
+            ctypes.byref(plan), _ptr(items), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+            _stream(stream))
+    return args, workspace
+
+
+def paged_mixed_attention(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int,
+                          max_context_len: int, scale: float, plan: MixedPlan, items, workspace=None, out=None,
+                          stream=None):
+    """One attention launch (plus one combine) for a mixed step from the work
+    list of plan_mixed (``items``: its device copy, int32 [n, 8]); returns out
+    [total_q, Hq, 128] bf16.  Same semantics as paged_chunk_attention."""
+    import torch
+
+    if out is None:
+        out = torch.empty((q.shape[0], q.shape[1], 128), dtype=torch.bfloat16, device=pool.device)
+    args, _ = _mixed_args(pool, q, query_start_loc, context_lens, block_tables, max_q_len, max_context_len, scale,
+                          plan, items, workspace, out, stream)
+    _check(lib().pgqa_paged_mixed_attention(*args))
+    return out
+
+
+def bind_mixed(pool: Pool, q, query_start_loc, context_lens, block_tables, max_q_len: int, max_context_len: int,
+               scale: float, out, plan: MixedPlan, items, workspace=None, stream=None) -> "BoundCall":
+    args, workspace = _mixed_args(pool, q, query_start_loc, context_lens, block_tables, max_q_len, max_context_len,
+                                  scale, plan, items, workspace, out, stream)
+    keep = (q, query_start_loc, context_lens, block_tables, out, items, workspace, plan)
+    return BoundCall(lib().pgqa_paged_mixed_attention, args, keep)
+
 
 def bind_stream_read(src, sink, grid: int = 0, stream=None) -> "BoundCall":
     """pgqa_stream_read over all of ``src`` (a device tensor of a multiple of 16

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpgqa.so")
 
-SOURCES = ["errors.cpp", "api.cpp", "sched.cpp", "cache_write.hip", "decode.hip", "chunk.hip", "stream_read.hip"]
+SOURCES = ["errors.cpp", "api.cpp", "sched.cpp", "cache_write.hip", "decode.hip", "chunk.hip", "mixed.hip",
+           "stream_read.hip"]
 
 ARCH = "gfx950"
 COMMON = [
@@ -28,10 +29,10 @@ COMMON = [
 ]
 # Packed fp32 VALU forms are kept out of the device code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file device options.  chunk.hip: MFMA accumulators in VGPRs rather than
-# AGPRs (the narrow kernel otherwise copies them between the register files
-# around every softmax rescale).
-EXTRA = {"chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file device options.  chunk.hip, mixed.hip: MFMA accumulators in VGPRs
+# rather than AGPRs (the narrow kernel otherwise copies them between the
+# register files around every softmax rescale).
+EXTRA = {"chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "mixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:

@@ -17,6 +17,8 @@
 #include <algorithm>
 #include <mutex>
 #include <new>
+#include <utility>
+#include <vector>
 
 #include "../../include/pgqa.h"
 #include "errors.hpp"
@@ -25,6 +27,7 @@
 using namespace pgqa;
 
 static_assert(kNoAllocScratchBytes == PGQA_NOALLOC_SCRATCH_BYTES, "fixed decode scratch size");
+static_assert(kMixedItemInts == PGQA_MIXED_ITEM_INTS, "mixed work item size");
 
 struct pgqa_pool {
   pgqa_pool_config cfg;
@@ -784,6 +787,217 @@ pgqa_status pgqa_paged_chunk_attention(pgqa_pool* pool, const void* q, const int
   a.out = static_cast<uint16_t*>(out);
   hipError_t e = launch_chunk(pool->geom, a, z.grids, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk launch");
+  return PGQA_OK;
+}
+
+// ---------------------------------------------------------------- mixed step
+namespace {
+
+struct MixedSeg {
+  int32_t s, q0, qlen, n;
+};
+
+// Keys a wide row group grp attends (up to its last query token's position).
+int64_t mixed_wide_kend(int64_t qlen, int64_t n, int64_t r, int64_t grp) {
+  const int64_t tiles = (qlen * r + 31) / 32;
+  const int64_t t_last = std::min((grp + 1) * 4, tiles) - 1;
+  const int64_t tok_last = std::min(qlen, (t_last * 32 + 32) / r) - 1;
+  return n - qlen + tok_last + 1;
+}
+
+}  // namespace
+
+pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_heads, int32_t num_q_heads,
+                            int32_t num_segments, const int32_t* query_start_loc, const int32_t* context_lens,
+                            int32_t split_wide, int32_t split_columns, int32_t* items, int64_t item_capacity,
+                            pgqa_mixed_plan* out) {
+  clear_error();
+  if (out == nullptr) return fail(PGQA_ERR_INVALID_ARG, "out is NULL");
+  if (num_cus <= 0 || !valid_block_size(block_size) || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_segments < 0)
+    return fail(PGQA_ERR_INVALID_ARG, "invalid planner input");
+  const int64_t hkv = num_kv_heads, r = num_q_heads / num_kv_heads;
+  if (r != 1 && r != 2 && r != 4 && r != 8)
+    return fail(PGQA_ERR_UNSUPPORTED, "query heads per kv head = %lld (supported: 1, 2, 4, 8)", (long long)r);
+  if (num_segments > 0 && (query_start_loc == nullptr || context_lens == nullptr))
+    return fail(PGQA_ERR_INVALID_ARG, "host query_start_loc / context_lens are NULL");
+  const int64_t gran = block_size > 64 ? block_size : 64;
+  if (split_wide < 0 || split_wide % kChunkStep || split_wide > kMaxSplitTokens)
+    return fail(PGQA_ERR_INVALID_ARG, "split_wide=%d (0, or a multiple of 32 up to 4096)", split_wide);
+  if (split_columns < 0 || split_columns % gran || split_columns > kMaxSplitTokens)
+    return fail(PGQA_ERR_INVALID_ARG, "split_columns=%d (0, or a multiple of %lld up to 4096)", split_columns,
+                (long long)gran);
+  // Segments by kind: more than 16 query rows per kv head -> wide items.
+  std::vector<MixedSeg> wide, cols;
+  int64_t units_w = 0, keys_c = 0, kend_w = 0, n_c = 0;
+  if (num_segments > 0 && query_start_loc[0] != 0) return fail(PGQA_ERR_INVALID_ARG, "query_start_loc[0] != 0");
+  for (int32_t s = 0; s < num_segments; ++s) {
+    const int32_t q0 = query_start_loc[s], qlen = query_start_loc[s + 1] - q0, n = context_lens[s];
+    if (qlen < 0 || n < qlen)
+      return fail(PGQA_ERR_INVALID_ARG, "segment %d: q_len %d, context %d (need 0 <= q_len <= context)", s, qlen, n);
+    if (qlen == 0) continue;
+    if (int64_t(qlen) * r > 16) {
+      wide.push_back(MixedSeg{s, q0, qlen, n});
+      units_w += (int64_t(qlen) * r + 127) / 128 * hkv;
+      kend_w = std::max<int64_t>(kend_w, n);
+    } else {
+      cols.push_back(MixedSeg{s, q0, qlen, n});
+      keys_c += int64_t(n) * hkv;
+      n_c = std::max<int64_t>(n_c, n);
+    }
+  }
+  // Wide splits: about two items per CU over the (row group, kv head) units,
+  // 256 .. 4096 keys.  Column splits: about two items per CU over all the
+  // columns' (key, kv head) pairs, at least 512 keys.
+  int64_t sw = split_wide, sc = split_columns;
+  if (sw == 0) {
+    sw = 256;
+    if (units_w > 0) {
+      const int64_t want = (2ll * num_cus + units_w - 1) / units_w;
+      sw = std::max<int64_t>(256, round_up((kend_w + want - 1) / want, kChunkStep));
+      sw = std::min<int64_t>({sw, round_up(kend_w, kChunkStep), kMaxSplitTokens});
+    }
+  }
+  if (sc == 0) {
+    sc = round_up(512, gran);
+    if (keys_c > 0) {
+      sc = std::max<int64_t>(round_up(512, gran), round_up((keys_c + 2ll * num_cus - 1) / (2ll * num_cus), gran));
+      sc = std::min<int64_t>({sc, std::max<int64_t>(round_up(n_c, gran), gran), kMaxSplitTokens / gran * gran});
+    }
+  }
+  // Items.  Wide items first, the kv head fastest (workgroups are dealt to the
+  // 8 XCDs round-robin, so one kv head's items share an L2), then column items,
+  // most keys first; then the combine items.
+  struct Item {
+    int32_t v[kMixedItemInts];
+  };
+  std::vector<Item> att, comb;
+  int64_t max_splits = 1;
+  int64_t max_ns_w = 0;
+  for (const MixedSeg& m : wide)
+    max_ns_w = std::max<int64_t>(max_ns_w, (int64_t(m.n) + sw - 1) / sw);
+  for (int64_t sp = 0; sp < max_ns_w; ++sp)
+    for (const MixedSeg& m : wide) {
+      const int64_t groups = ((int64_t(m.qlen) * r + 31) / 32 + 3) / 4;
+      for (int64_t grp = 0; grp < groups; ++grp) {
+        const int64_t ns = (mixed_wide_kend(m.qlen, m.n, r, grp) + sw - 1) / sw;
+        if (sp >= ns) continue;
+        for (int64_t g = 0; g < hkv; ++g)
+          att.push_back(Item{{m.s, 0, int32_t(g), int32_t(grp), int32_t(sp), m.q0, m.qlen, m.n}});
+      }
+    }
+  std::vector<std::pair<int64_t, Item>> citems;
+  for (const MixedSeg& m : cols) {
+    const int64_t ns = (int64_t(m.n) + sc - 1) / sc;
+    for (int64_t sp = 0; sp < ns; ++sp)
+      for (int64_t g = 0; g < hkv; ++g)
+        citems.push_back({std::min<int64_t>(sc, m.n - sp * sc),
+                          Item{{m.s, 1, int32_t(g), 0, int32_t(sp), m.q0, m.qlen, m.n}}});
+  }
+  std::stable_sort(citems.begin(), citems.end(),
+                   [](const std::pair<int64_t, Item>& x, const std::pair<int64_t, Item>& y) { return x.first > y.first; });
+  for (const auto& ci : citems) att.push_back(ci.second);
+  auto add_combine = [&](const MixedSeg& m, int64_t rho0, int64_t rho1, int64_t ns) {
+    max_splits = std::max(max_splits, ns);
+    if (ns < 2) return;
+    for (int64_t g = 0; g < hkv; ++g)
+      for (int64_t rho = rho0; rho < rho1; rho += 8)
+        comb.push_back(Item{{m.s, 2, int32_t(g), int32_t(rho), int32_t(ns), m.q0, m.qlen, m.n}});
+  };
+  for (const MixedSeg& m : wide) {
+    const int64_t rows = int64_t(m.qlen) * r, groups = ((rows + 31) / 32 + 3) / 4;
+    for (int64_t grp = 0; grp < groups; ++grp)
+      add_combine(m, grp * 128, std::min<int64_t>(rows, (grp + 1) * 128),
+                  (mixed_wide_kend(m.qlen, m.n, r, grp) + sw - 1) / sw);
+  }
+  for (const MixedSeg& m : cols) add_combine(m, 0, int64_t(m.qlen) * r, (int64_t(m.n) + sc - 1) / sc);
+  if (att.size() + comb.size() > size_t(0x7fffffff) || max_splits > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "too many mixed work items");
+  out->split_wide = int32_t(sw);
+  out->split_columns = int32_t(sc);
+  out->max_splits = int32_t(max_splits);
+  out->num_items = int32_t(att.size());
+  out->num_combine = int32_t(comb.size());
+  if (items == nullptr) return PGQA_OK;
+  if (item_capacity < int64_t(att.size() + comb.size()))
+    return fail(PGQA_ERR_INVALID_ARG, "item buffer holds %lld items, the plan has %lld", (long long)item_capacity,
+                (long long)(att.size() + comb.size()));
+  int32_t* dst = items;
+  for (const Item& it : att) dst = std::copy(it.v, it.v + kMixedItemInts, dst);
+  for (const Item& it : comb) dst = std::copy(it.v, it.v + kMixedItemInts, dst);
+  return PGQA_OK;
+}
+
+size_t pgqa_mixed_workspace_bytes(const pgqa_mixed_plan* plan, int32_t total_q, int32_t num_q_heads) {
+  if (plan == nullptr || total_q < 0 || num_q_heads <= 0 || plan->max_splits < 1) return 0;
+  return chunk_workspace_layout(total_q, num_q_heads, plan->max_splits).total;
+}
+
+pgqa_status pgqa_paged_mixed_attention(pgqa_pool* pool, const void* q, const int32_t* query_start_loc,
+                                       const int32_t* context_lens, const int32_t* block_tables, int32_t bt_stride,
+                                       int32_t num_segments, int32_t total_q, int32_t num_q_heads, int32_t max_q_len,
+                                       int32_t max_context_len, float scale, const pgqa_mixed_plan* plan,
+                                       const int32_t* items, void* workspace, size_t workspace_bytes, void* out,
+                                       void* stream) {
+  clear_error();
+  PGQA_TRY(check_pool(pool));
+  PGQA_TRY(check_group(pool, num_q_heads));
+  if (plan == nullptr) return fail(PGQA_ERR_INVALID_ARG, "plan is NULL (pgqa_plan_mixed builds it)");
+  if (num_segments < 0) return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d", num_segments);
+  if (pool->cfg.max_batch_size > 0 && num_segments > pool->cfg.max_batch_size)
+    return fail(PGQA_ERR_INVALID_ARG, "num_segments=%d exceeds max_batch_size=%d", num_segments,
+                pool->cfg.max_batch_size);
+  if (total_q < 0) return fail(PGQA_ERR_INVALID_ARG, "total_q=%d", total_q);
+  if (bt_stride <= 0) return fail(PGQA_ERR_INVALID_ARG, "bt_stride=%d", bt_stride);
+  if (max_q_len < 0 || max_context_len < max_q_len)
+    return fail(PGQA_ERR_INVALID_ARG, "max_q_len=%d max_context_len=%d", max_q_len, max_context_len);
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PGQA_ERR_INVALID_ARG, "scale=%g", double(scale));
+  const int32_t gran = pool->cfg.block_size > 64 ? pool->cfg.block_size : 64;
+  if (plan->split_wide <= 0 || plan->split_wide % kChunkStep || plan->split_wide > kMaxSplitTokens ||
+      plan->split_columns <= 0 || plan->split_columns % gran || plan->split_columns > kMaxSplitTokens ||
+      plan->max_splits < 1 || plan->max_splits > 65535 || plan->num_items < 0 || plan->num_combine < 0)
+    return fail(PGQA_ERR_INVALID_ARG, "plan (splits %d / %d, max_splits %d, items %d + %d) is not one of "
+                "pgqa_plan_mixed's for this pool", plan->split_wide, plan->split_columns, plan->max_splits,
+                plan->num_items, plan->num_combine);
+  if (num_segments == 0 || total_q == 0 || plan->num_items == 0) return PGQA_OK;
+  const size_t need = pgqa_mixed_workspace_bytes(plan, total_q, num_q_heads);
+  const int dev = pool->device;
+  PGQA_TRY(check_device_ptr(q, dev, "q", 16));
+  PGQA_TRY(check_device_ptr(query_start_loc, dev, "query_start_loc", 4));
+  PGQA_TRY(check_device_ptr(context_lens, dev, "context_lens", 4));
+  PGQA_TRY(check_device_ptr(block_tables, dev, "block_tables", 4));
+  PGQA_TRY(check_device_ptr(items, dev, "items", 16));
+  PGQA_TRY(check_device_ptr(out, dev, "out", 8));
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(PGQA_ERR_WORKSPACE, "mixed workspace of %zu bytes needed, %zu given", need,
+                  workspace == nullptr ? size_t(0) : workspace_bytes);
+    PGQA_TRY(check_device_ptr(workspace, dev, "workspace", 256));
+  }
+  ChunkArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.qsl = query_start_loc;
+  a.ctx = context_lens;
+  a.bt = block_tables;
+  a.bt_stride = bt_stride;
+  a.num_segments = num_segments;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.max_q_len = max_q_len;
+  a.max_ctx = max_context_len;
+  a.qk_scale_log2 = float(double(scale) * 1.4426950408889634);
+  a.split_wide = plan->split_wide;
+  a.split_short = plan->split_columns;
+  a.max_splits = plan->max_splits;
+  const ChunkWorkspace wl = chunk_workspace_layout(total_q, num_q_heads, plan->max_splits);
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = need > 0 ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
+  a.part_lse = need > 0 ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
+  a.out = static_cast<uint16_t*>(out);
+  a.items = items;
+  a.num_items = plan->num_items;
+  hipError_t e = launch_mixed(pool->geom, a, plan->num_combine, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "mixed attention launch");
   return PGQA_OK;
 }
 

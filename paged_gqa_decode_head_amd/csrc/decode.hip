@@ -390,7 +390,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
         tm = fmaxf(tm, dpp<kDppRowMirror>(tm));
         tm = fmaxf(tm, __shfl_xor(tm, 16));
         tm = fmaxf(tm, __shfl_xor(tm, 32));
-        if (tm > m[h]) {
+        // only a head whose own scores left the headroom re-bases (whatever the
+        // other heads did), so each head's result depends on its scores alone
+        if (tm > m[h] + kTau) {
           const float corr = fast_exp2(m[h] - tm);
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[h][j] *= corr;
@@ -493,20 +495,6 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
 // Each wave takes every W-th 32-key step of the split and keeps the next
 // step's 16 loads in flight while it computes the current one.  At most 256
 // registers per lane, so that two waves share each SIMD at every W.
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
-                                                 0, 0, 0);
-}
-
-// Component-wise select.  (A ternary on uint4 values can become a select
-// between their addresses, which keeps the operands out of registers.)
-__device__ __forceinline__ uint4 sel4(bool p, const uint4& x, const uint4& y) {
-  return make_uint4(p ? x.x : y.x, p ? x.y : y.y, p ? x.z : y.z, p ? x.w : y.w);
-}
 
 struct MStep {
   uint4 k[2][4];  // score product u, dim slice s: key row of the lane, dims 32s + 8c .. +7
@@ -785,7 +773,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     if (__ballot(mx > m + kTau)) {
       float tm = fmaxf(mx, __shfl_xor(mx, 16));
       tm = fmaxf(tm, __shfl_xor(tm, 32));
-      if (tm > m) {
+      if (tm > m + kTau) {  // only a column whose own scores left the headroom re-bases
         const float corr = fast_exp2(m - tm);
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[t] *= corr;

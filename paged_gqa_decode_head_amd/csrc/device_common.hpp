@@ -75,4 +75,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// v_mfma_f32_16x16x32_bf16: lane l supplies A[m][k] with m = l%16, k = 8(l/16)+j
+// and B[k][n] with n = l%16; D[i] of lane l is row 4(l/16)+i, column l%16.
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Component-wise select.  (A ternary on uint4 values can become a select
+// between their addresses, which keeps the operands out of registers.)
+__device__ __forceinline__ uint4 sel4(bool p, const uint4& x, const uint4& y) {
+  return make_uint4(p ? x.x : y.x, p ? x.y : y.y, p ? x.z : y.z, p ? x.w : y.w);
+}
+
 }  // namespace pgqa

@@ -100,9 +100,14 @@ struct ChunkArgs {
   int32_t split_wide;    // keys per split, segments of more than 32 rows per kv head
   int32_t split_short;   // keys per split, segments of at most 32 rows per kv head
   int32_t max_splits;    // partial slots per row: covers both split sizes
-  float* part_o;         // [Hkv][max_splits][total_q][r][128]
-  float* part_lse;       // [Hkv][max_splits][total_q][r]
+  float* part_o;         // [max_splits][total_q][Hq][128]
+  float* part_lse;       // [max_splits][total_q][Hq]
   uint16_t* out;
+  // Mixed-step calls (launch_mixed): the host-built work list, kMixedItemInts
+  // int32 per item, num_items attention items followed by the combine items;
+  // split_short is then the key split of the query-column items.
+  const int32_t* items;
+  int32_t num_items;
 };
 
 // Which chunk work lists a call can have: wide (segments of more than 32 rows
@@ -124,6 +129,13 @@ ChunkGrids chunk_grids(int32_t num_segments, int32_t total_q, int32_t num_kv_hea
                        int32_t max_ctx, int32_t split_wide, int32_t split_short, int32_t max_splits);
 
 hipError_t launch_chunk(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream);
+
+// One attention launch (and one combine launch when num_combine > 0) for a
+// mixed step from a host-built work list (items of kMixedItemInts int32:
+// segment, kind, kv head, row group or first combine row, split or split count,
+// and the host's query offset, query length and key count of the segment).
+constexpr int kMixedItemInts = 8;
+hipError_t launch_mixed(const PoolGeom& pool, const ChunkArgs& a, int32_t num_combine, hipStream_t stream);
 
 // Plain streaming read of words16 16-byte words (the achievable-bandwidth reference).
 hipError_t launch_stream_read(const void* src, int64_t words16, void* sink, int grid, hipStream_t stream);

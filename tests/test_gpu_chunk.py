@@ -102,18 +102,20 @@ def test_chunk_without_prefix_is_plain_causal_attention():
         compare(out[q0:q1], ref, f"causal segment {s}")
 
 
-def test_causal_boundary_probe():
+@pytest.mark.parametrize("q_len,i", [(12, 5), (40, 25)])   # a short segment and a wide one
+def test_causal_boundary_probe(q_len, i):
     """A key placed right after a query's position must not change that query's
-    output (bit-identical), and must change the next query's."""
-    spec = _chunk_spec("probe", 722, 4, 2, 16, [(20, 12)], 8)
+    output or any earlier one (bit-identical), and must change the next query's."""
+    spec = _chunk_spec("probe", 722, 4, 2, 16, [(20, q_len)], 8)
     w = make_step(spec)
     run = StepRun(w)
     run.write()
     q = run.chunk_q()
+    n = 20 + q_len
     plan = pg.ChunkPlan(64, 1, 0, 0)
-    base = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 12, 32, SCALE,
+    base = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, q_len, n, SCALE,
                                             plan=plan))
-    i = 5                                        # query i sits at position 20 + i
+    # query i sits at position 20 + i
     j = 20 + i + 1                               # the key right after it
     blk, off = int(w.block_tables[w.num_decode, j // 16]), j % 16
     kb, vb = run.pool.read_logical(blocks=[blk])
@@ -122,7 +124,7 @@ def test_causal_boundary_probe():
     kk[0, off] = bits_of(q[i + 1, 0::2] * 40)   # each kv head: aligned with query i+1, huge score
     vv[0, off] = O.f64_to_bf16_bits(np.full((2, 128), 50.0))
     run.pool.fill_logical(kk.view(np.int16), vv.view(np.int16), blocks=[blk])
-    got = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 12, 32, SCALE,
+    got = bits_of(pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, q_len, n, SCALE,
                                            plan=plan))
     assert np.array_equal(got[: i + 1], base[: i + 1])
     assert not np.array_equal(got[i + 1], base[i + 1])
