@@ -206,6 +206,33 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                                        "max_splits": cp.max_splits,
                                        "kernel": "columns" if cp.kernel == 2 else "chunk"}}
             rows["chunk_cfg5"] = res
+            # the whole mixed step's attention as ONE launch (plus one combine)
+            # from the host-built work list, against the decode call plus the
+            # chunk call it replaces
+            qlens = np.concatenate([np.ones(w.num_decode, dtype=np.int64), np.diff(w.chk_qsl)])
+            qsl_all = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+            ctx_all = np.concatenate([w.dec_ctx, w.chk_ctx]).astype(np.int32)
+            mplan, items = pg.plan_mixed(cus, s.block_size, s.num_kv_heads, s.num_q_heads, qsl_all, ctx_all)
+            o_all = torch.empty((w.num_tokens, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+            items_d = to_i32(items)
+            mq, mc = int(qlens.max()), int(ctx_all.max())
+            mcalls = [pg.bind_mixed(p, q_out, to_i32(qsl_all), to_i32(ctx_all), to_i32(w.block_tables), mq, mc, scale,
+                                    o_all, mplan, items_d) for p in pools]
+            med, _ = time_calls(mcalls, 30)
+            flops, kv = chunk_alg(w, qsl_all, ctx_all)
+            old_us = rows["decode"][name]["us"] + res["slice+verify"]["us"]
+            # the step's write and attention back to back, one event pair
+            step_calls = [lambda wr=wr, mc_=mc_: (wr(), mc_()) for wr, mc_ in zip(writes, mcalls)]
+            smed, _ = time_calls(step_calls, 30)
+            rows["mixed_cfg5"] = {
+                "attention_us": round(med, 2), "write_plus_attention_us": round(smed, 2),
+                "decode_call_plus_chunk_call_us": round(old_us, 2), "speedup_over_two_calls": round(old_us / med, 3),
+                "flops": flops, "kv_bytes": kv, "kv_gbs": round(kv / med / 1e3, 1),
+                "frac_hbm_peak": round(kv / med / 1e3 / HBM_PEAK_GBS, 4),
+                "tflops": round(flops / med / 1e6, 1),
+                "plan": {"split_wide": mplan.split_wide, "split_columns": mplan.split_columns,
+                         "max_splits": mplan.max_splits, "items": mplan.num_items, "combine_items": mplan.num_combine},
+                "launches": "one attention kernel + one combine kernel"}
         del pools
         torch.cuda.empty_cache()
     del flush
@@ -365,8 +392,9 @@ def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, ta
     """The decode-stall workload shape: `streams` decode streams (contexts
     U[2048, 8192] already cached) and one prompt of `prompt_len` tokens injected
     at step `inject_at`.  The step planner (host producers) feeds one fused
-    write and one attention call per step (the decode call when every segment
-    is a single token, else the chunk call); GPU time per step from events.
+    write and one attention call per step (the fused decode step when every
+    segment is a single token, else the one-launch mixed call from a work list
+    built on the host); GPU time per step from events.
     Chunked (token budget `budget`) vs whole-prompt prefill: worst and median
     step time seen by the decode streams, and the prompt's time to its first
     token.  Attention and cache write only: no projections or MLP."""
@@ -425,11 +453,12 @@ def measure_serving(dev, budget=512, prompt_len=6528, streams=8, inject_at=2, ta
             if (segs[:, 2] == 1).all():  # host routing: single decode tokens only -> one fused decode step
                 calls = [pg.bind_decode_step(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[4], args[5],
                                              int(ctx.max()), 1e-6, 1e6, scale, out, q_out=q_out)]
-            else:
+            else:  # the fused write, then the mixed step's one attention launch from the host-built work list
+                mplan, items = pg.plan_mixed(cus, bs, hkv, hq, qsl, ctx)
                 calls = [pg.bind_cache_write(pool, q_all[:T], k_all[:T], v_all[:T], wq, wk, args[0], args[1],
                                              args[2], 1e-6, 1e6, q_out),
-                         pg.bind_chunk(pool, q_out, args[3], args[4], args[5], int(segs[:, 2].max()),
-                                       int(ctx.max()), scale, out)]
+                         pg.bind_mixed(pool, q_out, args[3], args[4], args[5], int(segs[:, 2].max()),
+                                       int(ctx.max()), scale, out, mplan, to_i32(items))]
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()

@@ -196,9 +196,8 @@ __global__ __launch_bounds__(kWideThreads, 2) void chunk_wide_kernel(PoolGeom po
   __shared__ __align__(1024) uint8_t s_st1[kStageBytes];
   __shared__ __align__(1024) uint8_t s_st2[kStageBytes];
   __shared__ __align__(1024) uint8_t s_st3[kStageBytes];
-  __shared__ int32_t s_blk[kMaxBlockIds];
   wide_body<R>(pool, a, loc.si, loc.item.x, loc.item.y, loc.item.z, loc.item.w, a.split_wide,
-               WideLds{s_st0, s_st1, s_st2, s_st3, s_blk});
+               WideLds{s_st0, s_st1, s_st2, s_st3});
 }
 
 // ---------------------------------------------------------------- narrow kernel

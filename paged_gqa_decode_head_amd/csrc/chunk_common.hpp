@@ -37,12 +37,26 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// Maxima of scores straight out of the matrix cores.  These are never
+// signalling NaNs, so the max needs no canonicalisation of its inputs (which
+// the compiler adds to fmaxf in IEEE mode: one extra VALU instruction per score).
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // x of lane l combined with x of lane l ^ 32 (v_permlane32_swap: no LDS round
 // trip).  Each lane receives the pair {x_l, x_(l^32)}, so both halves compute
 // the same value.
 __device__ __forceinline__ float halves_max(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return max_raw(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -135,9 +149,10 @@ __device__ __forceinline__ void softmax_max(RowState& st, const f32x16_t& sacc, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) sv[i] = 16 * (i >> 3) + (i & 7) <= lim ? sacc[i] : -INFINITY;
   }
-  float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-  mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sv[8], sv[9]), fmaxf(sv[10], sv[11])),
-                       fmaxf(fmaxf(sv[12], sv[13]), fmaxf(sv[14], sv[15]))));
+  const float m0 = max3_raw(sv[0], sv[1], sv[2]), m1 = max3_raw(sv[3], sv[4], sv[5]);
+  const float m2 = max3_raw(sv[6], sv[7], sv[8]), m3 = max3_raw(sv[9], sv[10], sv[11]);
+  const float m4 = max3_raw(sv[12], sv[13], sv[14]);
+  float mx = max_raw(max3_raw(m0, m1, m2), max3_raw(m3, m4, sv[15]));
   mx = halves_max(mx);
   const bool raise = mx > st.m + tau_raw;
   if (__builtin_amdgcn_ballot_w64(raise)) {
@@ -340,6 +355,7 @@ __device__ __forceinline__ void combine_row(const ChunkArgs& a, int64_t base, in
 constexpr int kStageBytes = 16384;
 constexpr int kVBytes0 = 8192;
 constexpr int kWideRing = 4;  // stages: step i (V read), i+1 (K read), i+2 landing, i+3 issued
+constexpr int kWideWindow = 1024;  // keys whose block ids the 64 lanes hold at a time (16 keys each)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -368,7 +384,6 @@ struct WideLds {
   uint8_t* st1;
   uint8_t* st2;
   uint8_t* st3;
-  int32_t* blk;  // kMaxBlockIds entries
 };
 
 // One wide item: the 128 query rows of row group grp of segment s and kv head
@@ -382,7 +397,6 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
   uint8_t* const s_st1 = lds.st1;
   uint8_t* const s_st2 = lds.st2;
   uint8_t* const s_st3 = lds.st3;
-  int32_t* const s_blk = lds.blk;
   const int bs = pool.block_size, lbs = __ffs(bs) - 1;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
@@ -392,9 +406,24 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
   const int ns = cdiv(kend, split);
   const int k0 = sp * split;
   const int k1 = min(kend, k0 + split);
-  const int nsteps = cdiv(k1 - k0, kStep);
-  const int b0 = k0 >> lbs;
-  load_tiles(s_blk, a, pool, s, g, b0, ((k1 - 1) >> lbs) - b0 + 1, tid, kWideThreads);
+  // The split's keys stream through the pipeline below in windows of at most
+  // kWideWindow keys (one window for splits up to that size).  For the current
+  // window, lane h holds the (block, kv head) tile index of its 16-key half h,
+  // read into scalar registers by v_readlane.  A block id outside the pool
+  // reads tile (0, g) and raises the flag.
+  int wk0 = k0, wk1 = min(k1, k0 + kWideWindow), nsteps = cdiv(wk1 - wk0, kStep);
+  int32_t lblk = g;
+  auto load_window = [&]() {
+    const int key = wk0 + 16 * lane;
+    lblk = g;
+    if (key < wk1) {
+      const int32_t b = a.bt[int64_t(s) * a.bt_stride + (key >> lbs)];
+      const bool ok = unsigned(b) < unsigned(pool.num_blocks);
+      if (!ok && wave == 0) raise_error(pool.err, kErrBlockId);
+      lblk = (ok ? b : 0) * pool.num_kv_heads + g;
+    }
+  };
+  load_window();
 
   // This wave's row tile.
   const int tile = grp * kWideTiles + wave;
@@ -433,18 +462,18 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
   }
   const uint32_t voff = uint32_t((bs * kHeadDim + vd * kVSub + 8 * vhalf) * 2);  // V^T follows the K rows
   const uint8_t* kv_bytes = reinterpret_cast<const uint8_t*>(pool.kv);
-  // The two half tiles of a step (read from s_blk one iteration before their
-  // loads are issued, so the LDS latency is hidden), then the step's 4 loads.
+  // The two half tiles of a step (their tile indices read from the lanes that
+  // hold them, into scalar registers), then the step's 4 loads.
   struct HalfBases {
     const uint8_t* h[2];
   };
   auto half_bases = [&](int step) {
-    const int key0 = k0 + step * kStep;
+    const int key0 = wk0 + step * kStep;
     HalfBases hb;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int hk = min(key0 + 16 * h, k1 - 1) & ~15;
-      const int blk = __builtin_amdgcn_readfirstlane(s_blk[(hk >> lbs) - b0]);
+      const int hk = min(key0 + 16 * h, wk1 - 1) & ~15;
+      const int blk = __builtin_amdgcn_readlane(lblk, (hk - wk0) >> 4);  // the half's lane (wave-uniform)
       hb.h[h] = kv_bytes + ((int64_t(blk) << tshift) + (hk & (bs - 1)) * kHeadDim) * 2;
     }
     return hb;
@@ -459,7 +488,7 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
   // V of keys past the split end must be 0 (0 * NaN would poison O): each lane
   // clears its own chunks of the split's last step once they have landed.
   auto fix_tail = [&](uint8_t* st, int step) {
-    const int key0 = k0 + step * kStep;
+    const int key0 = wk0 + step * kStep;
     if (key0 + kStep <= k1) return;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -507,29 +536,43 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
   // step i+2 is readable.  Loads are clamped to the last step, never skipped,
   // so every lane has exactly 4 loads per step in flight and vmcnt(4) means
   // "all but the latest step".
-  dma_step(s_st0, half_bases(0));
-  dma_step(s_st1, half_bases(min(1, nsteps - 1)));
-  dma_step(s_st2, half_bases(min(2, nsteps - 1)));
-  HalfBases next_hb = half_bases(min(3, nsteps - 1));
-  __builtin_amdgcn_s_waitcnt(kWaitVm4);
-  fix_tail(s_st0, 0);
-  if (nsteps > 1) fix_tail(s_st1, 1);
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  stage_barrier();
-  f32x16_t s_cur = f32x16_t{};
-  if (tile_ok) {
-    uint4 kop[8];
-    read_k(s_st0, kop);
-    s_cur = qk(kop);
-  }
+  HalfBases next_hb;
+  f32x16_t s_cur;
+  auto prologue = [&]() {
+    dma_step(s_st0, half_bases(0));
+    dma_step(s_st1, half_bases(min(1, nsteps - 1)));
+    dma_step(s_st2, half_bases(min(2, nsteps - 1)));
+    next_hb = half_bases(min(3, nsteps - 1));
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    fix_tail(s_st0, 0);
+    if (nsteps > 1) fix_tail(s_st1, 1);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    stage_barrier();
+    s_cur = f32x16_t{};
+    if (tile_ok) {
+      uint4 kop[8];
+      read_k(s_st0, kop);
+      s_cur = qk(kop);
+    }
+  };
   // st: step i (V), nst: step i+1 (K), fst: step i+2 (landing), lst: step i+3 (issued now)
   auto iter = [&](int i, const uint8_t* st, const uint8_t* nst, uint8_t* fst, uint8_t* lst) {
     dma_step(lst, next_hb);
     if (tile_ok && i < nsteps) {
-      const int key0 = k0 + i * kStep;
+      const int key0 = wk0 + i * kStep;
       const bool full = key0 + kStep <= k1 && key0 + kStep - 1 <= qpos_first;
-      uint4 kop[8];
+      // All 16 operand reads of the iteration first (K of step i+1, V of step
+      // i), each into registers of its own: reading every V operand just
+      // before its MFMA into one reused register quad exposed the LDS latency
+      // eight times per step.
+      uint4 kop[8], vop[8];
       read_k(nst, kop);
+#pragma unroll
+      for (int s16 = 0; s16 < 2; ++s16) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          vop[4 * s16 + dt] = *reinterpret_cast<const uint4*>(st + v_off + 1024 * dt + 4096 * s16);
+      }
       float sv[16];
       softmax_max(rs, s_cur, full, key0, k1, qpos, half, c, tau_raw, sv);
       const f32x16_t s_next = qk(kop);
@@ -538,8 +581,7 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
 #pragma unroll
       for (int s16 = 0; s16 < 2; ++s16) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          rs.o[dt] = mfma32(*reinterpret_cast<const uint4*>(st + v_off + 1024 * dt + 4096 * s16), pb[s16], rs.o[dt]);
+        for (int dt = 0; dt < 4; ++dt) rs.o[dt] = mfma32(vop[4 * s16 + dt], pb[s16], rs.o[dt]);
       }
       // Issue order of this block: one MFMA, then three VALU instructions, 16
       // times.  The score MFMAs of step i+1 (a dependent chain) are ready first
@@ -558,13 +600,23 @@ __device__ __forceinline__ void wide_body(PoolGeom& pool, const ChunkArgs& a, co
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     stage_barrier();
   };
-  for (int base = 0; base < nsteps; base += kWideRing) {
-    iter(base, s_st0, s_st1, s_st2, s_st3);
-    iter(base + 1, s_st1, s_st2, s_st3, s_st0);
-    iter(base + 2, s_st2, s_st3, s_st0, s_st1);
-    iter(base + 3, s_st3, s_st0, s_st1, s_st2);
+  for (;;) {
+    prologue();
+    for (int base = 0; base < nsteps; base += kWideRing) {
+      iter(base, s_st0, s_st1, s_st2, s_st3);
+      iter(base + 1, s_st1, s_st2, s_st3, s_st0);
+      iter(base + 2, s_st2, s_st3, s_st0, s_st1);
+      iter(base + 3, s_st3, s_st0, s_st1, s_st2);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no direct load outlives the window (or the workgroup's LDS)
+    if (wk1 >= k1) break;
+    // next window: every wave is done with the stages before they are refilled
+    stage_barrier();
+    wk0 = wk1;
+    wk1 = min(k1, wk0 + kWideWindow);
+    nsteps = cdiv(wk1 - wk0, kStep);
+    load_window();
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no direct load outlives the workgroup's LDS
   if (!tile_ok) return;
   write_rows<R>(a, rs, half, row_ok, qrow, g, hh, sp, ns, c);
 }

@@ -297,7 +297,6 @@ __global__ __launch_bounds__(kWideThreads, 2) void mixed_kernel(PoolGeom pool, C
   __shared__ __align__(1024) uint8_t s_st1[kStageBytes];
   __shared__ __align__(1024) uint8_t s_st2[kStageBytes];
   __shared__ __align__(1024) uint8_t s_st3[kStageBytes];
-  __shared__ int32_t s_blk[kMaxBlockIds];
   SegInfo si{};
   si.err = kErrQuery;
   const bool wide = it.kind == kKindWide;
@@ -318,7 +317,7 @@ __global__ __launch_bounds__(kWideThreads, 2) void mixed_kernel(PoolGeom pool, C
     return;
   }
   if (wide) {
-    wide_body<R>(pool, a, si, it.s, it.g, it.grp, it.sp, split, WideLds{s_st0, s_st1, s_st2, s_st3, s_blk});
+    wide_body<R>(pool, a, si, it.s, it.g, it.grp, it.sp, split, WideLds{s_st0, s_st1, s_st2, s_st3});
   } else {
     // the 4 waves' [16][128] accumulators fill two stages; the maxima and sums a third
     ColumnLds cl;

@@ -201,6 +201,24 @@ def test_chunk_bad_metadata_flags_and_zero_rows():
     assert run.pool.check_errors() == 0
 
 
+@pytest.mark.parametrize("bs", [16, 256])
+def test_chunk_wide_split_over_several_windows(bs):
+    """Wide items whose split is longer than the 1024 keys the lanes hold block
+    ids for at a time: the split streams through several windows."""
+    spec = _chunk_spec(f"cwin{bs}", 728, 16, 8, bs, [(3000, 64), (1500, 40)], 3200 // bs * 2 + 8)
+    w = make_step(spec)
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    mc = int(w.chk_ctx.max())
+    _note(f"[chunk] windows bs={bs}")
+    for split in (4096, 2048, 1056):
+        out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, 64, mc, SCALE,
+                                       plan=pg.ChunkPlan(split, -(-mc // 256), 256, 1))
+        assert run.pool.check_errors() == 0
+        compare(out, run.oracle_chunk_on_gpu_inputs(q), f"split {split}")
+
+
 def test_chunk_last_offset_must_equal_total_q():
     """A lone segment whose offsets end before total_q: the host sized the call
     as one wide segment (40 tokens, 80 rows per kv head), the device offsets

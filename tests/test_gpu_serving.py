@@ -1,8 +1,10 @@
 """Serving steps driven by the host producers (include/pgqa_sched.h): the step
 planner feeds the fused norm + rotary + cache write and ONE attention call per
 step for the whole mixed batch (prefill chunks, decode rows and prompt-lookup
-verify rows together); a step of single decode tokens goes to the fused decode
-step (norm + rotary + cache write + decode in one launch).
+verify rows together): by default the one-launch mixed call, whose work list
+pgqa_plan_mixed builds from the planner's host-side lengths; also the chunk
+call.  A step of single decode tokens goes to the fused decode step (norm +
+rotary + cache write + decode in one launch).
 Every step's output is checked against the fp64 reference on the read-back
 cache and the GPU-produced q."""
 import numpy as np
@@ -24,8 +26,9 @@ def _bf16(rng, shape):
     return torch.from_numpy(rng.standard_normal(shape)).to(torch.bfloat16).cuda()
 
 
+@pytest.mark.parametrize("route", ["mixed", "chunk"])
 @pytest.mark.parametrize("chunked", [True, False])
-def test_planned_steps_match_reference(chunked):
+def test_planned_steps_match_reference(chunked, route):
     rng = np.random.default_rng(41 + int(chunked))
     nseq = 5
     pool = pg.Pool(NB, BS, HKV)
@@ -58,7 +61,7 @@ def test_planned_steps_match_reference(chunked):
             seen[kd] += 1
         mixed += len(kinds) > 1
         T = plan["token_pos"].size
-        print(f"[serving] chunked={chunked} step {step}: segments {segs.tolist()}", flush=True)
+        print(f"[serving] chunked={chunked} route={route} step {step}: segments {segs.tolist()}", flush=True)
         q, k, v = _bf16(rng, (T, HQ, 128)), _bf16(rng, (T, HKV, 128)), _bf16(rng, (T, HKV, 128))
         bt_full = dev_i32(planner.block_tables)
         bt_seg = np.ascontiguousarray(planner.block_tables[segs[:, 0]])
@@ -70,8 +73,14 @@ def test_planned_steps_match_reference(chunked):
         else:
             q_out = pg.rms_norm_rope_cache_write(pool, q, k, v, wq, wk, dev_i32(plan["token_pos"]),
                                                  dev_i32(plan["token_seq"]), bt_full, EPS, THETA)
-            out = pg.paged_chunk_attention(pool, q_out, dev_i32(qsl), dev_i32(ctx), dev_i32(bt_seg),
-                                           int(segs[:, 2].max()), int(ctx.max()), SCALE)
+            if route == "mixed":  # work list built on the host from the planner's lengths, uploaded
+                mplan, items = pg.plan_mixed(torch.cuda.get_device_properties(0).multi_processor_count, BS, HKV,
+                                             HQ, qsl, ctx)
+                out = pg.paged_mixed_attention(pool, q_out, dev_i32(qsl), dev_i32(ctx), dev_i32(bt_seg),
+                                               int(segs[:, 2].max()), int(ctx.max()), SCALE, mplan, dev_i32(items))
+            else:
+                out = pg.paged_chunk_attention(pool, q_out, dev_i32(qsl), dev_i32(ctx), dev_i32(bt_seg),
+                                               int(segs[:, 2].max()), int(ctx.max()), SCALE)
         kk, vv = pool.read_logical()
         ref = O.chunk_attention(O.bf16_bits_to_f64(bits_of(q_out)), qsl, kk.numpy().view(np.uint16),
                                 vv.numpy().view(np.uint16), bt_seg, ctx, SCALE)
