@@ -160,6 +160,8 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
         mx = int(w.dec_ctx.max())
         out = torch.empty((w.num_decode, s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
         plan = pg.plan_decode(cus, s.block_size, w.num_decode, s.num_kv_heads, s.num_q_heads, mx)
+        if not args.no_host_lengths:
+            plan.set_host_context_lens(w.dec_ctx)
         calls = [pg.bind_decode(p, qd, ctx, bt, mx, scale, out, plan=plan) for p in pools]
         med, mean = time_calls(calls, 40)
         nb = decode_alg_bytes(w)
@@ -778,6 +780,8 @@ def main():
                     help="profiling aid: run only one workload's rows and print them (cfg5 or chunk: the mixed "
                          "workload, chunk attention included)")
     ap.add_argument("--calibrate-copy", action="store_true", help="also run a 256 MiB plain copy (counter scaling)")
+    ap.add_argument("--no-host-lengths", action="store_true",
+                    help="do not pass the host-side context lengths to the decode plans (natural unit order)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
@@ -838,12 +842,20 @@ def main():
         plan.waves_per_split = args.waves
     ws = torch.zeros(pg.decode_workspace_bytes(pools[0], w.num_decode, s.num_q_heads, max_ctx, plan),
                      dtype=torch.uint8, device=dev)
+    # the serving loop's host-side lengths, for the length-balanced unit order
+    # (the same plan without them is timed beside it)
+    plan_nohint = pg.DecodePlan(plan.split_tokens, plan.max_splits, plan.waves_per_split, plan.load_hint,
+                                plan.kernel)
+    if not args.no_host_lengths:
+        plan.set_host_context_lens(w.dec_ctx)
     assert w.num_tokens == w.num_decode and np.array_equal(w.dec_tok, np.arange(w.num_decode))
     assert np.array_equal(w.tok_pos, w.dec_ctx - 1)
     fused = [pg.bind_decode_step(p, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, out, plan=plan,
                                  workspace=ws) for p in pools]
     two = [(pg.bind_cache_write(p, q, k, v, wq, wk, pos, seq, bt, s.eps, s.rope_theta, q_out),
             pg.bind_decode(p, q_out, ctx, bt, max_ctx, scale, out, plan=plan, workspace=ws)) for p in pools]
+    fused_nohint = [pg.bind_decode_step(p, q, k, v, wq, wk, ctx, bt, max_ctx, s.eps, s.rope_theta, scale, out,
+                                        plan=plan_nohint, workspace=ws) for p in pools]
 
     def timed(issue):
         """Warmup, then exactly args.steps steps between two synchronisations,
@@ -871,6 +883,7 @@ def main():
 
     ms_two, _ = timed(issue_two)
     ms_step, step_ms = timed(issue_fused)
+    ms_nohint, nohint_ms = timed(lambda i: fused_nohint[i % args.layers]())
     # the two-call step's split between its launches: events around each call, in a loop of its own
     ev_two = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i, e in enumerate(ev_two):
@@ -934,7 +947,8 @@ def main():
             "layers_cycled": args.layers,
             "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
                      "waves_per_split": plan.waves_per_split,
-                     "kernel": "mfma" if plan.kernel == 2 else "dot"},
+                     "kernel": "mfma" if plan.kernel == 2 else "dot",
+                     "host_context_lens": bool(plan.host_context_lens)},
         },
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s": round(w.num_decode / (ms_step * 1e-3), 1),
@@ -951,6 +965,11 @@ def main():
             "frac_of_stream_read": round(launch_gbs / ceiling["gbs"], 4) if ceiling else None,
         },
         "stream_read_ceiling": ceiling,
+        "without_host_lengths": {
+            "what": "the same fused step with plan.host_context_lens unset (natural unit order)",
+            "ms_per_step": round(ms_nohint, 5), "us_events": round(nohint_ms * 1e3, 3),
+            "frac_hbm_peak": round(step_bytes / (nohint_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
         "two_call_step": {
             "calls": "pgqa_rms_norm_rope_cache_write + pgqa_paged_decode_attention",
             "ms_per_step": round(ms_two, 5), "alg_bytes": two_bytes,
@@ -962,7 +981,7 @@ def main():
     if args.calibrate_copy:
         result["copy_calibration"] = copy_calibration(dev)
     if not args.main_only:
-        del pools, fused, two, fused_pool
+        del pools, fused, two, fused_pool, fused_nohint
         torch.cuda.empty_cache()
         result["rows"] = measure_rows(args, dev)
         result["rows"]["decode_graph"] = measure_graphs(dev)

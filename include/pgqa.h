@@ -162,6 +162,12 @@ typedef struct {
   int32_t kernel;           /* split kernel: 0 library default (matrix-core when 8 or more query heads share
                                a kv head, else dot-product), 1 dot-product (VALU) kernel, 2 matrix-core
                                (MFMA) kernel.  Both give the same results up to rounding. */
+  const int32_t* host_context_lens;
+                            /* optional HOST copy of context_lens ([batch]), NULL if not known.  [P1] Summary
+                               item 3: the host knows every sequence's length in a serving loop.  With it the
+                               call orders the (sequence, kv head) units (at most 1024) longest first, dealt
+                               so that workgroups sharing a CU pair long units with short ones.  Results are
+                               bit-identical with and without it; a stale hint only costs balance. */
 } pgqa_decode_plan;
 
 /* Host-only: the plan pgqa_paged_decode_attention uses when given plan = NULL,

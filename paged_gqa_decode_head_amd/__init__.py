@@ -44,11 +44,26 @@ class PoolConfig(ctypes.Structure):
 
 class DecodePlan(ctypes.Structure):
     _fields_ = [("split_tokens", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("waves_per_split", ctypes.c_int32), ("load_hint", ctypes.c_int32), ("kernel", ctypes.c_int32)]
+                ("waves_per_split", ctypes.c_int32), ("load_hint", ctypes.c_int32), ("kernel", ctypes.c_int32),
+                ("host_context_lens", ctypes.c_void_p)]
+
+    def set_host_context_lens(self, lens):
+        """Attach a host copy of the call's context lengths (kept alive with the
+        plan); None detaches it."""
+        import numpy as np
+
+        if lens is None:
+            self._host_lens = None
+            self.host_context_lens = None
+            return self
+        self._host_lens = np.ascontiguousarray(lens, dtype=np.int32)
+        self.host_context_lens = self._host_lens.ctypes.data
+        return self
 
     def __repr__(self):
         return (f"DecodePlan(split_tokens={self.split_tokens}, max_splits={self.max_splits}, "
-                f"waves_per_split={self.waves_per_split}, load_hint={self.load_hint}, kernel={self.kernel})")
+                f"waves_per_split={self.waves_per_split}, load_hint={self.load_hint}, kernel={self.kernel}, "
+                f"host_context_lens={'set' if self.host_context_lens else 'None'})")
 
 
 class ChunkPlan(ctypes.Structure):

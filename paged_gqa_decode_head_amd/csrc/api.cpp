@@ -401,6 +401,7 @@ pgqa_status pgqa_plan_decode(int32_t num_cus, int32_t block_size, int32_t batch,
   out->waves_per_split = waves;
   out->load_hint = 0;
   out->kernel = kernel;
+  out->host_context_lens = nullptr;
   return PGQA_OK;
 }
 
@@ -487,7 +488,28 @@ pgqa_status decode_common(pgqa_pool* pool, const void* q, int64_t q_row_stride, 
   a.part_o = ws ? reinterpret_cast<float*>(ws + wl.part_o_off) : nullptr;
   a.part_lse = ws ? reinterpret_cast<float*>(ws + wl.part_lse_off) : nullptr;
   a.out = static_cast<uint16_t*>(out);
-  hipError_t e = launch_decode(pool->geom, a, st, static_cast<hipStream_t>(stream));
+  // Host-side lengths: order the units so that the workgroups sharing a CU
+  // carry long and short units together.  Workgroups are dealt to the CUs in
+  // linear order, those num_cus apart landing on the same CU, so the units go
+  // longest first in a snake: rank k to position (k / C) C + j, j = k % C on
+  // even rounds and C - 1 - (k % C) on odd ones (C = CUs).
+  UnitOrder ord;
+  ord.count = 0;
+  const int64_t units = int64_t(batch) * pool->cfg.num_kv_heads;
+  if (p.host_context_lens != nullptr && units <= kMaxOrderedUnits) {
+    const int32_t* hl = p.host_context_lens;
+    const int32_t hkv = pool->cfg.num_kv_heads;
+    int32_t rank[kMaxOrderedUnits];
+    for (int32_t u = 0; u < int32_t(units); ++u) rank[u] = u;
+    std::stable_sort(rank, rank + units, [&](int32_t x, int32_t y) { return hl[x / hkv] > hl[y / hkv]; });
+    const int64_t C = std::max<int64_t>(1, pool->num_cus);
+    for (int64_t k = 0; k < units; ++k) {
+      const int64_t round = k / C, j = k % C, rem = std::min<int64_t>(C, units - round * C);
+      ord.unit[round * C + ((round & 1) ? rem - 1 - j : j)] = uint16_t(rank[k]);
+    }
+    ord.count = int32_t(units);
+  }
+  hipError_t e = launch_decode(pool->geom, a, st, ord.count > 0 ? &ord : nullptr, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PGQA_OK;
 }

@@ -136,15 +136,21 @@ __device__ __forceinline__ void store_new_token(const PoolGeom& pool, int g, int
 }
 
 template <int R, int W, bool kStream, bool kFused>
-__global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a, StepArgs st) {
+__global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArgs a, StepArgs st, UnitOrder ord) {
   // grid (kv head, sequence, split): the split index varies slowest, so every
   // split level is dealt over all 8 XCDs (workgroups go to XCDs round-robin by
   // linear id; with the split fastest, 2 or 4 splits would pin each split level,
   // and the always-present first splits, to a quarter or half of the XCDs)
-  const int g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
+  int g = blockIdx.x, b = blockIdx.y;
+  if (ord.count > 0) {  // the host's unit order (read from the kernel arguments)
+    const int u = ord.unit[blockIdx.y * hkv + blockIdx.x];
+    b = u / hkv;
+    g = u - b * hkv;
+  }
+  const int sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int grp = lane >> 3, sub = lane & 7, khalf = lane & 1;
-  const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
 
   __shared__ __align__(16) uint32_t s_p[W][R][8];
   __shared__ float s_m[W][R], s_l[W][R];
@@ -516,14 +522,21 @@ struct MStep {
 template <int R, int W, bool kStream, bool kFused, bool kChunk = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(PoolGeom pool,
                                                                                                   DecodeArgs a,
-                                                                                                  StepArgs st) {
+                                                                                                  StepArgs st,
+                                                                                                  UnitOrder ord) {
   static_assert(R <= 16, "query heads per kv head exceed the MFMA columns");
   static_assert(!(kFused && kChunk), "the fused step has one query token per sequence");
   constexpr int C = kChunk ? 16 : R;  // columns in use
-  const int g = blockIdx.x, b = blockIdx.y, sp = blockIdx.z;
+  const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
+  int g = blockIdx.x, b = blockIdx.y;
+  if (ord.count > 0) {  // the host's unit order (read from the kernel arguments)
+    const int u = ord.unit[blockIdx.y * hkv + blockIdx.x];
+    b = u / hkv;
+    g = u - b * hkv;
+  }
+  const int sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, c = lane >> 4;
-  const int hq = a.num_q_heads, hkv = pool.num_kv_heads, bs = pool.block_size;
 
   __shared__ float s_m[W][C], s_l[W][C];
   __shared__ __align__(16) float s_acc[W][C][kHeadDim];
@@ -986,45 +999,50 @@ hipError_t launch_combine_if_split(const PoolGeom& pool, const DecodeArgs& a, hi
 }
 
 template <int R, int W, bool kStream>
-hipError_t launch_dot(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+hipError_t launch_dot(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder& ord,
+                      hipStream_t stream) {
   const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
   if (st != nullptr) {
-    hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st, ord);
   } else {
-    hipLaunchKernelGGL((decode_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a, StepArgs{});
+    hipLaunchKernelGGL((decode_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a, StepArgs{},
+                       ord);
   }
   return launch_combine_if_split(pool, a, stream);
 }
 
 template <int R, int W, bool kStream>
-hipError_t launch_mfma(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+hipError_t launch_mfma(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder& ord,
+                       hipStream_t stream) {
   const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
   if (st != nullptr) {
-    hipLaunchKernelGGL((decode_mfma_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st);
+    hipLaunchKernelGGL((decode_mfma_kernel<R, W, kStream, true>), grid, dim3(64 * W), 0, stream, pool, a, *st, ord);
   } else {
     hipLaunchKernelGGL((decode_mfma_kernel<R, W, kStream, false>), grid, dim3(64 * W), 0, stream, pool, a,
-                       StepArgs{});
+                       StepArgs{}, ord);
   }
   return launch_combine_if_split(pool, a, stream);
 }
 
 template <int R, int W>
-hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+hipError_t launch_rw(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder& ord,
+                     hipStream_t stream) {
   if (a.mfma) {
-    if (a.stream_loads) return launch_mfma<R, W, true>(pool, a, st, stream);
-    return launch_mfma<R, W, false>(pool, a, st, stream);
+    if (a.stream_loads) return launch_mfma<R, W, true>(pool, a, st, ord, stream);
+    return launch_mfma<R, W, false>(pool, a, st, ord, stream);
   }
-  if (a.stream_loads) return launch_dot<R, W, true>(pool, a, st, stream);
-  return launch_dot<R, W, false>(pool, a, st, stream);
+  if (a.stream_loads) return launch_dot<R, W, true>(pool, a, st, ord, stream);
+  return launch_dot<R, W, false>(pool, a, st, ord, stream);
 }
 
 template <int R>
-hipError_t launch_r(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+hipError_t launch_r(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder& ord,
+                    hipStream_t stream) {
   switch (a.waves) {
-    case 1: return launch_rw<R, 1>(pool, a, st, stream);
-    case 2: return launch_rw<R, 2>(pool, a, st, stream);
-    case 4: return launch_rw<R, 4>(pool, a, st, stream);
-    case 8: return launch_rw<R, 8>(pool, a, st, stream);
+    case 1: return launch_rw<R, 1>(pool, a, st, ord, stream);
+    case 2: return launch_rw<R, 2>(pool, a, st, ord, stream);
+    case 4: return launch_rw<R, 4>(pool, a, st, ord, stream);
+    case 8: return launch_rw<R, 8>(pool, a, st, ord, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1050,8 +1068,10 @@ DecodeWorkspace decode_workspace_layout(int32_t batch, int32_t num_kv_heads, int
 template <int R>
 hipError_t launch_columns_r(const PoolGeom& pool, const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(pool.num_kv_heads, a.batch, a.max_splits);
+  UnitOrder none;
+  none.count = 0;
   hipLaunchKernelGGL((decode_mfma_kernel<R, 4, false, false, true>), grid, dim3(256), 0, stream, pool, a,
-                     StepArgs{});
+                     StepArgs{}, none);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_splits == 1) return e;
   hipLaunchKernelGGL(combine_columns_kernel, dim3(pool.num_kv_heads * columns_of(a, R), a.batch), dim3(kHeadDim), 0,
@@ -1098,14 +1118,19 @@ hipError_t noalloc_scratch(void** ptr) {
   return hipSuccess;
 }
 
-hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream) {
+hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder* ord,
+                         hipStream_t stream) {
   if (a.batch == 0) return hipSuccess;
   if (a.split_tokens > kMaxTilesPerWave * 16 * a.waves) return hipErrorInvalidValue;
+  UnitOrder none;
+  none.count = 0;
+  const UnitOrder& o = ord != nullptr ? *ord : none;
+  if (o.count != 0 && o.count != a.batch * pool.num_kv_heads) return hipErrorInvalidValue;
   switch (a.num_q_heads / pool.num_kv_heads) {
-    case 1: return launch_r<1>(pool, a, st, stream);
-    case 2: return launch_r<2>(pool, a, st, stream);
-    case 4: return launch_r<4>(pool, a, st, stream);
-    case 8: return launch_r<8>(pool, a, st, stream);
+    case 1: return launch_r<1>(pool, a, st, o, stream);
+    case 2: return launch_r<2>(pool, a, st, o, stream);
+    case 4: return launch_r<4>(pool, a, st, o, stream);
+    case 8: return launch_r<8>(pool, a, st, o, stream);
     default: return hipErrorInvalidValue;
   }
 }

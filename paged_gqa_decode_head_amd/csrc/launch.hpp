@@ -71,8 +71,19 @@ struct StepArgs {
   double rev_freq[64];   // theta^(-2i/128) / (2 pi): turns per position of rotary pair i
 };
 
-// st == nullptr: plain decode attention over q as given.
-hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, hipStream_t stream);
+// Optional order of the decode grid's (sequence, kv head) units, passed by
+// value as a kernel argument: position p = sequence * Hkv + kv head of the grid
+// computes unit unit[p] instead (count == 0: natural order).  Built on the host
+// from host-side context lengths so that long and short units share a CU.
+constexpr int kMaxOrderedUnits = 1024;
+struct UnitOrder {
+  int32_t count;
+  uint16_t unit[kMaxOrderedUnits];
+};
+
+// st == nullptr: plain decode attention over q as given; ord == nullptr: natural unit order.
+hipError_t launch_decode(const PoolGeom& pool, const DecodeArgs& a, const StepArgs* st, const UnitOrder* ord,
+                         hipStream_t stream);
 
 // Chunk segments of at most 16 query rows (q_len x group) per kv head on the
 // matrix-core decode kernel, one workgroup per (kv head, segment, split).
