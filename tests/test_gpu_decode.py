@@ -395,3 +395,23 @@ def test_decode_random_cases_both_kernels(seed):
         compare(out, ref, f"seed {seed} kernel {kernel}")
         outs.append(f64_of(out))
     assert np.abs(outs[0] - outs[1]).max() <= 2e-2
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_many_split_plans_are_deterministic(kernel):
+    """Many-split plans (split partials merged by the combine in split order):
+    40 calls in a row give the same bits every time and match the fp64
+    reference, also when plans of different shapes reuse one workspace."""
+    w = make_step(StepSpec("merge", 977, 16, 8, 3600, decode=(Group(1, 32000, 32000), Group(7, 100, 3000))))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    mx = int(w.dec_ctx.max())
+    ref = run.oracle_decode_on_gpu_inputs(q)
+    for split in (64, 256, 1024):
+        plan = pg.DecodePlan(split, -(-mx // split), 4, 0, kernel)
+        first = bits_of(run.decode(plan=plan, q=q))
+        compare(torch.from_numpy(first.view(np.int16)).view(torch.bfloat16), ref, f"split {split}")
+        for i in range(40):
+            assert np.array_equal(bits_of(run.decode(plan=plan, q=q)), first), (split, i)
+    assert run.pool.check_errors() == 0
