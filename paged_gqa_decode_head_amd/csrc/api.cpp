@@ -887,9 +887,9 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
       sc = std::min<int64_t>({sc, std::max<int64_t>(round_up(n_c, gran), gran), kMaxSplitTokens / gran * gran});
     }
   }
-  // Items.  Wide items first, the kv head fastest (workgroups are dealt to the
-  // 8 XCDs round-robin, so one kv head's items share an L2), then column items,
-  // most keys first; then the combine items.
+  // Items.  Wide items with the kv head fastest (workgroups are dealt to the
+  // 8 XCDs round-robin, so one kv head's items share an L2) and column items,
+  // most keys first, interleaved; then the combine items.
   struct Item {
     int32_t v[kMixedItemInts];
   };
@@ -918,7 +918,18 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
   }
   std::stable_sort(citems.begin(), citems.end(),
                    [](const std::pair<int64_t, Item>& x, const std::pair<int64_t, Item>& y) { return x.first > y.first; });
-  for (const auto& ci : citems) att.push_back(ci.second);
+  // Wide and column items alternate in blocks of 8 (one per XCD): every CU
+  // then runs an MFMA-bound wide item beside an HBM-bound column item, and
+  // wide item j still lands on XCD j % 8, so a kv head's slice items share an L2.
+  {
+    std::vector<Item> wide_items;
+    wide_items.swap(att);
+    size_t wi = 0, ci = 0;
+    while (wi < wide_items.size() || ci < citems.size()) {
+      for (int k = 0; k < 8 && wi < wide_items.size(); ++k) att.push_back(wide_items[wi++]);
+      for (int k = 0; k < 8 && ci < citems.size(); ++k) att.push_back(citems[ci++].second);
+    }
+  }
   auto add_combine = [&](const MixedSeg& m, int64_t rho0, int64_t rho1, int64_t ns) {
     max_splits = std::max(max_splits, ns);
     if (ns < 2) return;

@@ -70,12 +70,27 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
             assert (s, g, rho, ns) not in got
             got.add((s, g, rho, ns))
     assert got == need_combine
-    # order: wide items first with the kv head fastest, then column items by key count
+    # order: wide and column items alternate in blocks of 8; wide items keep
+    # the kv head fastest (and land on XCD position % 8), column items go most
+    # keys first
     kinds = att[:, 1]
-    nw = int((kinds == WIDE).sum())
-    assert np.all(kinds[:nw] == WIDE) and np.all(kinds[nw:] == COLUMN)
-    assert np.array_equal(att[:nw, 2], np.arange(nw) % hkv)
-    keys = [min(plan.split_columns, int(it[7]) - int(it[4]) * plan.split_columns) for it in att[nw:]]
+    wide_pos = np.nonzero(kinds == WIDE)[0]
+    col_pos = np.nonzero(kinds == COLUMN)[0]
+    nw, nc = len(wide_pos), len(col_pos)
+    expect = []
+    wi = ci = 0
+    while wi < nw or ci < nc:
+        take = min(8, nw - wi)
+        expect += [WIDE] * take
+        wi += take
+        take = min(8, nc - ci)
+        expect += [COLUMN] * take
+        ci += take
+    assert kinds.tolist() == expect
+    assert np.array_equal(att[wide_pos, 2], np.arange(nw) % hkv)
+    if 8 % hkv == 0:
+        assert np.array_equal(att[wide_pos, 2], wide_pos % hkv)
+    keys = [min(plan.split_columns, int(it[7]) - int(it[4]) * plan.split_columns) for it in att[col_pos]]
     assert keys == sorted(keys, reverse=True)
 
 
