@@ -372,8 +372,12 @@ pgqa_status pgqa_paged_chunk_attention(
  * kv head (q_len x group > 16) become wide items (128 rows over one key split of
  * split_wide keys, matrix cores), the others query-column items (the segment's
  * rows as MFMA columns over one split of split_columns keys).  0 for a split
- * lets the planner choose.  Returns PGQA_ERR_INVALID_ARG for inconsistent host
- * metadata or a buffer that is too small.
+ * lets the planner choose: it estimates the wide items' matrix-core time and
+ * the column items' K/V bytes and gives each kind a share of the CUs' two
+ * workgroup slots in proportion (rates measured on MI355X).  The attention
+ * items alternate between the two kinds in runs of num_cus.  Returns
+ * PGQA_ERR_INVALID_ARG for inconsistent host metadata or a buffer that is too
+ * small.
  *
  * The caller copies the items to device memory (with its other per-step
  * metadata) and passes them and the plan to pgqa_paged_mixed_attention, which

@@ -868,14 +868,33 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
       n_c = std::max<int64_t>(n_c, n);
     }
   }
-  // Wide splits: about two items per CU over the (row group, kv head) units,
-  // 256 .. 4096 keys.  Column splits: about two items per CU over all the
-  // columns' (key, kv head) pairs, at least 512 keys.
+  // Split lengths.  Wide items (matrix-core bound) and column items (HBM bound)
+  // share the CUs' two workgroup slots.  tw: the wide work's time with every
+  // slot busy, from its 32-key steps over 128-row units (kWideStepUs per step
+  // and slot, two wide items sharing a CU); tc: the columns' K/V bytes at
+  // kColumnBytesPerUs.  Wide items get the share phi = tw / (tw + tc) of the
+  // 2 num_cus slots, which sets their splits per unit (256 .. 4096 keys);
+  // column items number about 4 num_cus (1 - phi)^2 (many per slot when they
+  // are the critical path, about one per free slot when they only fill gaps
+  // beside the wide items), at least 512 keys per split.  Both rates were
+  // measured on MI355X; split_wide / split_columns override the choice.
+  constexpr double kWideStepUs = 1.45;
+  constexpr double kColumnBytesPerUs = 5.5e6;
+  int64_t steps_w = 0;
+  for (const MixedSeg& m : wide) {
+    const int64_t groups = ((int64_t(m.qlen) * r + 31) / 32 + 3) / 4;
+    for (int64_t grp = 0; grp < groups; ++grp)
+      steps_w += (mixed_wide_kend(m.qlen, m.n, r, grp) + kChunkStep - 1) / kChunkStep * hkv;
+  }
+  const double tw = double(steps_w) * kWideStepUs / (2.0 * num_cus);
+  const double tc = double(keys_c) * 512.0 / kColumnBytesPerUs;  // K and V: 128 bf16 each per key and kv head
+  const double phi = tw + tc > 0 ? tw / (tw + tc) : 0.0;
   int64_t sw = split_wide, sc = split_columns;
   if (sw == 0) {
     sw = 256;
     if (units_w > 0) {
-      const int64_t want = (2ll * num_cus + units_w - 1) / units_w;
+      const double target = 2.0 * num_cus * phi;
+      const int64_t want = std::max<int64_t>(1, std::llround(target / double(units_w)));
       sw = std::max<int64_t>(256, round_up((kend_w + want - 1) / want, kChunkStep));
       sw = std::min<int64_t>({sw, round_up(kend_w, kChunkStep), kMaxSplitTokens});
     }
@@ -883,13 +902,16 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
   if (sc == 0) {
     sc = round_up(512, gran);
     if (keys_c > 0) {
-      sc = std::max<int64_t>(round_up(512, gran), round_up((keys_c + 2ll * num_cus - 1) / (2ll * num_cus), gran));
+      const double target = std::max(1.0, 4.0 * num_cus * (1.0 - phi) * (1.0 - phi));
+      sc = std::max<int64_t>(round_up(512, gran), round_up(int64_t(std::ceil(double(keys_c) / target)), gran));
       sc = std::min<int64_t>({sc, std::max<int64_t>(round_up(n_c, gran), gran), kMaxSplitTokens / gran * gran});
     }
   }
-  // Items.  Wide items with the kv head fastest (workgroups are dealt to the
-  // 8 XCDs round-robin, so one kv head's items share an L2) and column items,
-  // most keys first, interleaved; then the combine items.
+  // Items.  Wide items with the kv head fastest, column items most keys
+  // first; the two kinds alternate in runs of num_cus, so that a CU's two
+  // slots start on one item of each kind.  Workgroups are dealt to the 8 XCDs
+  // round-robin, and a run of num_cus (a multiple of 8) keeps wide item j on
+  // XCD j % 8: one kv head's items share an L2.  Then the combine items.
   struct Item {
     int32_t v[kMixedItemInts];
   };
@@ -918,16 +940,14 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
   }
   std::stable_sort(citems.begin(), citems.end(),
                    [](const std::pair<int64_t, Item>& x, const std::pair<int64_t, Item>& y) { return x.first > y.first; });
-  // Wide and column items alternate in blocks of 8 (one per XCD): every CU
-  // then runs an MFMA-bound wide item beside an HBM-bound column item, and
-  // wide item j still lands on XCD j % 8, so a kv head's slice items share an L2.
   {
     std::vector<Item> wide_items;
     wide_items.swap(att);
+    const size_t run = size_t(num_cus);
     size_t wi = 0, ci = 0;
     while (wi < wide_items.size() || ci < citems.size()) {
-      for (int k = 0; k < 8 && wi < wide_items.size(); ++k) att.push_back(wide_items[wi++]);
-      for (int k = 0; k < 8 && ci < citems.size(); ++k) att.push_back(citems[ci++].second);
+      for (size_t k = 0; k < run && wi < wide_items.size(); ++k) att.push_back(wide_items[wi++]);
+      for (size_t k = 0; k < run && ci < citems.size(); ++k) att.push_back(citems[ci++].second);
     }
   }
   auto add_combine = [&](const MixedSeg& m, int64_t rho0, int64_t rho1, int64_t ns) {

@@ -70,9 +70,9 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
             assert (s, g, rho, ns) not in got
             got.add((s, g, rho, ns))
     assert got == need_combine
-    # order: wide and column items alternate in blocks of 8; wide items keep
-    # the kv head fastest (and land on XCD position % 8), column items go most
-    # keys first
+    # order: wide and column items alternate in runs of num_cus (256 here);
+    # wide items keep the kv head fastest (and land on XCD position % 8),
+    # column items go most keys first
     kinds = att[:, 1]
     wide_pos = np.nonzero(kinds == WIDE)[0]
     col_pos = np.nonzero(kinds == COLUMN)[0]
@@ -80,10 +80,10 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
     expect = []
     wi = ci = 0
     while wi < nw or ci < nc:
-        take = min(8, nw - wi)
+        take = min(256, nw - wi)
         expect += [WIDE] * take
         wi += take
-        take = min(8, nc - ci)
+        take = min(256, nc - ci)
         expect += [COLUMN] * take
         ci += take
     assert kinds.tolist() == expect
@@ -114,7 +114,9 @@ def test_mixed_plan_of_the_qwen3_mixed_step():
     ctx = np.concatenate([w.dec_ctx, w.chk_ctx]).astype(np.int32)
     plan, items = pg.plan_mixed(256, 16, 8, 16, qsl, ctx)
     _check_plan(plan, items, qsl, ctx, 8, 2, 16)
-    assert int((items[: plan.num_items, 1] == WIDE).sum()) == 8 * 8 * 8   # 8 row groups x 8 kv heads x 8 splits
+    # the wide work (8 row groups x 8 kv heads, up to 6656 keys) and the columns'
+    # K/V split the slots about evenly: one wide item per CU, 4 splits of 1664 keys
+    assert (plan.split_wide, int((items[: plan.num_items, 1] == WIDE).sum())) == (1664, 8 * 8 * 4)
 
 
 def test_mixed_plan_rejects_bad_host_metadata_and_small_buffers():
