@@ -165,9 +165,17 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
         calls = [pg.bind_decode(p, qd, ctx, bt, mx, scale, out, plan=plan) for p in pools]
         med, mean = time_calls(calls, 40)
         nb = decode_alg_bytes(w)
+        # the floor at this size: a plain streaming read of the same byte count,
+        # timed the same way (cold caches, events around the launch)
+        sbuf = torch.ones(nb // 16 * 4, dtype=torch.int32, device=dev)
+        ssink = torch.empty(3 * cus * 256, dtype=torch.int32, device=dev)
+        smed, _ = time_calls([pg.bind_stream_read(sbuf, ssink, 3 * cus)], 40)
+        del sbuf, ssink
         rows["decode"][name] = {"batch": w.num_decode, "keys": int(w.dec_ctx.sum()), "us": round(med, 2),
                                 "alg_bytes": nb, "gbs": round(nb / med / 1e3, 1),
                                 "frac_hbm_peak": round(nb / med / 1e3 / HBM_PEAK_GBS, 4),
+                                "stream_read_us": round(smed, 2),
+                                "frac_of_stream_read": round(smed / med, 4),
                                 "plan": {"split_tokens": plan.split_tokens, "max_splits": plan.max_splits,
                                          "waves": plan.waves_per_split,
                                          "kernel": "mfma" if plan.kernel == 2 else "dot"}}
@@ -208,6 +216,25 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                                        "max_splits": cp.max_splits,
                                        "kernel": "columns" if cp.kernel == 2 else "chunk"}}
             rows["chunk_cfg5"] = res
+            # the slice, and the slice with the verify rows, through the one-launch
+            # mixed call (host-built work list: the serving path's route for them)
+            mres = {}
+            for label in ("slice", "slice+verify"):
+                qq, qs, cx, bb = cases[label]
+                mq, mc = int(np.diff(qs).max()), int(cx.max())
+                o2 = torch.empty((qq.shape[0], s.num_q_heads, 128), dtype=torch.bfloat16, device=dev)
+                mp, mi = pg.plan_mixed(cus, s.block_size, s.num_kv_heads, s.num_q_heads, qs, cx)
+                mi_d = to_i32(mi)
+                calls = [pg.bind_mixed(p, qq, to_i32(qs), to_i32(cx), to_i32(bb), mq, mc, scale, o2, mp, mi_d)
+                         for p in pools]
+                med, _ = time_calls(calls, 30)
+                flops, kv = chunk_alg(w, qs, cx)
+                mres[label] = {"us": round(med, 2), "tflops": round(flops / med / 1e6, 1),
+                               "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "kv_gbs": round(kv / med / 1e3, 1),
+                               "plan": {"split_wide": mp.split_wide, "split_columns": mp.split_columns,
+                                        "max_splits": mp.max_splits, "items": mp.num_items}}
+            rows["mixed_call_cfg5_chunks"] = mres
             # the whole mixed step's attention as ONE launch (plus one combine)
             # from the host-built work list, against the decode call plus the
             # chunk call it replaces
