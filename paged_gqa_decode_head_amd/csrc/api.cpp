@@ -907,55 +907,95 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
       sc = std::min<int64_t>({sc, std::max<int64_t>(round_up(n_c, gran), gran), kMaxSplitTokens / gran * gran});
     }
   }
+  // Item counts and the partial slots per row (a size query stops here).
+  int64_t n_wide = 0, n_cols = 0, n_comb = 0, max_splits = 1, max_ns_w = 0;
+  for (const MixedSeg& m : wide) {
+    const int64_t rows = int64_t(m.qlen) * r, groups = ((rows + 31) / 32 + 3) / 4;
+    max_ns_w = std::max<int64_t>(max_ns_w, (int64_t(m.n) + sw - 1) / sw);
+    for (int64_t grp = 0; grp < groups; ++grp) {
+      const int64_t ns = (mixed_wide_kend(m.qlen, m.n, r, grp) + sw - 1) / sw;
+      n_wide += ns * hkv;
+      max_splits = std::max(max_splits, ns);
+      if (ns >= 2) n_comb += hkv * ((std::min<int64_t>(rows, (grp + 1) * 128) - grp * 128 + 7) / 8);
+    }
+  }
+  for (const MixedSeg& m : cols) {
+    const int64_t ns = (int64_t(m.n) + sc - 1) / sc;
+    n_cols += ns * hkv;
+    max_splits = std::max(max_splits, ns);
+    if (ns >= 2) n_comb += hkv * ((int64_t(m.qlen) * r + 7) / 8);
+  }
+  if (n_wide + n_cols + n_comb > int64_t(0x7fffffff) || max_splits > 65535)
+    return fail(PGQA_ERR_INVALID_ARG, "too many mixed work items");
+  out->split_wide = int32_t(sw);
+  out->split_columns = int32_t(sc);
+  out->max_splits = int32_t(max_splits);
+  out->num_items = int32_t(n_wide + n_cols);
+  out->num_combine = int32_t(n_comb);
+  if (items == nullptr) return PGQA_OK;
+  if (item_capacity < n_wide + n_cols + n_comb)
+    return fail(PGQA_ERR_INVALID_ARG, "item buffer holds %lld items, the plan has %lld", (long long)item_capacity,
+                (long long)(n_wide + n_cols + n_comb));
+
   // Items.  Wide items with the kv head fastest, column items most keys
   // first; the two kinds alternate in runs of num_cus, so that a CU's two
   // slots start on one item of each kind.  Workgroups are dealt to the 8 XCDs
   // round-robin, and a run of num_cus (a multiple of 8) keeps wide item j on
   // XCD j % 8: one kv head's items share an L2.  Then the combine items.
-  struct Item {
-    int32_t v[kMixedItemInts];
+  // Each item goes straight to its place in that order: wide item i after
+  // i / run earlier wide runs and the column runs between them, column item j
+  // after (j / run) + 1 wide runs and j / run column runs.
+  const int64_t run = num_cus;
+  auto put = [&](int64_t pos, int32_t s0, int32_t kind, int32_t g, int32_t grp, int32_t sp, const MixedSeg& m) {
+    int32_t* d = items + pos * kMixedItemInts;
+    d[0] = s0; d[1] = kind; d[2] = g; d[3] = grp; d[4] = sp; d[5] = m.q0; d[6] = m.qlen; d[7] = m.n;
   };
-  std::vector<Item> att, comb;
-  int64_t max_splits = 1;
-  int64_t max_ns_w = 0;
-  for (const MixedSeg& m : wide)
-    max_ns_w = std::max<int64_t>(max_ns_w, (int64_t(m.n) + sw - 1) / sw);
+  int64_t wk = 0, wj = 0;  // wide item wk * run + wj
   for (int64_t sp = 0; sp < max_ns_w; ++sp)
     for (const MixedSeg& m : wide) {
       const int64_t groups = ((int64_t(m.qlen) * r + 31) / 32 + 3) / 4;
       for (int64_t grp = 0; grp < groups; ++grp) {
         const int64_t ns = (mixed_wide_kend(m.qlen, m.n, r, grp) + sw - 1) / sw;
         if (sp >= ns) continue;
-        for (int64_t g = 0; g < hkv; ++g)
-          att.push_back(Item{{m.s, 0, int32_t(g), int32_t(grp), int32_t(sp), m.q0, m.qlen, m.n}});
+        for (int64_t g = 0; g < hkv; ++g) {
+          put(wk * run + std::min(wk * run, n_cols) + wj, m.s, 0, int32_t(g), int32_t(grp), int32_t(sp), m);
+          if (++wj == run) wj = 0, ++wk;
+        }
       }
     }
-  std::vector<std::pair<int64_t, Item>> citems;
-  for (const MixedSeg& m : cols) {
-    const int64_t ns = (int64_t(m.n) + sc - 1) / sc;
-    for (int64_t sp = 0; sp < ns; ++sp)
-      for (int64_t g = 0; g < hkv; ++g)
-        citems.push_back({std::min<int64_t>(sc, m.n - sp * sc),
-                          Item{{m.s, 1, int32_t(g), 0, int32_t(sp), m.q0, m.qlen, m.n}}});
-  }
-  std::stable_sort(citems.begin(), citems.end(),
-                   [](const std::pair<int64_t, Item>& x, const std::pair<int64_t, Item>& y) { return x.first > y.first; });
-  {
-    std::vector<Item> wide_items;
-    wide_items.swap(att);
-    const size_t run = size_t(num_cus);
-    size_t wi = 0, ci = 0;
-    while (wi < wide_items.size() || ci < citems.size()) {
-      for (size_t k = 0; k < run && wi < wide_items.size(); ++k) att.push_back(wide_items[wi++]);
-      for (size_t k = 0; k < run && ci < citems.size(); ++k) att.push_back(citems[ci++].second);
+  // Column items, most keys first: every split but a segment's last holds
+  // exactly sc keys, so the full splits go first in (segment, split, kv head)
+  // order, then the shorter last splits by length, longest first (segment
+  // order among equals).
+  struct Tail {
+    int32_t keys, sp;
+    const MixedSeg* m;
+  };
+  std::vector<Tail> tails;
+  tails.reserve(cols.size());
+  int64_t ck = 0, cj = 0;  // column item ck * run + cj
+  auto put_col = [&](const MixedSeg& m, int32_t sp) {
+    for (int64_t g = 0; g < hkv; ++g) {
+      put(std::min((ck + 1) * run, n_wide) + ck * run + cj, m.s, 1, int32_t(g), 0, sp, m);
+      if (++cj == run) cj = 0, ++ck;
     }
+  };
+  for (const MixedSeg& m : cols) {
+    const int32_t full = int32_t(int64_t(m.n) / sc), rest = int32_t(int64_t(m.n) - int64_t(full) * sc);
+    for (int32_t sp = 0; sp < full; ++sp) put_col(m, sp);
+    if (rest != 0) tails.push_back(Tail{rest, full, &m});
   }
+  std::stable_sort(tails.begin(), tails.end(), [](const Tail& x, const Tail& y) { return x.keys > y.keys; });
+  for (const Tail& t : tails) put_col(*t.m, t.sp);
+  int32_t* dst = items + (n_wide + n_cols) * kMixedItemInts;
   auto add_combine = [&](const MixedSeg& m, int64_t rho0, int64_t rho1, int64_t ns) {
-    max_splits = std::max(max_splits, ns);
     if (ns < 2) return;
     for (int64_t g = 0; g < hkv; ++g)
-      for (int64_t rho = rho0; rho < rho1; rho += 8)
-        comb.push_back(Item{{m.s, 2, int32_t(g), int32_t(rho), int32_t(ns), m.q0, m.qlen, m.n}});
+      for (int64_t rho = rho0; rho < rho1; rho += 8) {
+        dst[0] = m.s; dst[1] = 2; dst[2] = int32_t(g); dst[3] = int32_t(rho);
+        dst[4] = int32_t(ns); dst[5] = m.q0; dst[6] = m.qlen; dst[7] = m.n;
+        dst += kMixedItemInts;
+      }
   };
   for (const MixedSeg& m : wide) {
     const int64_t rows = int64_t(m.qlen) * r, groups = ((rows + 31) / 32 + 3) / 4;
@@ -964,20 +1004,6 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
                   (mixed_wide_kend(m.qlen, m.n, r, grp) + sw - 1) / sw);
   }
   for (const MixedSeg& m : cols) add_combine(m, 0, int64_t(m.qlen) * r, (int64_t(m.n) + sc - 1) / sc);
-  if (att.size() + comb.size() > size_t(0x7fffffff) || max_splits > 65535)
-    return fail(PGQA_ERR_INVALID_ARG, "too many mixed work items");
-  out->split_wide = int32_t(sw);
-  out->split_columns = int32_t(sc);
-  out->max_splits = int32_t(max_splits);
-  out->num_items = int32_t(att.size());
-  out->num_combine = int32_t(comb.size());
-  if (items == nullptr) return PGQA_OK;
-  if (item_capacity < int64_t(att.size() + comb.size()))
-    return fail(PGQA_ERR_INVALID_ARG, "item buffer holds %lld items, the plan has %lld", (long long)item_capacity,
-                (long long)(att.size() + comb.size()));
-  int32_t* dst = items;
-  for (const Item& it : att) dst = std::copy(it.v, it.v + kMixedItemInts, dst);
-  for (const Item& it : comb) dst = std::copy(it.v, it.v + kMixedItemInts, dst);
   return PGQA_OK;
 }
 
