@@ -20,7 +20,7 @@ def _segments(rng, n_seg, bs):
     return np.concatenate([[0], np.cumsum(qls)]).astype(np.int32), np.array(ctx, dtype=np.int32)
 
 
-def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
+def _check_plan(plan, items, qsl, ctx, hkv, r, bs, cus=256):
     att, comb = items[: plan.num_items], items[plan.num_items:]
     assert len(comb) == plan.num_combine
     assert plan.split_wide % 32 == 0 and 0 < plan.split_wide <= 4096
@@ -70,9 +70,9 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
             assert (s, g, rho, ns) not in got
             got.add((s, g, rho, ns))
     assert got == need_combine
-    # order: wide and column items alternate in runs of num_cus (256 here);
-    # wide items keep the kv head fastest (and land on XCD position % 8),
-    # column items go most keys first
+    # order: wide and column items alternate in runs of num_cus; wide items
+    # keep the kv head fastest (and land on XCD position % 8), column items go
+    # most keys first, in (segment, split, kv head) order among equals
     kinds = att[:, 1]
     wide_pos = np.nonzero(kinds == WIDE)[0]
     col_pos = np.nonzero(kinds == COLUMN)[0]
@@ -80,10 +80,10 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
     expect = []
     wi = ci = 0
     while wi < nw or ci < nc:
-        take = min(256, nw - wi)
+        take = min(cus, nw - wi)
         expect += [WIDE] * take
         wi += take
-        take = min(256, nc - ci)
+        take = min(cus, nc - ci)
         expect += [COLUMN] * take
         ci += take
     assert kinds.tolist() == expect
@@ -92,6 +92,8 @@ def _check_plan(plan, items, qsl, ctx, hkv, r, bs):
         assert np.array_equal(att[wide_pos, 2], wide_pos % hkv)
     keys = [min(plan.split_columns, int(it[7]) - int(it[4]) * plan.split_columns) for it in att[col_pos]]
     assert keys == sorted(keys, reverse=True)
+    order = [(-k, int(it[0]), int(it[4]), int(it[2])) for k, it in zip(keys, att[col_pos])]
+    assert order == sorted(order)
 
 
 @pytest.mark.parametrize("seed", range(24))
@@ -101,8 +103,9 @@ def test_mixed_plan_covers_every_row_and_key_once(seed):
     bs = [16, 32, 64, 128, 256][seed % 5]
     qsl, ctx = _segments(rng, int(rng.integers(1, 12)), bs)
     splits = [(0, 0), (32, max(64, bs)), (256, 0), (0, 4096 // max(64, bs) * max(64, bs))][seed % 4]
-    plan, items = pg.plan_mixed(256, bs, hkv, hq, qsl, ctx, *splits)
-    _check_plan(plan, items, qsl, ctx, hkv, hq // hkv, bs)
+    cus = [256, 8, 80, 304][(seed // 4) % 4]   # runs that end part-way through either list
+    plan, items = pg.plan_mixed(cus, bs, hkv, hq, qsl, ctx, *splits)
+    _check_plan(plan, items, qsl, ctx, hkv, hq // hkv, bs, cus)
 
 
 def test_mixed_plan_of_the_qwen3_mixed_step():
