@@ -19,11 +19,12 @@
 //             v_mfma_f32_16x16x32_bf16 products over one key split, 4 waves
 //             taking 32-key steps in turn, K/V loaded straight into operand
 //             registers; HBM-bound.
-// Wide items come first (the long ones), with the kv head fastest so that
-// workgroups dealt round-robin to the 8 XCDs keep one kv head's K/V of a slice
-// in one L2; then column items, longest first.  Split partials go to one
-// [split][token][head] layout, merged by one combine launch whose items
-// (8 rows each) follow the attention items in the same list.
+// Wide items are listed with the kv head fastest, so that workgroups dealt
+// round-robin to the 8 XCDs keep one kv head's K/V of a slice in one L2, and
+// column items longest first; the two kinds alternate in runs of num_cus, so
+// that the two workgroups sharing a CU start on one item of each kind.  Split
+// partials go to one [split][token][head] layout, merged by one combine launch
+// whose items (8 rows each) follow the attention items in the same list.
 //
 // Every item carries the host's copy of its segment's offset, length and key
 // count; the device compares them with query_start_loc and context_lens, and a
