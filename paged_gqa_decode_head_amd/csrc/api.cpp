@@ -876,8 +876,10 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
   // 2 num_cus slots, which sets their splits per unit (256 .. 4096 keys);
   // column items number about 4 num_cus (1 - phi)^2 (many per slot when they
   // are the critical path, about one per free slot when they only fill gaps
-  // beside the wide items), at least 512 keys per split.  Both rates were
-  // measured on MI355X; split_wide / split_columns override the choice.
+  // beside the wide items), at least 1024 keys per split (shorter splits only
+  // add start-up latency and combine work when the column work is small).
+  // Both rates were measured on MI355X; split_wide / split_columns override
+  // the choice.
   constexpr double kWideStepUs = 1.45;
   constexpr double kColumnBytesPerUs = 5.5e6;
   int64_t steps_w = 0;
@@ -900,10 +902,10 @@ pgqa_status pgqa_plan_mixed(int32_t num_cus, int32_t block_size, int32_t num_kv_
     }
   }
   if (sc == 0) {
-    sc = round_up(512, gran);
+    sc = round_up(1024, gran);
     if (keys_c > 0) {
       const double target = std::max(1.0, 4.0 * num_cus * (1.0 - phi) * (1.0 - phi));
-      sc = std::max<int64_t>(round_up(512, gran), round_up(int64_t(std::ceil(double(keys_c) / target)), gran));
+      sc = std::max<int64_t>(round_up(1024, gran), round_up(int64_t(std::ceil(double(keys_c) / target)), gran));
       sc = std::min<int64_t>({sc, std::max<int64_t>(round_up(n_c, gran), gran), kMaxSplitTokens / gran * gran});
     }
   }
