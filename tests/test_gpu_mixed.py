@@ -87,7 +87,7 @@ def _spec(name, seed, hq, hkv, bs, segs, decode=()):
                     chunks=tuple(Group(1, L, L, q) for L, q in segs), block_size=bs)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_mixed_random_steps(seed):
     """Seeded random steps: decode rows, wide segments (prefill slices), short
     ones (verify rows, single tokens) and empty ones in one call, random
