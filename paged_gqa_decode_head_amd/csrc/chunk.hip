@@ -103,7 +103,10 @@ __device__ __forceinline__ int4 list_item(const ChunkArgs& a, const SegInfo& si,
     const int ns = cdiv(wide_kend(si, grp, r), a.split_wide);
     const int per_head = K == kWideList ? ns : ns > 1 ? min(kWideTiles, si.tiles - grp * kWideTiles) * parts : 0;
     if (li < per_head * hkv) {
-      const int g = li % hkv, j = li / hkv;
+      // wide items: the kv head fastest (one head's items on one XCD); combine
+      // items: the rows fastest within a head (consecutive workgroups read
+      // neighbouring partial rows; 2% faster on a 512-token slice)
+      const int g = K == kWideList ? li % hkv : li / per_head, j = K == kWideList ? li / hkv : li % per_head;
       return K == kWideList ? make_int4(s, g, grp, j) : make_int4(s, g, grp * kWideTiles + j / parts, j % parts);
     }
     li -= per_head * hkv;
