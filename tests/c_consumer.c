@@ -1,6 +1,6 @@
 /*
  * A plain C11 caller of libpgqa's host-only entry points (no GPU needed):
- * version, pool sizing, the decode and chunk split planners, error
+ * version, pool sizing, the decode, chunk and mixed-step planners, error
  * reporting, prompt lookup, greedy acceptance and one step of the token-budget
  * planner.  tests/test_c_consumer.py builds it with gcc against include/ and
  * checks what it prints against the Python binding and the oracle.
@@ -29,6 +29,20 @@ int main(void) {
   printf("chunk_plan %d %d %d %d\n", cp.split_tokens, cp.max_splits, cp.short_split_tokens, cp.kernel);
   if (pgqa_plan_chunk(256, 16, 8, 40, 8, 16, 5, 4096, &cp) != PGQA_OK) return 1;
   printf("chunk_plan %d %d %d %d\n", cp.split_tokens, cp.max_splits, cp.short_split_tokens, cp.kernel);
+
+  /* a mixed step: two decode rows, a verify row of 5 tokens, a 40-token slice */
+  static int32_t mitems[4096 * PGQA_MIXED_ITEM_INTS];
+  const int32_t mqsl[] = {0, 1, 2, 7, 47};
+  const int32_t mctx[] = {300, 1200, 900, 2040};
+  pgqa_mixed_plan mp;
+  if (pgqa_plan_mixed(256, 16, 8, 16, 4, mqsl, mctx, 0, 0, NULL, 0, &mp) != PGQA_OK) return 3;
+  if (mp.num_items + mp.num_combine > 4096) return 3;
+  if (pgqa_plan_mixed(256, 16, 8, 16, 4, mqsl, mctx, 0, 0, mitems, 4096, &mp) != PGQA_OK) return 3;
+  long long checksum = 0;
+  for (long long i = 0; i < (long long)(mp.num_items + mp.num_combine) * PGQA_MIXED_ITEM_INTS; ++i)
+    checksum += (i + 1) * mitems[i];
+  printf("mixed_plan %d %d %d %d %d %lld\n", mp.split_wide, mp.split_columns, mp.max_splits, mp.num_items,
+         mp.num_combine, checksum);
 
   if (pgqa_plan_decode(0, 16, 1, 8, 16, 10, &dp) != PGQA_ERR_INVALID_ARG) return 2;
   printf("error %s | %s\n", pgqa_status_string(PGQA_ERR_INVALID_ARG), pgqa_last_error());

@@ -49,6 +49,19 @@ def test_version_pool_bytes_and_plans(output):
     assert want[0].endswith(" 1") and want[1].endswith(" 2")
 
 
+def test_mixed_plan_matches_the_binding(output):
+    import numpy as np
+
+    qsl = np.array([0, 1, 2, 7, 47], dtype=np.int32)
+    ctx = np.array([300, 1200, 900, 2040], dtype=np.int32)
+    p, items = pg.plan_mixed(256, 16, 8, 16, qsl, ctx)
+    flat = items.reshape(-1).astype(np.int64)
+    checksum = int(((np.arange(flat.size, dtype=np.int64) + 1) * flat).sum())
+    assert _line(output, "mixed_plan") == [
+        f"mixed_plan {p.split_wide} {p.split_columns} {p.max_splits} {p.num_items} {p.num_combine} {checksum}"]
+    assert p.num_items > 0 and p.num_combine > 0
+
+
 def test_error_reporting(output):
     (line,) = _line(output, "error")
     assert line.startswith("error ") and "|" in line and len(line.split("|")[1].strip()) > 0
