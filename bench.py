@@ -99,9 +99,10 @@ class CacheFlush:
         torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def time_calls_cold(calls, iters, flush, warmup=3):
+def time_calls_cold(calls, iters, flush, warmup=10, stats=None):
     """Median and mean microseconds of each call, each launch preceded by the
-    cache flush (HIP events around the launch only, on the current stream)."""
+    cache flush (HIP events around the launch only, on the current stream);
+    stats, if given, receives the p10 and p90."""
     import torch
 
     for i in range(warmup):
@@ -116,6 +117,9 @@ def time_calls_cold(calls, iters, flush, warmup=3):
         ev[i][1].record()
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    if stats is not None:
+        stats["p10_us"] = round(ts[len(ts) // 10], 2)
+        stats["p90_us"] = round(ts[(9 * len(ts)) // 10], 2)
     return ts[len(ts) // 2], sum(ts) / len(ts)
 
 
@@ -133,10 +137,10 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
     to_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
     scale = 1.0 / math.sqrt(128)
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    rows = {"decode": {}, "decode_step": {}, "cache_write": {}, "timing": "median of per-launch HIP events, each "
+    rows = {"decode": {}, "decode_step": {}, "cache_write": {}, "timing": "median (and p10, p90) of 50 per-launch HIP events after 10 warm-ups, each "
             "launch after a 1 GiB read that evicts the 256 MB Infinity Cache and L2 (cold caches)"}
     flush = CacheFlush(dev)
-    time_calls = lambda calls, iters: time_calls_cold(calls, iters, flush)  # noqa: E731
+    time_calls = lambda calls, iters, stats=None: time_calls_cold(calls, iters, flush, stats=stats)  # noqa: E731
     for name in names:
         w = make_step(SPECS[name])
         s = w.spec
@@ -163,15 +167,17 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
         if not args.no_host_lengths:
             plan.set_host_context_lens(w.dec_ctx)
         calls = [pg.bind_decode(p, qd, ctx, bt, mx, scale, out, plan=plan) for p in pools]
-        med, mean = time_calls(calls, 40)
+        dstats = {}
+        med, mean = time_calls(calls, 50, dstats)
         nb = decode_alg_bytes(w)
         # the floor at this size: a plain streaming read of the same byte count,
         # timed the same way (cold caches, events around the launch)
         sbuf = torch.ones(nb // 16 * 4, dtype=torch.int32, device=dev)
         ssink = torch.empty(3 * cus * 256, dtype=torch.int32, device=dev)
-        smed, _ = time_calls([pg.bind_stream_read(sbuf, ssink, 3 * cus)], 40)
+        smed, _ = time_calls([pg.bind_stream_read(sbuf, ssink, 3 * cus)], 50)
         del sbuf, ssink
-        rows["decode"][name] = {"batch": w.num_decode, "keys": int(w.dec_ctx.sum()), "us": round(med, 2),
+        rows["decode"][name] = {"batch": w.num_decode, "keys": int(w.dec_ctx.sum()), "us": round(med, 2), **dstats,
+                                "seqs_per_s": round(w.num_decode / med * 1e6, 1),
                                 "alg_bytes": nb, "gbs": round(nb / med / 1e3, 1),
                                 "frac_hbm_peak": round(nb / med / 1e3 / HBM_PEAK_GBS, 4),
                                 "stream_read_us": round(smed, 2),
@@ -185,9 +191,11 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
         qr, kr, vr = q[dsel].contiguous(), k[dsel].contiguous(), v[dsel].contiguous()
         fcalls = [pg.bind_decode_step(p, qr, kr, vr, to_bf16(w.wq), to_bf16(w.wk), ctx, bt, mx, s.eps, s.rope_theta,
                                       scale, out, plan=plan) for p in pools]
-        fmed, _ = time_calls(fcalls, 40)
+        fstats = {}
+        fmed, _ = time_calls(fcalls, 50, fstats)
         nbf = step_alg_bytes(w)
-        rows["decode_step"][name] = {"batch": w.num_decode, "us": round(fmed, 2), "alg_bytes": nbf,
+        rows["decode_step"][name] = {"batch": w.num_decode, "us": round(fmed, 2), **fstats,
+                                     "seqs_per_s": round(w.num_decode / fmed * 1e6, 1), "alg_bytes": nbf,
                                      "gbs": round(nbf / fmed / 1e3, 1),
                                      "frac_hbm_peak": round(nbf / fmed / 1e3 / HBM_PEAK_GBS, 4),
                                      "kernel": "mfma" if plan.kernel == 2 else "dot"}
@@ -207,9 +215,11 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                     cp = pg.ChunkPlan(256, -(-mc // 256), 256, 1)
                 calls = [pg.bind_chunk(p, qq, to_i32(qs), to_i32(cx), to_i32(bb), mq, mc, scale, o2, plan=cp)
                          for p in pools]
-                med, _ = time_calls(calls, 30)
+                cstats = {}
+                med, _ = time_calls(calls, 50, cstats)
                 flops, kv = chunk_alg(w, qs, cx)
-                res[label] = {"us": round(med, 2), "tflops": round(flops / med / 1e6, 1),
+                res[label] = {"us": round(med, 2), **cstats, "tokens_per_s": round(qq.shape[0] / med * 1e6, 1),
+                              "tflops": round(flops / med / 1e6, 1),
                               "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                               "kv_gbs": round(kv / med / 1e3, 1), "flops": flops, "kv_bytes": kv,
                               "plan": {"split_tokens": cp.split_tokens, "short_split_tokens": cp.short_split_tokens,
@@ -227,9 +237,11 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
                 mi_d = to_i32(mi)
                 calls = [pg.bind_mixed(p, qq, to_i32(qs), to_i32(cx), to_i32(bb), mq, mc, scale, o2, mp, mi_d)
                          for p in pools]
-                med, _ = time_calls(calls, 30)
+                mstats = {}
+                med, _ = time_calls(calls, 50, mstats)
                 flops, kv = chunk_alg(w, qs, cx)
-                mres[label] = {"us": round(med, 2), "tflops": round(flops / med / 1e6, 1),
+                mres[label] = {"us": round(med, 2), **mstats, "tokens_per_s": round(qq.shape[0] / med * 1e6, 1),
+                               "tflops": round(flops / med / 1e6, 1),
                                "frac_mfma_bf16_peak": round(flops / med / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                                "kv_gbs": round(kv / med / 1e3, 1),
                                "plan": {"split_wide": mp.split_wide, "split_columns": mp.split_columns,
@@ -247,14 +259,17 @@ def measure_rows(args, dev, names=("cfg2", "cfg3a", "cfg4", "cfg5")):
             mq, mc = int(qlens.max()), int(ctx_all.max())
             mcalls = [pg.bind_mixed(p, q_out, to_i32(qsl_all), to_i32(ctx_all), to_i32(w.block_tables), mq, mc, scale,
                                     o_all, mplan, items_d) for p in pools]
-            med, _ = time_calls(mcalls, 30)
+            xstats = {}
+            med, _ = time_calls(mcalls, 50, xstats)
             flops, kv = chunk_alg(w, qsl_all, ctx_all)
             old_us = rows["decode"][name]["us"] + res["slice+verify"]["us"]
             # the step's write and attention back to back, one event pair
             step_calls = [lambda wr=wr, mc_=mc_: (wr(), mc_()) for wr, mc_ in zip(writes, mcalls)]
             smed, _ = time_calls(step_calls, 30)
             rows["mixed_cfg5"] = {
-                "attention_us": round(med, 2), "write_plus_attention_us": round(smed, 2),
+                "attention_us": round(med, 2), "attention_p10_us": xstats["p10_us"],
+                "attention_p90_us": xstats["p90_us"], "tokens_per_s": round(w.num_tokens / med * 1e6, 1),
+                "write_plus_attention_us": round(smed, 2),
                 "decode_call_plus_chunk_call_us": round(old_us, 2), "speedup_over_two_calls": round(old_us / med, 3),
                 "flops": flops, "kv_bytes": kv, "kv_gbs": round(kv / med / 1e3, 1),
                 "frac_hbm_peak": round(kv / med / 1e3 / HBM_PEAK_GBS, 4),
