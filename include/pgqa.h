@@ -389,9 +389,11 @@ pgqa_status pgqa_paged_chunk_attention(
  * Every item carries the host's offset, length and key count of its segment;
  * the kernels compare them with the device metadata.  A mismatch, or metadata
  * that fails the chunk call's checks, sets PGQA_DEVERR_QUERY (or
- * PGQA_DEVERR_CONTEXT) and zeroes that item's output rows.  Items must come from
- * pgqa_plan_mixed for the same metadata: rows that no item covers are not
- * written.
+ * PGQA_DEVERR_CONTEXT) and zeroes the output rows the item's own offsets
+ * address (inside total_q; with wrong offsets these may be rows of another
+ * segment): once the flag is set, treat the call's whole output as invalid.
+ * Items must come from pgqa_plan_mixed for the same metadata: rows that no item
+ * covers are not written.
  */
 #define PGQA_MIXED_ITEM_INTS 8
 
