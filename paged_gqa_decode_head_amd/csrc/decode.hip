@@ -157,6 +157,10 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   __shared__ __align__(16) float s_acc[W][R][kHeadDim];
   __shared__ __align__(16) uint16_t s_newk[kFused ? kHeadDim : 1];  // fused step: the new token's k and v
   __shared__ __align__(16) uint16_t s_newv[kFused ? kHeadDim : 1];
+  // fused step: each wave's normed, rotated q rows and the cos / sin of the 64
+  // rotary pairs at the new token's position
+  __shared__ __align__(16) uint16_t s_q[kFused ? W : 1][R][kHeadDim];
+  __shared__ __align__(16) float s_cs[kFused ? W : 1][64], s_sn[kFused ? W : 1][64];
 
   // Issue the context length, this wave's block ids and q together: lane i
   // fetches the block id of the wave's i-th tile (tile wave + i*W of the
@@ -171,31 +175,44 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     if (tile * 16 < a.split_tokens && entry < a.bt_stride) lane_blk = a.bt[int64_t(b) * a.bt_stride + entry];
   }
   // q of the group, as bf16 pairs, for the lane's dims 8s.. and 64+8s..
+  // (fused step: filled after the norm and rotary, below)
   uint32_t qv[R][8];
+  if constexpr (!kFused) {
 #pragma unroll
-  for (int h = 0; h < R; ++h) {
-    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + h) * kHeadDim + sub * 8;
-    const uint4 x = *reinterpret_cast<const uint4*>(qrow);
-    const uint4 y = *reinterpret_cast<const uint4*>(qrow + 64);
-    qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
-    qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
+    for (int h = 0; h < R; ++h) {
+      const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + h) * kHeadDim + sub * 8;
+      const uint4 x = *reinterpret_cast<const uint4*>(qrow);
+      const uint4 y = *reinterpret_cast<const uint4*>(qrow + 64);
+      qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
+      qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
+    }
   }
 
-  // Fused step: lanes 0..7 of every wave fetch the new token's raw k, v and the
-  // k norm weight now, before the context length is known (one of these waves
-  // will write the token; see below).
-  uint4 nk0, nk1, nv0, nv1, nw0, nw1;
+  // Fused step: lane i fetches the rotary frequency of pair i; lanes 8h + s
+  // the raw q row of head g R + h % R and the q norm weight, dims 8s.. and
+  // 64+8s.. (groups h < R use them); every lane the new token's raw k, v and
+  // the k norm weight of its dims (lanes 0..7 of the wave that writes the token
+  // use them; see below).  All are issued now, before the context length is
+  // known, and without branches, so that the first tile's loads wait for the
+  // block ids alone (the wait counts only loads issued on every path).
+  uint4 qx, qy, nk0, nk1, nv0, nv1, nw0, nw1, qw0, qw1;
+  double rf = 0.0;
   if constexpr (kFused) {
-    if (lane < 8) {
-      const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
-      const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
-      nk0 = *reinterpret_cast<const uint4*>(kr);
-      nk1 = *reinterpret_cast<const uint4*>(kr + 64);
-      nv0 = *reinterpret_cast<const uint4*>(vr);
-      nv1 = *reinterpret_cast<const uint4*>(vr + 64);
-      nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
-      nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
-    }
+    static_assert(!kFused || (R <= 8 && (R & (R - 1)) == 0), "fused step: one q row per 8-lane group");
+    rf = st.rev_freq[lane];
+    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + (grp & (R - 1))) * kHeadDim + sub * 8;
+    qx = *reinterpret_cast<const uint4*>(qrow);
+    qy = *reinterpret_cast<const uint4*>(qrow + 64);
+    qw0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
+    qw1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
+    const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
+    const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
+    nk0 = *reinterpret_cast<const uint4*>(kr);
+    nk1 = *reinterpret_cast<const uint4*>(kr + 64);
+    nv0 = *reinterpret_cast<const uint4*>(vr);
+    nv1 = *reinterpret_cast<const uint4*>(vr + 64);
+    nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
+    nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
   }
 
   const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;
@@ -217,31 +234,45 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   // that computes the last tile norms and rotates the token's k and keeps it
   // and v in LDS for its own use when it reaches that tile; it stores them into
   // the cache slot only after its tile loop, so the stores hold up no tile
-  // load (the slot is read again only after this kernel).
+  // load (the slot is read again only after this kernel).  Each wave computes
+  // every rotary angle once (lane i: pair i) and every q row once (the 8 lanes
+  // of group h: row h), and shares them through its own LDS rows.
   const int patch_tile = kFused && sp == ns - 1 ? (n - 1 - k0) >> 4 : -1;
   const bool writer = kFused && patch_tile >= 0 && wave == patch_tile % W;
+  auto wave_lds_order = [&]() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
   auto fused_prologue = [&]() {
     if constexpr (kFused) {
-      float cs[8], sn[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) rope_angle(n - 1, st.rev_freq[8 * sub + j], cs[j], sn[j]);
-      const uint4 w0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
-      const uint4 w1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
-#pragma unroll
-      for (int h = 0; h < R; ++h) {
-        uint4 o0, o1;
-        norm_rope_lane(make_uint4(qv[h][0], qv[h][1], qv[h][2], qv[h][3]),
-                       make_uint4(qv[h][4], qv[h][5], qv[h][6], qv[h][7]), w0, w1, cs, sn, st.eps, o0, o1);
-        qv[h][0] = o0.x; qv[h][1] = o0.y; qv[h][2] = o0.z; qv[h][3] = o0.w;
-        qv[h][4] = o1.x; qv[h][5] = o1.y; qv[h][6] = o1.z; qv[h][7] = o1.w;
-        if (st.q_out != nullptr && sp == 0 && tid < 8) {
-          uint16_t* dst = st.q_out + (int64_t(b) * hq + g * R + h) * kHeadDim + sub * 8;
-          *reinterpret_cast<uint4*>(dst) = o0;
-          *reinterpret_cast<uint4*>(dst + 64) = o1;
-        }
+      {
+        float c1, s1;
+        rope_angle(n - 1, rf, c1, s1);
+        s_cs[wave][lane] = c1;
+        s_sn[wave][lane] = s1;
       }
-      if (writer) {
-        if (lane < 8) {
+      wave_lds_order();
+      if (grp < R || (writer && lane < 8)) {
+        float cs[8], sn[8];
+        const float4 c0 = *reinterpret_cast<const float4*>(&s_cs[wave][8 * sub]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&s_cs[wave][8 * sub + 4]);
+        const float4 s0 = *reinterpret_cast<const float4*>(&s_sn[wave][8 * sub]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&s_sn[wave][8 * sub + 4]);
+        cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w; cs[4] = c4.x; cs[5] = c4.y; cs[6] = c4.z; cs[7] = c4.w;
+        sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w; sn[4] = s4.x; sn[5] = s4.y; sn[6] = s4.z; sn[7] = s4.w;
+        if (grp < R) {
+          uint4 o0, o1;
+          norm_rope_lane(qx, qy, qw0, qw1, cs, sn, st.eps, o0, o1);
+          *reinterpret_cast<uint4*>(&s_q[wave][grp][8 * sub]) = o0;
+          *reinterpret_cast<uint4*>(&s_q[wave][grp][64 + 8 * sub]) = o1;
+          if (st.q_out != nullptr && sp == 0 && wave == 0) {
+            uint16_t* dst = st.q_out + (int64_t(b) * hq + g * R + grp) * kHeadDim + sub * 8;
+            *reinterpret_cast<uint4*>(dst) = o0;
+            *reinterpret_cast<uint4*>(dst + 64) = o1;
+          }
+        }
+        if (writer && lane < 8) {
           uint4 o0, o1;
           norm_rope_lane(nk0, nk1, nw0, nw1, cs, sn, st.eps, o0, o1);
           *reinterpret_cast<uint4*>(&s_newk[8 * sub]) = o0;
@@ -249,10 +280,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
           *reinterpret_cast<uint4*>(&s_newv[8 * sub]) = nv0;
           *reinterpret_cast<uint4*>(&s_newv[64 + 8 * sub]) = nv1;
         }
-        // the wave's own LDS rows are read back in compute(): order them
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      // the q rows are read back now, the new token's rows in compute()
+      wave_lds_order();
+#pragma unroll
+      for (int h = 0; h < R; ++h) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&s_q[wave][h][8 * sub]);
+        const uint4 y = *reinterpret_cast<const uint4*>(&s_q[wave][h][64 + 8 * sub]);
+        qv[h][0] = x.x; qv[h][1] = x.y; qv[h][2] = x.z; qv[h][3] = x.w;
+        qv[h][4] = y.x; qv[h][5] = y.y; qv[h][6] = y.z; qv[h][7] = y.w;
       }
     }
   };
@@ -439,7 +475,11 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
     auto at = [&](int i) { return min(i, my_tiles - 1); };
     Tile ta, tb;
     load(ta, 0);
-    fused_prologue();  // fused step: while the first tile is in flight
+    // fused step: the norm and rotary run while the first tile is in flight;
+    // the barrier keeps the scheduler from moving them (and the reuse of the
+    // tile's registers) ahead of its loads
+    if constexpr (kFused) __builtin_amdgcn_sched_barrier(0);
+    fused_prologue();
     for (int i = 0; i < my_tiles; i += 2) {
       load(tb, at(i + 1));
       compute(ta, wave + i * W);
@@ -540,8 +580,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
 
   __shared__ float s_m[W][C], s_l[W][C];
   __shared__ __align__(16) float s_acc[W][C][kHeadDim];
-  // fused step: each wave's normed, rotated q rows, and the new token's k and v
+  // fused step: each wave's normed, rotated q rows, the cos / sin of the 64
+  // rotary pairs at the new token's position, and the new token's k and v
   __shared__ __align__(16) uint16_t s_q[kFused ? W : 1][kFused ? R : 1][kHeadDim];
+  __shared__ __align__(16) float s_cs[kFused ? W : 1][64], s_sn[kFused ? W : 1][64];
   __shared__ __align__(16) uint16_t s_newk[kFused ? kHeadDim : 1];
   __shared__ __align__(16) uint16_t s_newv[kFused ? kHeadDim : 1];
 
@@ -572,27 +614,33 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   // head g R + col (zero past R), dims 32s + 8c .. +7; chunk segments: head
   // g R + col % R of query token q0 + col / R.  Fused step: lanes
   // 8h + sub (h < R) hold dims 8 sub .. and 64 + 8 sub .. of the raw q row of
-  // head g R + h (the layout of the shared norm + rotary code); lanes 0..7 also
-  // fetch the new token's raw k, v and the k norm weight.
+  // head g R + h (the layout of the shared norm + rotary code) and the q norm
+  // weight of those dims (lanes past 8 R fetch row (h mod R) and leave it
+  // unused); lane i fetches the rotary frequency of pair i; every lane fetches
+  // the new token's raw k, v and the k norm weight of its dims (lanes 0..7 of
+  // the writer use them).  All are issued here, without branches, so that the
+  // first step's loads wait for the block ids alone (the wait counts only
+  // loads issued on every path).
   uint4 qb[4];
-  uint4 qx, qy, nk0, nk1, nv0, nv1, nw0, nw1;
+  uint4 qx, qy, nk0, nk1, nv0, nv1, nw0, nw1, qw0, qw1;
+  double rf = 0.0;
   const int sub = lane & 7;
   if constexpr (kFused) {
-    if (lane < 8 * R) {
-      const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + (lane >> 3)) * kHeadDim + 8 * sub;
-      qx = *reinterpret_cast<const uint4*>(qrow);
-      qy = *reinterpret_cast<const uint4*>(qrow + 64);
-    }
-    if (lane < 8) {
-      const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
-      const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
-      nk0 = *reinterpret_cast<const uint4*>(kr);
-      nk1 = *reinterpret_cast<const uint4*>(kr + 64);
-      nv0 = *reinterpret_cast<const uint4*>(vr);
-      nv1 = *reinterpret_cast<const uint4*>(vr + 64);
-      nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
-      nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
-    }
+    static_assert(!kFused || (R <= 8 && (R & (R - 1)) == 0), "fused step: one q row per 8-lane group");
+    rf = st.rev_freq[lane];
+    const uint16_t* qrow = a.q + int64_t(b) * a.q_stride + (g * R + ((lane >> 3) & (R - 1))) * kHeadDim + 8 * sub;
+    qx = *reinterpret_cast<const uint4*>(qrow);
+    qy = *reinterpret_cast<const uint4*>(qrow + 64);
+    qw0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
+    qw1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
+    const uint16_t* kr = st.k + int64_t(b) * st.k_stride + g * kHeadDim + sub * 8;
+    const uint16_t* vr = st.v + int64_t(b) * st.v_stride + g * kHeadDim + sub * 8;
+    nk0 = *reinterpret_cast<const uint4*>(kr);
+    nk1 = *reinterpret_cast<const uint4*>(kr + 64);
+    nv0 = *reinterpret_cast<const uint4*>(vr);
+    nv1 = *reinterpret_cast<const uint4*>(vr + 64);
+    nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
+    nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
   } else {
     const int64_t qr = kChunk ? (cvalid ? q0 + tcol : 0) : b;   // an invalid column reads row 0
     const int qh = kChunk ? (cvalid ? g * R + col % R : 0) : g * R + (col < R ? col : 0);
@@ -644,15 +692,27 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
   const bool writer = kFused && patch_step >= 0 && wave == patch_step % W;
   auto fused_prologue = [&]() {
     if constexpr (kFused) {
+      {
+        // each rotary angle once: lane i computes pair i
+        float c1, s1;
+        rope_angle(n - 1, rf, c1, s1);
+        s_cs[wave][lane] = c1;
+        s_sn[wave][lane] = s1;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (lane < 8 * R) {
         float cs[8], sn[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rope_angle(n - 1, st.rev_freq[8 * sub + j], cs[j], sn[j]);
-        const uint4 w0 = *reinterpret_cast<const uint4*>(st.wq + 8 * sub);
-        const uint4 w1 = *reinterpret_cast<const uint4*>(st.wq + 64 + 8 * sub);
+        const float4 c0 = *reinterpret_cast<const float4*>(&s_cs[wave][8 * sub]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&s_cs[wave][8 * sub + 4]);
+        const float4 s0 = *reinterpret_cast<const float4*>(&s_sn[wave][8 * sub]);
+        const float4 s4 = *reinterpret_cast<const float4*>(&s_sn[wave][8 * sub + 4]);
+        cs[0] = c0.x; cs[1] = c0.y; cs[2] = c0.z; cs[3] = c0.w; cs[4] = c4.x; cs[5] = c4.y; cs[6] = c4.z; cs[7] = c4.w;
+        sn[0] = s0.x; sn[1] = s0.y; sn[2] = s0.z; sn[3] = s0.w; sn[4] = s4.x; sn[5] = s4.y; sn[6] = s4.z; sn[7] = s4.w;
         const int h = lane >> 3;
         uint4 o0, o1;
-        norm_rope_lane(qx, qy, w0, w1, cs, sn, st.eps, o0, o1);
+        norm_rope_lane(qx, qy, qw0, qw1, cs, sn, st.eps, o0, o1);
         *reinterpret_cast<uint4*>(&s_q[wave][h][8 * sub]) = o0;
         *reinterpret_cast<uint4*>(&s_q[wave][h][64 + 8 * sub]) = o1;
         if (st.q_out != nullptr && sp == 0 && wave == 0) {
@@ -827,7 +887,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     auto at = [&](int i) { return min(i, my_steps - 1); };
     MStep ta, tb;
     load(ta, 0);
-    fused_prologue();  // fused step: while the first step is in flight
+    // fused step: the norm and rotary run while the first step is in flight
+    // (the barrier keeps them behind its loads)
+    if constexpr (kFused) __builtin_amdgcn_sched_barrier(0);
+    fused_prologue();
     for (int i = 0; i < my_steps; i += 2) {
       load(tb, at(i + 1));
       compute(ta, i);
