@@ -317,22 +317,29 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
 
   // Branch-free tile load (no atomics, no divergent paths), so that the
   // compiler counts outstanding loads exactly and waits only for the tile
-  // about to be used.  i is the wave-local tile number.
-  auto load = [&](Tile& tb, int i) {
+  // about to be used.  i is the wave-local tile number.  The loads go through
+  // a buffer descriptor of the (block, kv head) tile: a prefetch past the
+  // wave's last tile (live false) and a tile whose block id is invalid get a
+  // descriptor of size 0, so their loads return zeros and read no memory.
+  const uint32_t tile_bytes = uint32_t(tstride) * 2u;
+  auto load = [&](Tile& tb, int i, bool live) {
     const int tt = wave + i * W;
     const int32_t raw = __builtin_amdgcn_readlane(lane_blk, i);
     const int sub16 = ((k0 + tt * 16) & (bs - 1)) >> 4;
     tb.ok = unsigned(raw) < unsigned(pool.num_blocks);
     const int32_t blk = tb.ok ? raw : 0;
-    const uint16_t* base = pool_g + int64_t(blk) * bstride;
-    const uint16_t* kp = base + (sub16 * 16 + 2 * grp) * kHeadDim + sub * 8;
-    tb.k[0] = ld16<kStream>(kp);
-    tb.k[1] = ld16<kStream>(kp + 64);
-    tb.k[2] = ld16<kStream>(kp + kHeadDim);
-    tb.k[3] = ld16<kStream>(kp + kHeadDim + 64);
-    const uint16_t* vp = base + v_elem(bs, sub16 * 16 + khalf * 8, lane >> 1);
+    // (live depends on the wave index, which the compiler takes as varying per
+    // lane: readfirstlane keeps the descriptor in scalar registers)
+    const uint32_t nbytes = __builtin_amdgcn_readfirstlane(tb.ok && live ? tile_bytes : 0u);
+    const auto rsrc = buffer_rsrc(pool_g + int64_t(blk) * bstride, nbytes);
+    const uint32_t koff = uint32_t((sub16 * 16 + 2 * grp) * kHeadDim + sub * 8) * 2u;
+    tb.k[0] = load_buf<kStream>(rsrc, koff);
+    tb.k[1] = load_buf<kStream>(rsrc, koff + 128);
+    tb.k[2] = load_buf<kStream>(rsrc, koff + 2 * kHeadDim);
+    tb.k[3] = load_buf<kStream>(rsrc, koff + 2 * kHeadDim + 128);
+    const uint32_t voff = uint32_t(v_elem(bs, sub16 * 16 + khalf * 8, lane >> 1)) * 2u;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tb.v[j] = ld16<kStream>(vp + 32 * j * kVSub);
+    for (int j = 0; j < 4; ++j) tb.v[j] = load_buf<kStream>(rsrc, voff + 64 * j * kVSub);
   };
 
   // Zero the V entries of keys that are not attended (past the split end, or
@@ -469,21 +476,21 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(PoolGeom pool, DecodeArg
   };
 
   // Two register buffers; every iteration prefetches unconditionally (past
-  // the wave's last tile it re-reads that tile).
+  // the wave's last tile the load is a no-op: descriptor of size 0).
   const int my_tiles = ntiles > wave ? (ntiles - wave + W - 1) / W : 0;
   if (my_tiles > 0) {
     auto at = [&](int i) { return min(i, my_tiles - 1); };
     Tile ta, tb;
-    load(ta, 0);
+    load(ta, 0, true);
     // fused step: the norm and rotary run while the first tile is in flight;
     // the barrier keeps the scheduler from moving them (and the reuse of the
     // tile's registers) ahead of its loads
     if constexpr (kFused) __builtin_amdgcn_sched_barrier(0);
     fused_prologue();
     for (int i = 0; i < my_tiles; i += 2) {
-      load(tb, at(i + 1));
+      load(tb, at(i + 1), i + 1 < my_tiles);
       compute(ta, wave + i * W);
-      load(ta, at(i + 2));
+      load(ta, at(i + 2), i + 2 < my_tiles);
       if (i + 1 < my_tiles) compute(tb, wave + (i + 1) * W);
     }
   }

@@ -18,6 +18,22 @@ __device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Raw buffer descriptor (stride 0; dword 3 as the gfx9 family expects) of
+// `bytes` bytes at base.  A load past `bytes` returns zeros and makes no
+// memory access, so a descriptor of size 0 turns a wave's loads into no-ops
+// without a branch (the compiler's wait counts stay exact).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// 16-byte load at byte offset off through a buffer descriptor; kStream adds
+// the non-temporal hint (buffer_load ... nt).
+template <bool kStream>
+__device__ __forceinline__ uint4 load_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream ? 2 : 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Sticky error bits, mirrored from include/pgqa.h.
 constexpr uint32_t kErrSeqId = 0x1u;
 constexpr uint32_t kErrPosition = 0x2u;
