@@ -649,13 +649,22 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2))) voi
     nw0 = *reinterpret_cast<const uint4*>(st.wk + 8 * sub);
     nw1 = *reinterpret_cast<const uint4*>(st.wk + 64 + 8 * sub);
   } else {
-    const int64_t qr = kChunk ? (cvalid ? q0 + tcol : 0) : b;   // an invalid column reads row 0
-    const int qh = kChunk ? (cvalid ? g * R + col % R : 0) : g * R + (col < R ? col : 0);
-    const uint16_t* qrow = a.q + qr * a.q_stride + qh * kHeadDim + 8 * c;
+    // q through a buffer descriptor of the rows this workgroup may read
+    // (decode: the q heads of sequence b; chunk: the segment's rows, none when
+    // its offsets are bad).  An unused column reads past the end and gets
+    // zeros, so the loads are unconditional and no select follows them.  (With
+    // a select after plain loads the compiler sank them into per-dword loads
+    // under branches; the wait before the first step could then not skip them
+    // and held that step's loads back until q had landed.)
+    const int64_t row0 = kChunk ? (q_ok ? q0 : 0) : b;
+    const int64_t span = kChunk ? (q_ok ? int64_t(qlen) * a.q_stride : 0) : int64_t(hq) * kHeadDim;
+    const uint32_t qbytes =
+        __builtin_amdgcn_readfirstlane(uint32_t(span * 2 < 0x7fffffff ? span * 2 : 0x7fffffff));
+    const auto qrsrc = buffer_rsrc(a.q + row0 * a.q_stride, qbytes);
+    const int64_t qe = (kChunk ? int64_t(tcol) * a.q_stride : 0) + (g * R + col % R) * kHeadDim + 8 * c;
+    const uint32_t qoff = cvalid ? uint32_t(qe * 2) : 0x80000000u;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qb[s] = sel4(cvalid, *reinterpret_cast<const uint4*>(qrow + 32 * s), make_uint4(0u, 0u, 0u, 0u));
-    }
+    for (int s = 0; s < 4; ++s) qb[s] = load_buf<false>(qrsrc, qoff + 64 * s);
   }
 
   const bool bad_ctx = n < 0 || n > a.max_ctx || int64_t(n) > int64_t(a.bt_stride) * bs;

@@ -123,13 +123,18 @@ __device__ __forceinline__ void column_body(PoolGeom& pool, const ChunkArgs& a, 
   }
   const int tcol = col / R;
   const bool cvalid = tcol < qlen;
+  // q through a buffer descriptor of the segment's rows: an unused column
+  // reads past the end and gets zeros, so the loads are unconditional and no
+  // select follows them (a select after plain loads let the compiler sink them
+  // into per-dword loads under branches, which the wait before the first step
+  // could not skip).
   uint4 qb[4];
   {
-    const int64_t qr = cvalid ? q0 + tcol : 0;  // an unused column reads row 0 and is zeroed
-    const int qh = cvalid ? g * R + col % R : 0;
-    const uint16_t* qrow = a.q + (qr * hq + qh) * kHeadDim + 8 * c;
+    const auto qrsrc = buffer_rsrc(a.q + int64_t(q0) * hq * kHeadDim,
+                                   __builtin_amdgcn_readfirstlane(uint32_t(qlen) * uint32_t(hq) * (2u * kHeadDim)));
+    const uint32_t qoff = cvalid ? uint32_t(((tcol * hq + g * R + col % R) * kHeadDim + 8 * c) * 2) : 0x80000000u;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) qb[t] = sel4(cvalid, *reinterpret_cast<const uint4*>(qrow + 32 * t), make_uint4(0, 0, 0, 0));
+    for (int t = 0; t < 4; ++t) qb[t] = load_buf<false>(qrsrc, qoff + 64 * t);
   }
   const int klim = cvalid ? min(k1, n - qlen + tcol + 1) : k0;  // keys the lane's column attends
 
