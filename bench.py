@@ -826,7 +826,7 @@ def main():
                     help="do not pass the host-side context lengths to the decode plans (natural unit order)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}); the decode path "
               "shards by sequence or kv head with no exchange, which this benchmark does not exercise",
               file=sys.stderr)
         sys.exit(2)
