@@ -241,6 +241,30 @@ def test_bad_metadata_sets_flags_without_faulting(kernel):
     assert f & pg.DEVERR_POSITION and f & pg.DEVERR_SEQ_ID
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_bad_block_id_leaves_other_sequences_exact(kernel):
+    """A block id outside the pool in one sequence's table row (at its first, a
+    middle and its last tile): the flag is raised, nothing faults, and every
+    other sequence's output still matches the fp64 reference, with the
+    planner's plan and with many short splits (combine)."""
+    w = make_step(StepSpec("badblk", 983, 16, 8, 128, decode=(Group(4, 150, 400),)))
+    run = StepRun(w)
+    run.write()
+    q = run.decode_q()
+    ref = run.oracle_decode_on_gpu_inputs(q)
+    mx = int(w.dec_ctx.max())
+    nb1 = -(-int(w.dec_ctx[1]) // 16)
+    keep = [0, 2, 3]
+    for j in (0, nb1 // 2, nb1 - 1):
+        bt = w.dec_block_tables.copy()
+        bt[1, j] = 10_000
+        for plan in (default_plan(w, kernel), pg.DecodePlan(64, -(-mx // 64), 4, 0, kernel)):
+            _note(f"bad block id at tile {j} of sequence 1, plan {plan}")
+            out = pg.paged_decode_attention(run.pool, q, run.dec_ctx, dev_i32(bt), mx, SCALE, plan=plan)
+            assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
+            compare(out[keep], ref[keep], f"other sequences, bad block id at tile {j}")
+
+
 def test_host_pointer_rejected():
     """The C ABI refuses a host buffer where device memory is required."""
     import ctypes

@@ -112,7 +112,14 @@ def test_fused_step_zero_context_and_bad_block(kernel):
                    s.rope_theta, SCALE, out=out, plan=default_plan(w, kernel))
     assert run.pool.check_errors() & pg.DEVERR_BLOCK_ID
     assert torch.all(out[1] == 0)
-    assert torch.all(torch.isfinite(out[0].float()))
+    # sequence 0 is untouched by the others' bad metadata: the fp64 chain on its own token
+    assert w.tok_seq[0] == 0 and w.dec_tok[0] == 0
+    bt_c = compact(w.block_tables, run.used)
+    pk, pv = w.prefix_k[run.used].copy(), w.prefix_v[run.used].copy()
+    q_ref, _ = O.fused_norm_rope_write(w.tok_q[:1], w.tok_k[:1], w.tok_v[:1], w.wq, w.wk, w.tok_pos[:1],
+                                       w.tok_seq[:1], bt_c, s.eps, s.rope_theta, pk, pv)
+    ref = O.decode_attention(O.bf16_round(q_ref), pk, pv, bt_c[:1], w.dec_ctx[:1], SCALE)
+    compare(out[:1], ref, "sequence 0 beside a zero context and a bad block id")
 
 
 @pytest.mark.parametrize("seed", range(32))
