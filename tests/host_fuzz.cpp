@@ -7,12 +7,11 @@
 // self-consistent.  It prints one "ok" line per part, or a message and exits 1.
 //
 // Built by tests/test_host_fuzz.py with g++ against libpgqa.so.  For a run
-// under AddressSanitizer and UndefinedBehaviorSanitizer, build the library's
-// host sources and this file with the sanitizers on the host side only, e.g.
-//   hipcc -O1 -g -std=c++17 -fPIC -Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined
-//         -Iinclude --offload-arch=gfx950 -c paged_gqa_decode_head_amd/csrc/{errors,api,sched}.cpp
-// and link those objects, the library's device objects and this file with
-// -fsanitize=address -fsanitize=undefined.
+// under AddressSanitizer and UndefinedBehaviorSanitizer, compile the library's
+// host sources (errors.cpp, api.cpp, sched.cpp) and this file with hipcc, each
+// sanitizer option preceded by -Xarch_host so that only host code is
+// instrumented, and link them with the library's device objects and the same
+// two sanitizers.
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
