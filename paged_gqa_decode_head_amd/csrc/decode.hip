@@ -1054,6 +1054,22 @@ __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool
   const int hkv = pool.num_kv_heads, r = a.num_q_heads / hkv;
   const int cols = columns_of(a, r);
   const int g = blockIdx.x / cols, col = blockIdx.x - g * cols, s = blockIdx.y, d = threadIdx.x;
+  const int64_t unit = int64_t(s) * hkv + g;
+  const float* pl = a.part_lse + unit * a.max_splits * 16 + col;
+  const float* po = a.part_o + (unit * a.max_splits * 16 + col) * kHeadDim + d;
+  // Plans of up to kCombineFast splits load every partial slot of the column
+  // (slots past the segment's splits are read but unused) together with the
+  // segment's metadata, so the merge waits one round trip instead of two; the
+  // arithmetic is merge_splits' for one group of splits (same bits).
+  const bool fast = a.max_splits <= kCombineFast;
+  float v[kCombineFast];
+  float lraw = -INFINITY;
+  const int lane = d & 63;
+  if (fast) {
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) v[k] = k < a.max_splits ? po[int64_t(k) * 16 * kHeadDim] : 0.f;
+    lraw = lane < a.max_splits ? pl[lane * 16] : -INFINITY;
+  }
   const int q0 = a.qsl[s], q1 = a.qsl[s + 1], n = a.ctx[s];
   const int qlen = q1 - q0;
   const bool ok = q0 >= 0 && q1 >= q0 && q1 <= a.total_q && (s + 1 < a.batch || q1 == a.total_q) &&
@@ -1062,11 +1078,26 @@ __global__ __launch_bounds__(kHeadDim) void combine_columns_kernel(PoolGeom pool
   if (!ok || col >= qlen * r) return;
   const int ns = (n + a.split_tokens - 1) / a.split_tokens;
   if (ns <= 1) return;
-  const int64_t unit = int64_t(s) * hkv + g;
-  const float* pl = a.part_lse + unit * a.max_splits * 16 + col;
-  const float* po = a.part_o + (unit * a.max_splits * 16 + col) * kHeadDim + d;
-  a.out[(int64_t(q0) + col / r) * a.q_stride + (g * r + col % r) * kHeadDim + d] =
-      f32_to_bf16(merge_splits(pl, 16, po, 16 * kHeadDim, ns));
+  uint16_t* dst = a.out + (int64_t(q0) + col / r) * a.q_stride + (g * r + col % r) * kHeadDim + d;
+  if (!fast) {
+    *dst = f32_to_bf16(merge_splits(pl, 16, po, 16 * kHeadDim, ns));
+    return;
+  }
+  const float lk = lane < ns ? lraw : -INFINITY;
+  float M = lk;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+  float L = e;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineFast; ++k) {
+    const float ek = __shfl(e, k);
+    if (k < ns) acc += ek * v[k];
+  }
+  *dst = f32_to_bf16(L > 0.f ? acc / L : 0.f);
 }
 
 // The combine launch that follows the split kernel when the plan has splits.
