@@ -252,6 +252,32 @@ __device__ __forceinline__ uint32_t keep2(int key, int klim) {
   return key + 1 < klim ? 0xffffffffu : key < klim ? 0x0000ffffu : 0u;
 }
 
+// The merge of one row from at most kCombineFast split partials already in
+// registers: v[k] = lane j's 4 dims of split k (k < ns), lk = the lse of split j
+// on lane j (-inf for j >= ns).  The weights travel between the row's 32 lanes
+// by shuffle and the partials are summed in split order.
+__device__ __forceinline__ void merge_row_fast(const float4 (&v)[kCombineFast], float lk, int ns, bool row_ok,
+                                               uint16_t* dst) {
+  float M = lk;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
+  float L = e;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int k = 0; k < kCombineFast; ++k) {
+    const float w = __shfl(e, k, 32) * inv;  // lane k of this row's 32
+    if (k < ns) {
+      acc.x += w * v[k].x; acc.y += w * v[k].y; acc.z += w * v[k].z; acc.w += w * v[k].w;
+    }
+  }
+  if (!row_ok) return;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+}
+
 // Log-sum-exp combine of the ns split partials of one output row: 32 lanes per
 // row (lane j owns dims 4j .. 4j + 3); partial row base of split k is
 // base + k * total_q * Hq ([split][token][head] layout), dst the row's bf16
@@ -268,32 +294,14 @@ __device__ __forceinline__ void combine_row(const ChunkArgs& a, int64_t base, in
 
   if (ns <= kCombineFast) {
     // Up to 16 splits: every partial load is issued first, beside the one lse
-    // value lane j (< ns) reads; the weights then travel between the row's 32
-    // lanes by shuffle, and the partials are summed in split order.
+    // value lane j (< ns) reads.
     float4 v[kCombineFast];
 #pragma unroll
     for (int k = 0; k < kCombineFast; ++k)
       v[k] = row_ok && k < ns ? *reinterpret_cast<const float4*>(src + k * stride * kHeadDim)
                               : make_float4(0.f, 0.f, 0.f, 0.f);
     const float lk = row_ok && j < ns ? a.part_lse[base + j * stride] : -INFINITY;
-    float M = lk;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float e = lk == -INFINITY ? 0.f : fast_exp2(lk - M);
-    float L = e;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < kCombineFast; ++k) {
-      const float w = __shfl(e, k, 32) * inv;  // lane k of this row's 32
-      if (k < ns) {
-        acc.x += w * v[k].x; acc.y += w * v[k].y; acc.z += w * v[k].z; acc.w += w * v[k].w;
-      }
-    }
-    if (!row_ok) return;
-    *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+    merge_row_fast(v, lk, ns, row_ok, dst);
     return;
   }
 

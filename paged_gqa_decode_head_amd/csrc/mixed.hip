@@ -338,20 +338,53 @@ __global__ __launch_bounds__(kWideThreads, 2) void mixed_kernel(PoolGeom pool, C
 // Combine items: rows grp .. grp + 7 of segment s and kv head g, each merged
 // over its sp split partials (32 lanes per row).  Items whose segment does not
 // match the device metadata are skipped (the attention items zeroed the rows).
+//
+// Items of at most kCombineFast splits issue their partial loads before the
+// segment metadata arrives, addressed from the item's own copy of the segment
+// offset, so the merge waits one round trip after the item instead of two.
+// The loads go through buffer descriptors over the partials: an address
+// outside them reads zeros.  The rows are merged only once the item matches the
+// metadata, and then those addresses are the ones combine_row would read.
 template <int R>
 __global__ __launch_bounds__(256) void mixed_combine_kernel(PoolGeom pool, ChunkArgs a) {
   const MixedItem it = load_item(a.items, int64_t(a.num_items) + blockIdx.x);
   __shared__ float s_w[kCombineRows][kCombineChunk];
-  SegInfo si{};
+  const int row = threadIdx.x >> 5, j = threadIdx.x & 31;
   const int ns = it.sp;
+  const int64_t stride = int64_t(a.total_q) * a.num_q_heads;  // partial rows per split
+  const int64_t lse_bytes = stride * a.max_splits * 4;
+  const bool early = it.kind == kKindCombine && ns >= 2 && ns <= kCombineFast && ns <= a.max_splits &&
+                     lse_bytes * kHeadDim < 0x7fffffff;
+  float4 v[kCombineFast];
+  float lk = -INFINITY;
+  if (early) {
+    const int rho_h = it.grp + row;
+    const int64_t orow_h = (int64_t(it.q0) + rho_h / R) * a.num_q_heads + it.g * R + rho_h % R;
+    const bool in = rho_h >= 0 && orow_h >= 0 && orow_h < stride;
+    const auto ro = buffer_rsrc(a.part_o, uint32_t(lse_bytes * kHeadDim));
+    const auto rl = buffer_rsrc(a.part_lse, uint32_t(lse_bytes));
+    const uint32_t o0 = in ? uint32_t((orow_h * kHeadDim + 4 * j) * 4) : 0x80000000u;
+    const uint32_t sstep = uint32_t(stride * kHeadDim * 4);
+#pragma unroll
+    for (int k = 0; k < kCombineFast; ++k) {
+      const u32x4 x = k < ns ? __builtin_amdgcn_raw_buffer_load_b128(ro, o0 + k * sstep, 0, 0) : u32x4{0, 0, 0, 0};
+      v[k] = make_float4(__uint_as_float(x.x), __uint_as_float(x.y), __uint_as_float(x.z), __uint_as_float(x.w));
+    }
+    if (j < ns && in)
+      lk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, uint32_t((orow_h + j * stride) * 4), 0, 0));
+  }
+  SegInfo si{};
   if (it.kind != kKindCombine || !item_matches(a, pool, it, R, si) || ns < 2 || ns > a.max_splits) {
     if (threadIdx.x == 0 && it.kind != kKindCombine) raise_error(pool.err, kErrQuery);
     return;
   }
-  const int row = threadIdx.x >> 5, j = threadIdx.x & 31;
   const int rho = it.grp + row;
   const bool row_ok = rho >= 0 && rho < si.rows;
   const int64_t orow = (int64_t(si.q0) + rho / R) * a.num_q_heads + it.g * R + rho % R;
+  if (early) {
+    merge_row_fast(v, row_ok ? lk : -INFINITY, ns, row_ok, a.out + orow * kHeadDim + 4 * j);
+    return;
+  }
   combine_row(a, orow, ns, row_ok, j, s_w[row], a.out + orow * kHeadDim + 4 * j);
 }
 
