@@ -45,6 +45,8 @@
 //   * LDS operand reads are conflict-free: the 16 lanes of each read phase hit
 //     16 different 4-bank groups of the XOR-swizzled stages, which direct
 //     global->LDS loads can fill.
+#include <limits.h>
+
 #include "chunk_common.hpp"
 
 namespace pgqa {
@@ -364,6 +366,102 @@ __global__ __launch_bounds__(256) void chunk_combine_kernel(PoolGeom pool, Chunk
               a.out + (qrow * a.num_q_heads + g * R + hh) * kHeadDim + 4 * j);
 }
 
+// Row combine, for calls of at most 64 segments: one workgroup per kv head g
+// and 8 consecutive query rows (token t, head in group) of the call, in token
+// order.  A row's partials are addressed by (t, head) alone, so the loads of
+// its first splits go out at once, beside the segment offsets and context
+// lengths (one segment per lane): as many splits as a wide row can have, at
+// most kCombineFast.  The row's segment is then the number of segments that
+// end at or before t (a ballot), and its split count follows from the segment.
+// Rows of bad segments, rows that no segment holds and rows with one split
+// (written directly by the attention kernels) are skipped; a row with more
+// splits than were loaded early loads them now.  The merges are combine_row's
+// (same bits), the long one without LDS, since the rows of a workgroup may
+// take different paths.  No item list is derived, so the common merge waits one
+// round trip instead of the list scan and two.
+constexpr int kRowCombineSegs = 64;
+
+template <int R>
+__global__ __launch_bounds__(256) void chunk_combine_rows_kernel(PoolGeom pool, ChunkArgs a) {
+  const int hkv = pool.num_kv_heads, N = a.num_segments;
+  const int g = blockIdx.x % hkv;
+  const int64_t G = int64_t(blockIdx.x / hkv) * kCombineRows + (threadIdx.x >> 5);  // row of kv head g
+  const int lane = threadIdx.x & 63, j = threadIdx.x & 31;
+  const bool in = G < int64_t(a.total_q) * R;
+  const int t = in ? int(G / R) : 0, hh = int(G % R);
+  const int64_t stride = int64_t(a.total_q) * a.num_q_heads;  // partial rows per split
+  const int64_t base = int64_t(t) * a.num_q_heads + g * R + hh;
+  const float* src = a.part_o + base * kHeadDim + 4 * j;
+  const float* lse = a.part_lse + base;
+  // splits loaded early: a wide row's at most (its keys end by max_ctx)
+  const int early = min(min(a.max_splits, cdiv(max(a.max_ctx, 1), a.split_wide)), kCombineFast);
+  float4 v[kCombineFast];
+#pragma unroll
+  for (int k = 0; k < kCombineFast; ++k)
+    v[k] = in && k < early ? *reinterpret_cast<const float4*>(src + k * stride * kHeadDim)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+  float lk = in && j < early ? lse[j * stride] : -INFINITY;
+  const int e0 = lane < N ? a.qsl[lane] : 0;
+  const int e1 = lane < N ? a.qsl[lane + 1] : INT_MAX;
+  const int nn = lane < N ? a.ctx[lane] : 0;
+  // the wave's two rows: lanes 0-31 and 32-63
+  const int t_lo = __shfl(t, 0), t_hi = __shfl(t, 32);
+  const int s_lo = __popcll(__ballot(e1 <= t_lo)), s_hi = __popcll(__ballot(e1 <= t_hi));
+  const int s = lane < 32 ? s_lo : s_hi;
+  const int q0 = __shfl(e0, s & 63), q1 = __shfl(e1, s & 63), n = __shfl(nn, s & 63);
+  if (!in || s >= N) return;
+  const SegInfo si = seg_info_of(a, s, q0, q1, n, R, pool.block_size);
+  const int rho = (t - si.q0) * R + hh;
+  if (si.bad || rho < 0 || rho >= si.rows) return;
+  const int ns = si.tiles == 1 ? cdiv(si.n, a.split_short)
+                               : cdiv(wide_kend(si, rho / (kRows * kWideTiles), R), a.split_wide);
+  if (ns <= 1) return;
+  uint16_t* dst = a.out + base * kHeadDim + 4 * j;
+  if (ns <= kCombineFast) {
+    if (ns > early) {
+#pragma unroll
+      for (int k = 0; k < kCombineFast; ++k)
+        if (k >= early && k < ns) v[k] = *reinterpret_cast<const float4*>(src + k * stride * kHeadDim);
+      lk = j < ns ? lse[j * stride] : -INFINITY;
+    }
+    merge_row_fast(v, j < ns ? lk : -INFINITY, ns, true, dst);
+    return;
+  }
+  // Long rows: the row max and weight sum in one pass over the split lse values
+  // (lane j takes splits j, j + 32, ...), then the weights of 32 splits at a
+  // time travel by shuffle and every lane sums its 4 dims in split order.
+  float M = -INFINITY, L = 0.f;
+  for (int k = j; k < ns; k += 32) {
+    const float l = lse[k * stride];
+    if (l > M) {
+      L = L * fast_exp2(M - l) + 1.f;
+      M = l;
+    } else if (l != -INFINITY) {
+      L += fast_exp2(l - M);
+    }
+  }
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    const float Mo = __shfl_xor(M, o), Lo = __shfl_xor(L, o);
+    const float Mn = fmaxf(M, Mo);
+    L = (M == -INFINITY ? 0.f : L * fast_exp2(M - Mn)) + (Mo == -INFINITY ? 0.f : Lo * fast_exp2(Mo - Mn));
+    M = Mn;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < ns; c0 += 32) {
+    const float l = c0 + j < ns ? lse[(c0 + j) * stride] : -INFINITY;
+    const float wj = l == -INFINITY || M == -INFINITY ? 0.f : fast_exp2(l - M) * inv;
+    const int cn = min(32, ns - c0);
+    for (int k = 0; k < cn; ++k) {
+      const float w = __shfl(wj, k, 32);
+      const float4 x = *reinterpret_cast<const float4*>(src + int64_t(c0 + k) * stride * kHeadDim);
+      acc.x += w * x.x; acc.y += w * x.y; acc.z += w * x.z; acc.w += w * x.w;
+    }
+  }
+  *reinterpret_cast<uint2*>(dst) = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+}
+
 template <int R>
 hipError_t launch_r(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& grids, hipStream_t stream) {
   if (grids.wide > 0) {
@@ -377,7 +475,13 @@ hipError_t launch_r(const PoolGeom& pool, const ChunkArgs& a, const ChunkGrids& 
     if (e != hipSuccess) return e;
   }
   if (grids.combine > 0) {
-    hipLaunchKernelGGL((chunk_combine_kernel<R>), dim3(grids.combine), dim3(256), 0, stream, pool, a);
+    if (a.num_segments <= kRowCombineSegs) {
+      const int64_t rows = (int64_t(a.total_q) * R + kCombineRows - 1) / kCombineRows;
+      hipLaunchKernelGGL((chunk_combine_rows_kernel<R>), dim3(rows * pool.num_kv_heads), dim3(256), 0, stream, pool,
+                         a);
+    } else {
+      hipLaunchKernelGGL((chunk_combine_kernel<R>), dim3(grids.combine), dim3(256), 0, stream, pool, a);
+    }
     return hipGetLastError();
   }
   return hipSuccess;

@@ -72,11 +72,10 @@ struct SegInfo {
   uint32_t err;
 };
 
-__device__ __forceinline__ SegInfo seg_info(const ChunkArgs& a, int s, int r, int bs) {
+__device__ __forceinline__ SegInfo seg_info_of(const ChunkArgs& a, int s, int q0, int q1, int n, int r, int bs) {
   SegInfo si;
-  si.q0 = a.qsl[s];
-  const int q1 = a.qsl[s + 1];
-  si.n = a.ctx[s];
+  si.q0 = q0;
+  si.n = n;
   si.qlen = q1 - si.q0;
   const bool rows_ok = si.q0 >= 0 && q1 >= si.q0 && q1 <= a.total_q;
   // the last segment must end at total_q: the host sized the call's work lists from total_q
@@ -90,6 +89,10 @@ __device__ __forceinline__ SegInfo seg_info(const ChunkArgs& a, int s, int r, in
   si.rows = si.bad ? 0 : si.qlen * r;
   si.tiles = si.bad ? 0 : si.claimed_tiles;
   return si;
+}
+
+__device__ __forceinline__ SegInfo seg_info(const ChunkArgs& a, int s, int r, int bs) {
+  return seg_info_of(a, s, a.qsl[s], a.qsl[s + 1], a.ctx[s], r, bs);
 }
 
 __device__ __forceinline__ int wide_groups(const SegInfo& si) { return cdiv(si.tiles, kWideTiles); }

@@ -322,3 +322,37 @@ def test_chunk_random_mixed_steps(seed):
                                    plan=plan)
     assert run.pool.check_errors() == 0
     compare(out, run.oracle_chunk_on_gpu_inputs(q), f"seed {seed}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])
+def test_chunk_more_than_64_segments(hq, hkv):
+    """A call of 70 segments (wide, short, single-token and empty ones) with
+    forced short splits: its combine finds items by scanning the metadata
+    (the row combine serves calls of at most 64 segments).  Against the fp64
+    reference, and the first 64 segments bit-identical to the same segments
+    called alone (row combine, same split plan)."""
+    rng = np.random.default_rng(9700 + hq)
+    bs = 16
+    segs = []
+    for i in range(70):
+        q_len = [40, 3, 1, 0, 24][i % 5]
+        segs.append((int(rng.integers(0, 300)), q_len))
+    nb = sum(-(-(L + q) // bs) for L, q in segs) + 4
+    w = make_step(_chunk_spec(f"cseg70-{hq}", 9710 + hq, hq, hkv, bs, segs, nb))
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    qsl, ctx = w.chk_qsl, w.chk_ctx
+    mq, mc = int(np.diff(qsl).max()), int(ctx.max())
+    plan = pg.ChunkPlan(64, -(-mc // 32), 32, 0)
+    _note(f"[cseg70] heads {hq}/{hkv}: 70 segments, plan {plan}")
+    out = pg.paged_chunk_attention(run.pool, q, run.chk_qsl, run.chk_ctx, run.chk_bt, mq, mc, SCALE, plan=plan)
+    assert run.pool.check_errors() == 0
+    compare(out, run.oracle_chunk_on_gpu_inputs(q), "70 segments")
+    t64 = int(qsl[64])
+    out64 = pg.paged_chunk_attention(run.pool, q[:t64].contiguous(), dev_i32(qsl[:65]), dev_i32(ctx[:64]),
+                                     run.chk_bt[:64].contiguous(), int(np.diff(qsl[:65]).max()), int(ctx[:64].max()),
+                                     SCALE, plan=plan)
+    assert run.pool.check_errors() == 0
+    assert np.array_equal(bits_of(out64), bits_of(out[:t64]))
+
