@@ -27,7 +27,9 @@
 //     the cache straight into the MFMA operand registers (whole 128-byte lines per
 //     load); K goes through a per-wave LDS ring (direct loads) to reach the operand
 //     layout.  HBM-bound.
-// Splits are merged by a log-sum-exp combine kernel when a row has several.
+// Splits are merged by a log-sum-exp combine kernel when a row has several:
+// the row combine (one workgroup per 8 query rows, no item list) for calls of
+// at most 64 segments, else the item combine over the combine list below.
 //
 // Operand layouts (verified on the hardware): lane l supplies A[m][k] with
 // m = l%32, k = 8(l/32)+j and B[k][n] with n = l%32; D[i] of lane l is
@@ -59,7 +61,8 @@ namespace {
 //           bad segment that claims more than one tile;
 //   short   {segment, kv head, 0, split} of one-tile segments; {.., -1, 0} for bad
 //           one-tile segments;
-//   combine {segment, kv head, tile, part} for every row tile with several splits,
+//   combine {segment, kv head, tile, part} for every row tile with several splits
+//           (calls of more than 64 segments),
 //           in kCombineParts parts of 8 rows.
 // No list is stored: every workgroup derives its own item from the segment
 // metadata (a wave-wide scan of per-segment counts, then a search), so no
