@@ -356,3 +356,28 @@ def test_chunk_more_than_64_segments(hq, hkv):
     assert run.pool.check_errors() == 0
     assert np.array_equal(bits_of(out64), bits_of(out[:t64]))
 
+
+def test_chunk_bad_segment_beside_split_rows():
+    """A bad segment between two good ones, with every row split: the bad rows
+    come back zero with the flag raised, and the combine still merges the good
+    rows around them (some combine workgroups hold rows of both kinds)."""
+    segs = [(300, 41), (200, 6), (500, 3)]
+    nb = sum(-(-(L + q) // 16) for L, q in segs) + 4
+    w = make_step(_chunk_spec("cbadsplit", 9740, 16, 8, 16, segs, nb))
+    run = StepRun(w)
+    run.write()
+    q = run.chunk_q()
+    ref = run.oracle_chunk_on_gpu_inputs(q)
+    qsl = w.chk_qsl
+    mq, mc = int(np.diff(qsl).max()), int(w.chk_ctx.max())
+    plan = pg.ChunkPlan(64, -(-mc // 64), 64, 0)
+    ctx = w.chk_ctx.copy()
+    ctx[1] = 2  # fewer keys than the segment's 6 query tokens
+    out = torch.full((int(qsl[-1]), 16, 128), 3.0, dtype=torch.bfloat16, device="cuda")
+    pg.paged_chunk_attention(run.pool, q, run.chk_qsl, dev_i32(ctx), run.chk_bt, mq, mc, SCALE, out=out, plan=plan)
+    assert run.pool.check_errors() & pg.DEVERR_QUERY
+    a, b = int(qsl[1]), int(qsl[2])
+    assert torch.all(out[a:b] == 0)
+    keep = np.r_[0:a, b:int(qsl[-1])]
+    compare(out[torch.from_numpy(keep).to(out.device)], ref[keep], "good segments beside a bad one")
+
